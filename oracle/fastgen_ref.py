@@ -1,0 +1,359 @@
+"""Plain fp64 CPU oracle of FastGen's per-head profiling, compaction and decode.
+
+TEST INFRASTRUCTURE ONLY: used by ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py``; never by the product path.
+
+Source: the hyper.ai summary pages of "Model Tells You What to Discard:
+Adaptive KV Cache Compression for LLMs" (Ge et al., ICLR 2024), section
+Method (the English text on the Korean page; the Chinese page says the same):
+
+* two-phase inference -- profile every head while the prompt is encoded, then
+  keep head-specific caches while generating (Method, first paragraph);
+* the attention map A = softmax(Q K^T), the compressed cache
+  K_C, V_C = f(K, V, C), and the policy choice C* = argmin CacheMemoryCost(C)
+  subject to |A - softmax(Q K_C^T)| <= 1 - T with T the recover ratio
+  (Method, second paragraph and its constraint equation);
+* the base policies: special tokens, punctuation tokens, a local window set
+  by a ratio r_l, the tokens with the largest cumulative attention set by a
+  ratio r_f, and the full cache (Method, policy paragraph);
+* the greedy shortlist of nested unions special, +punct, +frequent, +local,
+  full (Method, shortlist equation);
+* the policy picked on the prompt is reused for every generated token
+  (Method, stability paragraph).
+
+Readings taken where the pages are silent or garbled (each is listed with its
+reason in the design notes of the repository):
+
+* scores are scaled by 1/sqrt(d) and causally masked (Llama attention);
+* the constraint's norm is, per query row, half the L1 distance between the
+  full attention row and the softmax restricted to the kept keys, which equals
+  one minus the attention mass the kept keys receive; rows (and the query
+  heads sharing one KV head) are averaged.  So recovery R_k is the retained
+  share of all attention mass, and the policy is the first shortlist entry
+  with R_k >= T (nested entries have non-decreasing cost);
+* k_f = floor(r_f n), w_l = floor(r_l n) computed in fp64;
+* the cumulative attention score of key j is sum_{i >= j} A_ij over the
+  prompt rows (diagonal included) and over the query heads of the group;
+* the frequent set F is the k_f keys with the largest score, ties to the lower
+  index, fixed after the prompt;
+* row i keeps key j (j <= i) under the local base iff i - j < w_l;
+* a key that several bases keep counts once, at the first level of the list
+  (0 special, 1 punct, 2 frequent, 3 local, 4 full);
+* CacheMemoryCost(C) is the number of prompt keys the first generated token
+  (row n) keeps;
+* during decode, position p attends to {j <= p : level(p, j) <= policy} and the
+  cache afterwards holds {j <= p : level(p + 1, j) <= policy}.
+
+Everything here is fp64 numpy, one KV head (with its G query heads) at a time.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+TOKEN_NORMAL, TOKEN_SPECIAL, TOKEN_PUNCT = 0, 1, 2
+LEVEL_SPECIAL, LEVEL_PUNCT, LEVEL_FREQUENT, LEVEL_LOCAL, LEVEL_FULL = 0, 1, 2, 3, 4
+N_LEVELS = 5
+
+NEAR_T_WINDOW = 1e-4          # a head whose R_k lies this close to T is flagged
+TIE_TAU_DEFAULT = 3e-5        # relative gap at the k-th score below which top-k is flagged
+UNDERFLOW_FLOOR = 2.0 ** -100 # k-th score below this is flagged as well
+ROW_BLOCK = 512
+
+
+def budgets(n: int, r_l: float, r_f: float) -> tuple:
+    """k_f = floor(r_f * n) frequent keys, w_l = floor(r_l * n) local window (policy paragraph)."""
+    k_f = int(math.floor(float(r_f) * float(n)))
+    w_l = int(math.floor(float(r_l) * float(n)))
+    return k_f, w_l
+
+
+def causal_attention_rows(q: np.ndarray, K: np.ndarray, row0: int) -> np.ndarray:
+    """Rows row0 .. row0+m-1 of A = softmax(q K^T / sqrt(d)) under the causal mask.
+
+    q: [m, d] query rows at positions row0.., K: [n, d].  Returns [m, n] fp64 with
+    zeros above the diagonal.  (Method, second paragraph: the attention map.)
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    m, d = q.shape
+    n = K.shape[0]
+    S = (q @ K.T) / math.sqrt(d)
+    i = row0 + np.arange(m)[:, None]
+    j = np.arange(n)[None, :]
+    S = np.where(j <= i, S, -np.inf)
+    mx = S.max(axis=1, keepdims=True)
+    E = np.exp(S - mx)
+    return E / E.sum(axis=1, keepdims=True)
+
+
+def _row_logsumexp(q: np.ndarray, K: np.ndarray, row0: int) -> np.ndarray:
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    m, d = q.shape
+    S = (q @ K.T) / math.sqrt(d)
+    i = row0 + np.arange(m)[:, None]
+    j = np.arange(K.shape[0])[None, :]
+    S = np.where(j <= i, S, -np.inf)
+    mx = S.max(axis=1)
+    return mx + np.log(np.exp(S - mx[:, None]).sum(axis=1))
+
+
+def column_scores(Qg: np.ndarray, K: np.ndarray, w_l: int) -> Dict[str, np.ndarray]:
+    """Per-key cumulative attention of one KV head and the per-row logsumexp.
+
+    cum[j]  = sum_g sum_{i >= j} A^g_ij    (the cumulative attention score that
+              ranks keys for the frequent policy, policy paragraph);
+    band[j] = sum_g sum_{j <= i < j + w_l} A^g_ij, the part of cum that rows
+              inside the local window contribute (a checked intermediate of
+              the profiling kernels, not part of the method's definition);
+    lse[g, i] = log sum_{j <= i} exp(q^g_i . k_j / sqrt(d)).
+    """
+    G, n, _ = Qg.shape
+    cum = np.zeros(n, dtype=np.float64)
+    band = np.zeros(n, dtype=np.float64)
+    lse = np.zeros((G, n), dtype=np.float64)
+    for g in range(G):
+        for r0 in range(0, n, ROW_BLOCK):
+            r1 = min(n, r0 + ROW_BLOCK)
+            A = causal_attention_rows(Qg[g, r0:r1], K, r0)
+            cum += A.sum(axis=0)
+            i = np.arange(r0, r1)[:, None]
+            j = np.arange(n)[None, :]
+            band += np.where((i - j >= 0) & (i - j < w_l), A, 0.0).sum(axis=0)
+            lse[g, r0:r1] = _row_logsumexp(Qg[g, r0:r1], K, r0)
+    return {"cum": cum, "band": band, "lse": lse}
+
+
+def frequent_set(cum: np.ndarray, k_f: int) -> np.ndarray:
+    """F: the k_f keys with the largest cumulative score, ties to the lower index."""
+    n = cum.shape[0]
+    order = sorted(range(n), key=lambda j: (-float(cum[j]), j))
+    F = np.zeros(n, dtype=bool)
+    F[order[:k_f]] = True
+    return F
+
+
+def key_levels(cls: np.ndarray, F: np.ndarray, rows: np.ndarray, w_l: int) -> np.ndarray:
+    """level(i, j) for query rows ``rows`` and every key j < len(cls).
+
+    First shortlist entry whose union keeps (i, j): 0 special, 1 punct, 2 frequent,
+    3 local (i - j < w_l), 4 full only.  F may be shorter than cls (decode positions
+    are never frequent).  Entries with j > i are returned as 5 (not attended).
+    """
+    m = len(rows)
+    nk = len(cls)
+    Fx = np.zeros(nk, dtype=bool)
+    Fx[: len(F)] = F[: nk]
+    i = np.asarray(rows)[:, None]
+    j = np.arange(nk)[None, :]
+    lev = np.full((m, nk), LEVEL_FULL, dtype=np.int64)
+    lev = np.where(i - j < w_l, LEVEL_LOCAL, lev)
+    lev = np.where(Fx[None, :], LEVEL_FREQUENT, lev)
+    lev = np.where((cls == TOKEN_PUNCT)[None, :], LEVEL_PUNCT, lev)
+    lev = np.where((cls == TOKEN_SPECIAL)[None, :], LEVEL_SPECIAL, lev)
+    return np.where(j <= i, lev, N_LEVELS)
+
+
+def row_bins(Qg: np.ndarray, K: np.ndarray, cls: np.ndarray, F: np.ndarray, w_l: int) -> np.ndarray:
+    """bins[g, i, l] = attention mass row i of query head g puts on keys of level l."""
+    G, n, _ = Qg.shape
+    bins = np.zeros((G, n, N_LEVELS), dtype=np.float64)
+    for g in range(G):
+        for r0 in range(0, n, ROW_BLOCK):
+            r1 = min(n, r0 + ROW_BLOCK)
+            A = causal_attention_rows(Qg[g, r0:r1], K, r0)
+            lev = key_levels(cls, F, np.arange(r0, r1), w_l)
+            for lv in range(N_LEVELS):
+                bins[g, r0:r1, lv] = np.where(lev == lv, A, 0.0).sum(axis=1)
+    return bins
+
+
+def recovery_from_bins(bins: np.ndarray) -> np.ndarray:
+    """R_k = share of all attention mass kept by shortlist entry k (rows and heads averaged).
+
+    The pages' constraint reads per row as half the L1 distance between A_i and
+    the renormalised restriction to the kept keys, which is 1 - kept mass; the
+    rows of the head (and of the G query heads of a KV head) are averaged.
+    R_4 (full cache) is 1 by definition; the computed value is checked.
+    """
+    G, n, _ = bins.shape
+    per_level = bins.sum(axis=(0, 1)) / float(G * n)
+    R = np.cumsum(per_level)
+    if abs(R[LEVEL_FULL] - 1.0) > 1e-12:
+        raise AssertionError(f"full-cache recovery {R[LEVEL_FULL]!r} is not 1")
+    R[LEVEL_FULL] = 1.0
+    return R
+
+
+def select_policy(R: np.ndarray, T: float) -> int:
+    """Cheapest shortlist entry meeting R_k >= T (costs are non-decreasing along the list)."""
+    for k in range(N_LEVELS):
+        if R[k] >= T:
+            return k
+    return LEVEL_FULL
+
+
+def kept_positions(cls: np.ndarray, F: np.ndarray, w_l: int, policy: int) -> np.ndarray:
+    """Prompt keys kept in the compressed cache: {j < n : level(n, j) <= policy}.
+
+    Row n is the first generated token, so this is the cache that
+    K_C, V_C = f(K, V, C) hands to generation.
+    """
+    n = len(cls)
+    lev = key_levels(cls, F, np.array([n]), w_l)[0]          # row n never sees key n: no key n here
+    return np.flatnonzero(lev <= policy).astype(np.int64)
+
+
+def compact_head(K: np.ndarray, V: np.ndarray, kept: np.ndarray):
+    """K_C, V_C = K[kept], V[kept] (rows in ascending position)."""
+    return K[kept], V[kept]
+
+
+@dataclass
+class HeadProfile:
+    k_f: int
+    w_l: int
+    lse: np.ndarray               # [G, n]
+    cum: np.ndarray               # [n]
+    band: np.ndarray              # [n]
+    F: np.ndarray                 # [n] bool
+    bins: np.ndarray              # [G, n, 5]
+    R: np.ndarray                 # [5]
+    policy: int
+    kept: np.ndarray              # positions kept for generation
+    near_T: bool
+    topk_tie: bool
+    kth_gap: float = field(default=float("nan"))
+
+
+def topk_tie_flag(cum: np.ndarray, k_f: int, tau: float) -> tuple:
+    n = len(cum)
+    if k_f <= 0 or k_f >= n:
+        return False, float("inf")
+    s = np.sort(cum)[::-1]
+    sk, sk1 = s[k_f - 1], s[k_f]
+    gap = (sk - sk1) / sk if sk > 0 else 0.0
+    return bool(sk - sk1 <= tau * sk or sk < UNDERFLOW_FLOOR), float(gap)
+
+
+def profile_head(Qg: np.ndarray, K: np.ndarray, cls: np.ndarray, r_l: float, r_f: float, T: float,
+                 tau: float = TIE_TAU_DEFAULT) -> HeadProfile:
+    """Profile one KV head from its G query heads' prompt rows and pick its policy."""
+    Qg = np.asarray(Qg, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    G, n, _ = Qg.shape
+    k_f, w_l = budgets(n, r_l, r_f)
+    cs = column_scores(Qg, K, w_l)
+    F = frequent_set(cs["cum"], k_f)
+    bins = row_bins(Qg, K, cls, F, w_l)
+    R = recovery_from_bins(bins)
+    policy = select_policy(R, T)
+    kept = kept_positions(cls, F, w_l, policy)
+    near = bool(np.any(np.abs(R[:LEVEL_FULL] - T) <= NEAR_T_WINDOW))
+    tie, gap = topk_tie_flag(cs["cum"], k_f, tau)
+    return HeadProfile(k_f, w_l, cs["lse"], cs["cum"], cs["band"], F, bins, R, policy, kept, near, tie, gap)
+
+
+def profile_layer(Q: np.ndarray, K: np.ndarray, cls: np.ndarray, r_l: float, r_f: float, T: float,
+                  tau: float = TIE_TAU_DEFAULT) -> List[List[HeadProfile]]:
+    """profile_head over every (batch entry, KV head) of one layer.  Q: [B,Hq,n,d], K: [B,Hkv,n,d]."""
+    B, Hq = Q.shape[:2]
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    return [[profile_head(Q[b, h * G:(h + 1) * G], K[b, h], cls[b], r_l, r_f, T, tau)
+             for h in range(Hkv)] for b in range(B)]
+
+
+def _masked_softmax_out(qg: np.ndarray, Ks: np.ndarray, Vs: np.ndarray) -> np.ndarray:
+    """softmax(q K^T / sqrt(d)) V for each of G query rows; zeros when no key is kept."""
+    G, d = qg.shape
+    if Ks.shape[0] == 0:
+        return np.zeros((G, Vs.shape[1] if Vs.ndim == 2 else d), dtype=np.float64)
+    S = (qg @ Ks.T) / math.sqrt(d)
+    S = S - S.max(axis=1, keepdims=True)
+    E = np.exp(S)
+    return (E / E.sum(axis=1, keepdims=True)) @ Vs
+
+
+def decode_incremental(K: np.ndarray, V: np.ndarray, cls: np.ndarray, F: np.ndarray, w_l: int, policy: int,
+                       q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, new_cls: np.ndarray):
+    """Generation with a head-specific cache, step by step.
+
+    The cache starts as the compacted prompt keys {j < n : level(n, j) <= policy}.
+    At position p = n + t the new token attends to the cache plus itself when
+    level(p, p) <= policy; afterwards the cache keeps {j <= p : level(p + 1, j) <= policy},
+    obtained by re-testing every cached key and the new one against row p + 1.
+
+    q: [steps, G, d]; k_new, v_new: [steps, d]; new_cls: [steps].
+    Returns (out [steps, G, d], caches: list of kept position arrays after each step).
+    """
+    n = len(cls)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    steps = q.shape[0]
+    cls_all = np.concatenate([cls, np.asarray(new_cls, dtype=cls.dtype)])
+    rows = {int(j): (K[j], V[j]) for j in kept_positions(cls, F, w_l, policy)}
+    outs = np.zeros((steps, q.shape[1], q.shape[2]), dtype=np.float64)
+    caches = []
+    for t in range(steps):
+        p = n + t
+        cand = dict(rows)
+        cand[p] = (np.asarray(k_new[t], dtype=np.float64), np.asarray(v_new[t], dtype=np.float64))
+        lev_p = key_levels(cls_all[: p + 1], F, np.array([p]), w_l)[0]
+        att = sorted(j for j in cand if lev_p[j] <= policy)
+        Ks = np.stack([cand[j][0] for j in att]) if att else np.zeros((0, K.shape[1]))
+        Vs = np.stack([cand[j][1] for j in att]) if att else np.zeros((0, V.shape[1]))
+        outs[t] = _masked_softmax_out(np.asarray(q[t], dtype=np.float64), Ks, Vs)
+        lev_next = key_levels(cls_all[: p + 1], F, np.array([p + 1]), w_l)[0]
+        rows = {j: cand[j] for j in cand if lev_next[j] <= policy}
+        caches.append(np.array(sorted(rows), dtype=np.int64))
+    return outs, caches
+
+
+def decode_masked(K: np.ndarray, V: np.ndarray, cls: np.ndarray, F: np.ndarray, w_l: int, policy: int,
+                  q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, new_cls: np.ndarray):
+    """The same generation computed in one shot: row p of the level-masked attention
+    over the concatenated prompt + generated sequence.  Returns (out, caches) like
+    ``decode_incremental``; caches[t] = {j <= p : level(p + 1, j) <= policy}."""
+    n = len(cls)
+    steps = q.shape[0]
+    K_all = np.concatenate([np.asarray(K, np.float64), np.asarray(k_new, np.float64)])
+    V_all = np.concatenate([np.asarray(V, np.float64), np.asarray(v_new, np.float64)])
+    cls_all = np.concatenate([cls, np.asarray(new_cls, dtype=cls.dtype)])
+    lev = key_levels(cls_all, F, n + np.arange(steps + 1), w_l)     # rows n .. n+steps
+    outs = np.zeros((steps, q.shape[1], q.shape[2]), dtype=np.float64)
+    caches = []
+    for t in range(steps):
+        p = n + t
+        att = np.flatnonzero(lev[t, : p + 1] <= policy)
+        outs[t] = _masked_softmax_out(np.asarray(q[t], np.float64), K_all[att], V_all[att])
+        caches.append(np.flatnonzero(lev[t + 1, : p + 1] <= policy).astype(np.int64))
+    return outs, caches
+
+
+def decode_head_from_profile(prof: HeadProfile, K, V, cls, q, k_new, v_new, new_cls,
+                             policy: Optional[int] = None, F: Optional[np.ndarray] = None):
+    """Incremental decode of one KV head, optionally forcing the policy / frequent set."""
+    pol = prof.policy if policy is None else int(policy)
+    Fs = prof.F if F is None else np.asarray(F, dtype=bool)
+    return decode_incremental(K, V, cls, Fs, prof.w_l, pol, q, k_new, v_new, new_cls)
+
+
+def forced_kept(cls: np.ndarray, F: np.ndarray, w_l: int, policy: int) -> np.ndarray:
+    """kept_positions under a policy / frequent set given from outside (flagged heads)."""
+    return kept_positions(cls, np.asarray(F, dtype=bool), w_l, int(policy))
+
+
+def pairs_causal(n: int) -> int:
+    return n * (n + 1) // 2
+
+
+__all__: Sequence[str] = [
+    "budgets", "causal_attention_rows", "column_scores", "frequent_set", "key_levels", "row_bins",
+    "recovery_from_bins", "select_policy", "kept_positions", "compact_head", "profile_head",
+    "profile_layer", "decode_incremental", "decode_masked", "HeadProfile",
+]
