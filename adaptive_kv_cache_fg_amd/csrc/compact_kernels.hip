@@ -1,0 +1,229 @@
+// Compaction of K/V into ragged head-specific caches (hyper.ai summary of
+// "Model Tells You What to Discard", Method, second paragraph:
+// K_C, V_C = f(K, V, C)).
+//
+// The cache of a head holds the prompt keys its first generated token (query
+// row n) keeps: {j < n : level(n, j) <= policy}.  Permanent rows -- special,
+// punct (policy >= 1), frequent (policy >= 2), everything (policy 4) -- are
+// packed in ascending position after a ring of w_l - 1 slots that holds the
+// normal keys of the local window (policy 3); slot = position mod (w_l - 1),
+// so a new token always lands in the slot of the key leaving the window.
+//
+// Kernels: a per-head count (plan), one scan over heads for row and work-item
+// offsets, a gather over (head, 256-position chunk) whose workgroups rank
+// their kept keys with a wave ballot prefix and copy rows with 16-byte loads,
+// and the per-head list of decode work items.
+#include "fg_common.h"
+#include "fg_internal.h"
+
+namespace fg {
+
+constexpr int kPosChunk = 256;
+
+__device__ __forceinline__ bool fbit(const uint32_t* fm, int j) { return (fm[j >> 5] >> (j & 31)) & 1u; }
+
+__device__ __forceinline__ bool perm_keep(uint8_t c, bool f, int pol) {
+  return c == kSpecial || (c == kPunct && pol >= 1) || (f && pol >= 2) || pol == 4;
+}
+
+__device__ __forceinline__ int ring_slots(int pol, int w_l) { return (pol == 3 && w_l >= 2) ? w_l - 1 : 0; }
+
+__device__ __forceinline__ int block_sum_i(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  int t = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  return t;   // valid in every thread
+}
+
+__global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ cls, const uint8_t* __restrict__ policy,
+                                                   const uint32_t* __restrict__ fmask, int Hkv, int n, int w_l,
+                                                   int max_new, int max_new_kept, int32_t* __restrict__ kept_count,
+                                                   int32_t* __restrict__ ring, int32_t* __restrict__ capacity) {
+  __shared__ int red[4];
+  const int hd = blockIdx.x, b = hd / Hkv;
+  const int nw = (n + 31) / 32;
+  const uint8_t* cl = cls + (size_t)b * n;
+  const uint32_t* fm = fmask + (size_t)hd * nw;
+  const int pol = policy[hd];
+  const int R = ring_slots(pol, w_l);
+  int np = 0, nr = 0;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    const bool p = perm_keep(cl[j], fbit(fm, j), pol);
+    np += p;
+    nr += (!p && R > 0 && j >= n - R);
+  }
+  np = block_sum_i(np, red);
+  nr = block_sum_i(nr, red);
+  if (threadIdx.x == 0) {
+    kept_count[hd] = np + nr;
+    ring[hd] = R;
+    capacity[hd] = R + np + (pol == 4 ? max_new : max_new_kept);
+  }
+}
+
+// Exclusive prefix sums over heads: rows and decode work items.  One workgroup.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ capacity, int H, int chunk,
+                                                    int64_t* __restrict__ row_offset, int64_t* __restrict__ work_offset,
+                                                    int64_t* __restrict__ totals) {
+  __shared__ long long sr[1024], sw[1024];
+  __shared__ long long carry_r, carry_w;
+  if (threadIdx.x == 0) { carry_r = 0; carry_w = 0; }
+  __syncthreads();
+  for (int base = 0; base < H; base += blockDim.x) {
+    const int i = base + threadIdx.x;
+    const long long cap = i < H ? capacity[i] : 0;
+    sr[threadIdx.x] = cap;
+    sw[threadIdx.x] = (cap + chunk - 1) / chunk;
+    __syncthreads();
+    for (int o = 1; o < (int)blockDim.x; o <<= 1) {          // inclusive Hillis-Steele scan
+      const long long ar = threadIdx.x >= (unsigned)o ? sr[threadIdx.x - o] : 0;
+      const long long aw = threadIdx.x >= (unsigned)o ? sw[threadIdx.x - o] : 0;
+      __syncthreads();
+      sr[threadIdx.x] += ar;
+      sw[threadIdx.x] += aw;
+      __syncthreads();
+    }
+    if (i < H) {
+      row_offset[i + 1] = carry_r + sr[threadIdx.x];
+      work_offset[i + 1] = carry_w + sw[threadIdx.x];
+    }
+    __syncthreads();
+    if (threadIdx.x == blockDim.x - 1) { carry_r += sr[threadIdx.x]; carry_w += sw[threadIdx.x]; }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    row_offset[0] = 0;
+    work_offset[0] = 0;
+    totals[0] = carry_r;
+    totals[1] = carry_w;
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, const T* __restrict__ V,
+                                                     const uint8_t* __restrict__ cls, const uint8_t* __restrict__ policy,
+                                                     const uint32_t* __restrict__ fmask,
+                                                     const int64_t* __restrict__ row_offset, const int32_t* __restrict__ ring,
+                                                     int Hkv, int n, int nch, T* __restrict__ Kc, T* __restrict__ Vc,
+                                                     int32_t* __restrict__ pos, int32_t* __restrict__ len,
+                                                     uint32_t* __restrict__ error_word) {
+  constexpr int kCPR = D * (int)sizeof(T) / 16;           // 16-byte chunks per row
+  __shared__ int red[4];
+  __shared__ int wcnt[4], wrows[4];
+  __shared__ int src_j[kPosChunk], dst_r[kPosChunk];
+
+  const int hd = blockIdx.x / nch, ch = blockIdx.x % nch, b = hd / Hkv;
+  const int nw = (n + 31) / 32;
+  const uint8_t* cl = cls + (size_t)b * n;
+  const uint32_t* fm = fmask + (size_t)hd * nw;
+  const int pol = policy[hd];
+  const int R = ring[hd];
+  const int64_t off = row_offset[hd];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (blockIdx.x == 0 && tid == 0) *error_word = 0u;
+
+  // permanent keys at positions before this chunk
+  int before = 0;
+  for (int j = tid; j < ch * kPosChunk; j += blockDim.x) before += perm_keep(cl[j], fbit(fm, j), pol);
+  before = block_sum_i(before, red);
+
+  const int j = ch * kPosChunk + tid;
+  const bool valid = j < n;
+  const bool pf = valid && perm_keep(cl[j], fbit(fm, j), pol);
+  const bool win = valid && R > 0 && j >= n - R;          // inside the local window of row n
+  const bool rf = win && !pf;
+  const bool any = pf || rf;
+  const unsigned long long bp = __ballot(pf), ba = __ballot(any);
+  if (lane == 0) { wcnt[wave] = __popcll(bp); wrows[wave] = __popcll(ba); }
+  __syncthreads();
+  int pbefore = 0, abefore = 0, ptotal = 0, atotal = 0;
+  for (int w = 0; w < 4; ++w) {
+    pbefore += (w < wave) ? wcnt[w] : 0;
+    abefore += (w < wave) ? wrows[w] : 0;
+    ptotal += wcnt[w];
+    atotal += wrows[w];
+  }
+  const unsigned long long below = (1ull << lane) - 1ull;
+  if (any) {
+    const int e = abefore + __popcll(ba & below);
+    const int64_t dst = pf ? off + R + before + pbefore + __popcll(bp & below) : off + (j % R);
+    src_j[e] = j;
+    dst_r[e] = (int)(dst - off);
+    pos[dst] = j;
+  }
+  if (win && pf) pos[off + (j % R)] = -1;                 // its slot stays empty
+  if (ch == 0 && R > 0) {                                  // window positions before the prompt start
+    for (int t = tid; t < R; t += blockDim.x) {
+      const int jj = n - R + t;
+      if (jj < 0) pos[off + (((jj % R) + R) % R)] = -1;
+    }
+  }
+  if (ch == nch - 1 && tid == 0) len[hd] = R + before + ptotal;
+  __syncthreads();
+
+  const T* Ks = K + (size_t)hd * n * D;
+  const T* Vs = V + (size_t)hd * n * D;
+  for (int idx = tid; idx < atotal * kCPR; idx += blockDim.x) {
+    const int e = idx / kCPR, q = idx % kCPR;
+    const size_t s = (size_t)src_j[e] * D * sizeof(T) + q * 16;
+    const size_t d = (size_t)(off + dst_r[e]) * D * sizeof(T) + q * 16;
+    *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Kc) + d) =
+        *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(Ks) + s);
+    *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Vc) + d) =
+        *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(Vs) + s);
+  }
+}
+
+__global__ __launch_bounds__(256) void worklist_kernel(const int64_t* __restrict__ work_offset, int chunk,
+                                                       int32_t* __restrict__ work) {
+  const int hd = blockIdx.x;
+  const int64_t w0 = work_offset[hd], w1 = work_offset[hd + 1];
+  for (int64_t w = w0 + threadIdx.x; w < w1; w += blockDim.x) {
+    work[2 * w] = hd;
+    work[2 * w + 1] = (int32_t)((w - w0) * chunk);
+  }
+}
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
+  const int H = a.B * a.Hkv;
+  timed_begin(FG_K_PLAN, st);
+  plan_kernel<<<dim3(H), dim3(256), 0, st>>>(a.cls, a.policy, a.fmask, a.Hkv, a.n, a.w_l, a.max_new, a.max_new_kept,
+                                             a.kept_count, a.ring, a.capacity);
+  timed_end(st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  timed_begin(FG_K_SCAN, st);
+  scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(a.capacity, H, a.chunk_rows, a.row_offset, a.work_offset, a.totals);
+  timed_end(st);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st) {
+  const int H = a.B * a.Hkv;
+  const int nch = (a.n + kPosChunk - 1) / kPosChunk;
+  timed_begin(FG_K_GATHER, st);
+  gather_kernel<T, D><<<dim3(H * nch), dim3(256), 0, st>>>(
+      (const T*)a.K, (const T*)a.V, a.cls, a.policy, a.fmask, a.row_offset, a.ring, a.Hkv, a.n, nch, (T*)a.Kc,
+      (T*)a.Vc, a.pos, a.len, a.error_word);
+  timed_end(st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  timed_begin(FG_K_WORKLIST, st);
+  worklist_kernel<<<dim3(H), dim3(256), 0, st>>>(a.work_offset, a.chunk_rows, a.work);
+  timed_end(st);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st) {
+  if (a.dtype == FG_DTYPE_BF16)
+    return a.D == 128 ? launch_gather_t<__bf16, 128>(a, st) : launch_gather_t<__bf16, 64>(a, st);
+  return a.D == 128 ? launch_gather_t<float, 128>(a, st) : launch_gather_t<float, 64>(a, st);
+}
+
+}  // namespace fg

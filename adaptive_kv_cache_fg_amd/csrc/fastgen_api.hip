@@ -1,0 +1,361 @@
+// C ABI of libfastgen: argument validation, workspace carving, launches,
+// status codes and kernel timing.  Every check runs on the host before any
+// launch; nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "fg_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fg_status fail(fg_status s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+
+fg_status hip_fail(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return FG_ERR_HIP;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t elem_size(int dtype) { return dtype == FG_DTYPE_BF16 ? 2 : 4; }
+
+fg_status check_shape(const fg_shape* s) {
+  if (!s) return fail(FG_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->seq_len < 1)
+    return fail(FG_ERR_INVALID_ARG, "batch, heads and seq_len must be >= 1");
+  if (s->n_q_heads % s->n_kv_heads != 0) return fail(FG_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
+  if (s->head_dim != 64 && s->head_dim != 128) return fail(FG_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (s->dtype != FG_DTYPE_BF16 && s->dtype != FG_DTYPE_F32) return fail(FG_ERR_UNSUPPORTED, "dtype must be bf16 or fp32");
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(FG_ERR_UNSUPPORTED, "group size must be 1, 2, 4 or 8");
+  if (s->seq_len > (1 << 24)) return fail(FG_ERR_UNSUPPORTED, "seq_len above 2^24");
+  const double rows = (double)s->batch * s->n_q_heads * s->seq_len;
+  if (rows * s->head_dim > 4.0e12) return fail(FG_ERR_UNSUPPORTED, "tensor too large");
+  if ((double)s->batch * s->n_kv_heads > 2.0e9) return fail(FG_ERR_UNSUPPORTED, "too many heads");
+  return FG_OK;
+}
+
+fg_status check_params(const fg_params* p) {
+  if (!p) return fail(FG_ERR_INVALID_ARG, "params is NULL");
+  if (!(p->T > 0.0 && p->T <= 1.0)) return fail(FG_ERR_INVALID_ARG, "T must lie in (0, 1]");
+  if (!(p->r_l >= 0.0 && p->r_l <= 1.0) || !(p->r_f >= 0.0 && p->r_f <= 1.0))
+    return fail(FG_ERR_INVALID_ARG, "r_l and r_f must lie in [0, 1]");
+  return FG_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+void budgets(const fg_shape* s, const fg_params* p, int* k_f, int* w_l) {
+  *k_f = (int)std::floor(p->r_f * (double)s->seq_len);
+  *w_l = (int)std::floor(p->r_l * (double)s->seq_len);
+}
+
+// ---------------------------------------------------------------- kernel timing
+struct TimingRec {
+  int id;
+  hipEvent_t start, stop;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+thread_local TimingRec g_open = {-1, nullptr, nullptr};
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace fg {
+
+void timed_begin(int kernel_id, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_open.id = -1;
+  if (!g_timing) return;
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return;
+  g_open = {kernel_id, a, b};
+  (void)hipEventRecord(a, st);
+}
+
+void timed_end(hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (g_open.id < 0) return;
+  (void)hipEventRecord(g_open.stop, st);
+  g_recs.push_back(g_open);
+  g_open.id = -1;
+}
+
+}  // namespace fg
+
+extern "C" {
+
+const char* fg_status_string(fg_status s) {
+  switch (s) {
+    case FG_OK: return "ok";
+    case FG_ERR_INVALID_ARG: return "invalid argument";
+    case FG_ERR_UNSUPPORTED: return "unsupported";
+    case FG_ERR_WORKSPACE: return "workspace too small";
+    case FG_ERR_CAPACITY: return "cache capacity exceeded";
+    case FG_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* fg_last_error(void) { return g_last_error.c_str(); }
+
+const char* fg_kernel_name(int32_t id) {
+  static const char* names[FG_K_COUNT] = {"profile_rowstats", "profile_colsums", "profile_select", "compact_plan",
+                                          "compact_scan",     "compact_gather",  "compact_worklist",
+                                          "decode_partial",   "decode_combine"};
+  return (id >= 0 && id < FG_K_COUNT) ? names[id] : "unknown";
+}
+
+void fg_kernel_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+}
+
+int32_t fg_kernel_timing_read(int32_t* ids, float* ms, int32_t max) {
+  std::vector<TimingRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    recs.swap(g_recs);
+  }
+  int32_t k = 0;
+  for (const TimingRec& r : recs) {
+    float t = -1.f;
+    if (hipEventSynchronize(r.stop) == hipSuccess) (void)hipEventElapsedTime(&t, r.start, r.stop);
+    if (k < max && ids && ms) {
+      ids[k] = r.id;
+      ms[k] = t;
+      ++k;
+    }
+  }
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (const TimingRec& r : recs) {
+    g_pool.push_back(r.start);
+    g_pool.push_back(r.stop);
+  }
+  return k;
+}
+
+size_t fg_profile_workspace_size(const fg_shape* s) {
+  if (check_shape(s) != FG_OK) return 0;
+  const size_t rows_q = (size_t)s->batch * s->n_q_heads * s->seq_len;
+  const size_t rows_k = (size_t)s->batch * s->n_kv_heads * s->seq_len;
+  return align256(rows_q * sizeof(float)) + align256(rows_k * sizeof(float));
+}
+
+fg_status fg_profile(const fg_shape* shape, const fg_params* params, const void* Q, const void* K,
+                     const uint8_t* token_class, uint8_t* policy, float* cum_score, float* recovery,
+                     uint32_t* freq_mask, float* lse_out, float* band_out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  fg_status s = check_shape(shape);
+  if (s != FG_OK) return s;
+  if ((s = check_params(params)) != FG_OK) return s;
+  if (!Q || !K || !token_class || !policy || !cum_score || !recovery || !freq_mask)
+    return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(Q) || !aligned16(K)) return fail(FG_ERR_INVALID_ARG, "Q and K must be 16-byte aligned");
+  const size_t need = fg_profile_workspace_size(shape);
+  if (!workspace || workspace_bytes < need) return fail(FG_ERR_WORKSPACE, "profile workspace too small");
+  fg::ProfileArgs a{};
+  a.dtype = shape->dtype;
+  a.D = shape->head_dim;
+  a.B = shape->batch;
+  a.Hq = shape->n_q_heads;
+  a.Hkv = shape->n_kv_heads;
+  a.n = shape->seq_len;
+  budgets(shape, params, &a.k_f, &a.w_l);
+  a.T = params->T;
+  a.Q = Q;
+  a.K = K;
+  a.cls = token_class;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(ws);
+  const size_t rows_q = (size_t)a.B * a.Hq * a.n;
+  a.band = band_out ? band_out : reinterpret_cast<float*>(ws + align256(rows_q * sizeof(float)));
+  a.lse_out = lse_out;
+  a.cum = cum_score;
+  a.fmask = freq_mask;
+  a.recovery = recovery;
+  a.policy = policy;
+  hipError_t e = fg::launch_profile_sweeps(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "profile sweeps");
+  e = fg::launch_select(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "profile select");
+  return FG_OK;
+}
+
+int32_t fg_decode_chunk_rows(void) { return fg::kDecodeChunk; }
+
+fg_status fg_compact_plan(const fg_shape* shape, const fg_params* params, const uint8_t* token_class,
+                          const uint8_t* policy, const uint32_t* freq_mask, int32_t max_new_tokens,
+                          int32_t max_new_kept, int32_t* kept_count, int32_t* ring, int32_t* capacity,
+                          int64_t* row_offset, int64_t* work_offset, int64_t* totals, hipStream_t stream) {
+  fg_status s = check_shape(shape);
+  if (s != FG_OK) return s;
+  if ((s = check_params(params)) != FG_OK) return s;
+  if (!token_class || !policy || !freq_mask || !kept_count || !ring || !capacity || !row_offset || !work_offset ||
+      !totals)
+    return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (max_new_tokens < 0 || max_new_kept < 0 || max_new_kept > max_new_tokens)
+    return fail(FG_ERR_INVALID_ARG, "need 0 <= max_new_kept <= max_new_tokens");
+  if ((double)shape->seq_len + max_new_tokens > 2.0e9) return fail(FG_ERR_UNSUPPORTED, "capacity above 2^31");
+  fg::PlanArgs a{};
+  a.B = shape->batch;
+  a.Hkv = shape->n_kv_heads;
+  a.n = shape->seq_len;
+  int k_f = 0;
+  budgets(shape, params, &k_f, &a.w_l);
+  a.max_new = max_new_tokens;
+  a.max_new_kept = max_new_kept;
+  a.cls = token_class;
+  a.policy = policy;
+  a.fmask = freq_mask;
+  a.kept_count = kept_count;
+  a.ring = ring;
+  a.capacity = capacity;
+  a.row_offset = row_offset;
+  a.work_offset = work_offset;
+  a.totals = totals;
+  a.chunk_rows = fg::kDecodeChunk;
+  hipError_t e = fg::launch_plan(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "compact plan");
+  return FG_OK;
+}
+
+static fg_status check_cache_views(const fg_cache* c) {
+  if (!c) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
+  if (!c->k || !c->v || !c->pos || !c->row_offset || !c->len || !c->capacity || !c->ring || !c->policy ||
+      !c->work_offset || !c->error_word || (c->n_work > 0 && !c->work))
+    return fail(FG_ERR_INVALID_ARG, "a cache buffer is NULL");
+  if (!aligned16(c->k) || !aligned16(c->v)) return fail(FG_ERR_INVALID_ARG, "cache k and v must be 16-byte aligned");
+  if (c->total_rows < 0 || c->n_work < 0 || c->n_work > 0x7fffffff)
+    return fail(FG_ERR_INVALID_ARG, "bad total_rows or n_work");
+  return FG_OK;
+}
+
+fg_status fg_compact(const fg_shape* shape, const fg_params* params, const void* K, const void* V,
+                     const uint8_t* token_class, const uint8_t* policy, const uint32_t* freq_mask, fg_cache* cache,
+                     hipStream_t stream) {
+  fg_status s = check_shape(shape);
+  if (s != FG_OK) return s;
+  if ((s = check_params(params)) != FG_OK) return s;
+  if ((s = check_cache_views(cache)) != FG_OK) return s;
+  if (!K || !V || !token_class || !policy || !freq_mask) return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(K) || !aligned16(V)) return fail(FG_ERR_INVALID_ARG, "K and V must be 16-byte aligned");
+  fg::GatherArgs a{};
+  a.dtype = shape->dtype;
+  a.D = shape->head_dim;
+  a.B = shape->batch;
+  a.Hkv = shape->n_kv_heads;
+  a.n = shape->seq_len;
+  int k_f = 0;
+  budgets(shape, params, &k_f, &a.w_l);
+  a.K = K;
+  a.V = V;
+  a.cls = token_class;
+  a.policy = policy;
+  a.fmask = freq_mask;
+  a.row_offset = cache->row_offset;
+  a.ring = cache->ring;
+  a.work_offset = cache->work_offset;
+  a.Kc = cache->k;
+  a.Vc = cache->v;
+  a.pos = cache->pos;
+  a.len = cache->len;
+  a.work = cache->work;
+  a.error_word = cache->error_word;
+  a.chunk_rows = fg::kDecodeChunk;
+  hipError_t e = fg::launch_gather(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "compact gather");
+  cache->shape = *shape;
+  cache->n_prompt = shape->seq_len;
+  cache->w_l = a.w_l;
+  cache->next_pos = shape->seq_len;
+  return FG_OK;
+}
+
+size_t fg_decode_workspace_size(const fg_cache* c) {
+  if (!c || check_shape(&c->shape) != FG_OK) return 0;
+  const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
+  return align256((size_t)(c->n_work > 0 ? c->n_work : 1) * G * (c->shape.head_dim + 2) * sizeof(float));
+}
+
+fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
+                         const uint8_t* new_class, float* out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  fg_status s = check_cache_views(cache);
+  if (s != FG_OK) return s;
+  if ((s = check_shape(&cache->shape)) != FG_OK) return s;
+  if (!q || !k_new || !v_new || !out) return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(q)) return fail(FG_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  if (cache->next_pos < cache->n_prompt || cache->next_pos >= 0x7fffffff)
+    return fail(FG_ERR_INVALID_ARG, "cache position out of range (was fg_compact called?)");
+  if (!workspace || workspace_bytes < fg_decode_workspace_size(cache))
+    return fail(FG_ERR_WORKSPACE, "decode workspace too small");
+  fg::DecodeArgs a{};
+  a.dtype = cache->shape.dtype;
+  a.D = cache->shape.head_dim;
+  a.B = cache->shape.batch;
+  a.Hq = cache->shape.n_q_heads;
+  a.Hkv = cache->shape.n_kv_heads;
+  a.w_l = cache->w_l;
+  a.p = cache->next_pos;
+  a.n_work = cache->n_work;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_class = new_class;
+  a.out = out;
+  a.part = static_cast<float*>(workspace);
+  a.Kc = cache->k;
+  a.Vc = cache->v;
+  a.pos = cache->pos;
+  a.row_offset = cache->row_offset;
+  a.len = cache->len;
+  a.capacity = cache->capacity;
+  a.ring = cache->ring;
+  a.policy = cache->policy;
+  a.work_offset = cache->work_offset;
+  a.work = cache->work;
+  a.error_word = cache->error_word;
+  a.chunk_rows = fg::kDecodeChunk;
+  hipError_t e = fg::launch_decode(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode step");
+  cache->next_pos += 1;
+  return FG_OK;
+}
+
+fg_status fg_cache_error(const fg_cache* cache, uint32_t* bits_out, hipStream_t stream) {
+  if (!cache || !cache->error_word) return fail(FG_ERR_INVALID_ARG, "cache or error_word is NULL");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  uint32_t bits = 0;
+  e = hipMemcpy(&bits, cache->error_word, sizeof(bits), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "read error word");
+  if (bits_out) *bits_out = bits;
+  return bits ? fail(FG_ERR_CAPACITY, "a cache append exceeded its capacity") : FG_OK;
+}
+
+}  // extern "C"

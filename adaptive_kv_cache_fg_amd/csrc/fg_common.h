@@ -1,0 +1,56 @@
+// Internal helpers shared by the libfastgen kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -3.0e38f;   // finite "minus infinity" for running maxima
+
+constexpr uint8_t kNormal = 0, kSpecial = 1, kPunct = 2;
+
+// 32x32 MFMA tile traits.  One MFMA multiplies a 32 x KS block of A (rows
+// m = lane % 32, k = (lane / 32) * EPL + e) by a KS x 32 block of B (columns
+// n = lane % 32, same k mapping) into a 32 x 32 fp32 tile whose element
+// (row 8*(r/4) + 4*(lane/32) + r%4, column lane%32) sits in accumulator r.
+template <typename T> struct Mfma;
+
+template <> struct Mfma<__bf16> {
+  using op_t = bf16x8;
+  static constexpr int KS = 16;   // reduction depth per instruction
+  static constexpr int EPL = 8;   // elements per lane per instruction
+  static __device__ __forceinline__ f32x16 mac(op_t a, op_t b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  using op_t = float;
+  static constexpr int KS = 2;
+  static constexpr int EPL = 1;
+  static __device__ __forceinline__ f32x16 mac(op_t a, op_t b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Row (within the 32x32 tile) held by accumulator r of this lane.
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+template <typename T>
+__device__ __forceinline__ T zero_val() { return T(0.0f); }
+
+}  // namespace fg

@@ -1,0 +1,97 @@
+// Host-side declarations shared by the libfastgen translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fastgen.h"
+
+namespace fg {
+
+// Kernel timing hooks (no-ops unless fg_kernel_timing_enable(1)).
+void timed_begin(int kernel_id, hipStream_t st);
+void timed_end(hipStream_t st);
+
+struct ProfileArgs {
+  int dtype, D, B, Hq, Hkv, n;
+  int k_f, w_l;
+  double T;
+  const void* Q;
+  const void* K;
+  const uint8_t* cls;
+  float* lse2;       // [B*Hq*n] log2-domain row log-sum-exp (workspace)
+  float* lse_out;    // optional natural-log copy
+  float* cum;        // [B*Hkv*n]
+  float* band;       // [B*Hkv*n]
+  uint32_t* fmask;   // [B*Hkv*ceil(n/32)]
+  float* recovery;   // [B*Hkv*5]
+  uint8_t* policy;   // [B*Hkv]
+};
+
+hipError_t launch_profile_sweeps(const ProfileArgs& a, hipStream_t st);
+hipError_t launch_select(const ProfileArgs& a, hipStream_t st);
+
+struct PlanArgs {
+  int B, Hkv, n, w_l;
+  int max_new, max_new_kept;
+  const uint8_t* cls;
+  const uint8_t* policy;
+  const uint32_t* fmask;
+  int32_t* kept_count;
+  int32_t* ring;
+  int32_t* capacity;
+  int64_t* row_offset;
+  int64_t* work_offset;
+  int64_t* totals;
+  int chunk_rows;
+};
+hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
+
+struct GatherArgs {
+  int dtype, D, B, Hkv, n, w_l;
+  const void* K;
+  const void* V;
+  const uint8_t* cls;
+  const uint8_t* policy;
+  const uint32_t* fmask;
+  const int64_t* row_offset;
+  const int32_t* ring;
+  const int64_t* work_offset;
+  void* Kc;
+  void* Vc;
+  int32_t* pos;
+  int32_t* len;
+  int32_t* work;
+  uint32_t* error_word;
+  int chunk_rows;
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+  int dtype, D, B, Hq, Hkv, w_l, p;
+  int64_t n_work;
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const uint8_t* new_class;
+  float* out;
+  float* part;       // [n_work * G * (D + 2)]
+  void* Kc;
+  void* Vc;
+  int32_t* pos;
+  const int64_t* row_offset;
+  int32_t* len;
+  const int32_t* capacity;
+  const int32_t* ring;
+  const uint8_t* policy;
+  const int64_t* work_offset;
+  const int32_t* work;
+  uint32_t* error_word;
+  int chunk_rows;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+constexpr int kDecodeChunk = 64;   // cache rows per decode work item
+constexpr int kMaxGroup = 8;       // query heads per KV head supported by decode
+
+}  // namespace fg

@@ -1,0 +1,260 @@
+// Head-wise profiling of the prompt on gfx950: two MFMA sweeps over the causal
+// score matrix S = Q K^T / sqrt(d).
+//
+// FastGen's profiling (hyper.ai summary of "Model Tells You What to Discard",
+// Method, second paragraph and policy paragraph) needs, per head, the
+// attention map A = softmax(S) only through two per-key reductions: the
+// cumulative attention of each key (column sums of A, which rank the frequent
+// set) and the attention that rows inside the local window give each key (the
+// local band).  With those two vectors and the token classes every policy's
+// retained mass follows in O(n), so A is never stored:
+//
+//   sweep 1 (row statistics): one workgroup per 128 query rows, streaming key
+//     tiles through LDS, keeps an online max / sum of exp2 per query row and
+//     writes lse2_i = log2 sum_j 2^{x_ij} with x_ij = S_ij * log2(e).
+//   sweep 2 (column sums): one workgroup per 128 keys (all query heads of the
+//     KV group), streaming query tiles through LDS, recomputes S, forms
+//     P_ij = 2^{x_ij - lse2_i} in fp32 and accumulates each key's column and
+//     band sums in registers -- no atomics, no partial buffers, a fixed
+//     summation order.
+//
+// MFMA orientation: sweep 1 computes K Q^T tiles so that a lane owns one query
+// row (row reductions stay in-lane); sweep 2 computes Q K^T tiles so that a
+// lane owns one key (column reductions stay in-lane).  The operand held in
+// registers is the one the workgroup owns (Q rows in sweep 1, K rows in
+// sweep 2); the streamed operand is staged in LDS once per workgroup.
+#include "fg_common.h"
+#include "fg_internal.h"
+
+namespace fg {
+
+constexpr int kRowsPerWG = 128;   // sweep 1: 4 waves x 32 query rows
+constexpr int kKeyTile = 64;      // sweep 1: keys staged per LDS tile
+constexpr int kKeysPerWG = 128;   // sweep 2: 4 waves x 32 keys
+constexpr int kRowTile = 64;      // sweep 2: query rows staged per LDS tile
+constexpr int kPadBytes = 16;     // LDS row padding against bank conflicts
+
+// Cooperative copy of `rows` rows of D elements (row r0 onward, zero past n)
+// into an LDS tile whose rows are padded to RB bytes.
+template <typename T, int D, int ROWS>
+__device__ __forceinline__ void stage_rows(unsigned char* lds, const T* src, int r0, int n) {
+  constexpr int kRowBytes = D * (int)sizeof(T);
+  constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per row
+  constexpr int kRB = kRowBytes + kPadBytes;
+  constexpr int kTotal = ROWS * kChunks;
+  for (int c = threadIdx.x; c < kTotal; c += blockDim.x) {
+    const int r = c / kChunks, q = c % kChunks;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r0 + r < n) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(src) +
+                                                         (size_t)(r0 + r) * kRowBytes + q * 16);
+    *reinterpret_cast<uint4*>(lds + r * kRB + q * 16) = v;
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma<T>::op_t lds_operand(const unsigned char* lds, int row, int kk, int lane) {
+  using M = Mfma<T>;
+  constexpr int kRB = D * (int)sizeof(T) + kPadBytes;
+  const int col = kk * M::KS + (lane >> 5) * M::EPL;
+  return *reinterpret_cast<const typename M::op_t*>(lds + row * kRB + col * (int)sizeof(T));
+}
+
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma<T>::op_t global_operand(const T* rowptr, int kk, int lane) {
+  using M = Mfma<T>;
+  const int col = kk * M::KS + (lane >> 5) * M::EPL;
+  return *reinterpret_cast<const typename M::op_t*>(rowptr + col);
+}
+
+// ---------------------------------------------------------------- sweep 1: row statistics
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                       float* __restrict__ lse2, float* __restrict__ lse_out,
+                                                       int Hq, int Hkv, int n, int n_rb, float c) {
+  using M = Mfma<T>;
+  using op_t = typename M::op_t;
+  constexpr int NK = D / M::KS;
+  constexpr int kRB = D * (int)sizeof(T) + kPadBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[kKeyTile * kRB];
+
+  const int nbh = gridDim.x / n_rb;                      // B * Hq
+  const int rb = n_rb - 1 - (int)(blockIdx.x / nbh);     // heaviest row blocks first
+  const int bh = blockIdx.x % nbh;
+  const int b = bh / Hq, hq = bh % Hq, G = Hq / Hkv;
+  const T* Qh = Q + (size_t)bh * n * D;
+  const T* Kh = K + ((size_t)b * Hkv + hq / G) * n * D;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q0 = rb * kRowsPerWG + wave * 32;
+  const int qrow = q0 + (lane & 31);
+
+  op_t qop[NK];
+  {
+    const int qr = qrow < n ? qrow : n - 1;             // clamp: row discarded below
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qop[kk] = global_operand<T, D>(Qh + (size_t)qr * D, kk, lane);
+  }
+
+  float m = kNegBig, l = 0.f;
+  const int kend = min(n, (rb + 1) * kRowsPerWG);
+  for (int k0 = 0; k0 < kend; k0 += kKeyTile) {
+    __syncthreads();
+    stage_rows<T, D, kKeyTile>(ktile, Kh, k0, n);
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < kKeyTile / 32; ++sub) {
+      const int key0 = k0 + sub * 32;
+      if (key0 > q0 + 31 || key0 >= n) continue;          // wave-uniform: tile entirely in the future
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        acc = M::mac(lds_operand<T, D>(ktile, sub * 32 + (lane & 31), kk, lane), qop[kk], acc);
+      const bool edge = (key0 + 31 > q0) || (key0 + 32 > n);
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + acc_row(r, lane);
+          if (key > qrow || key >= n) acc[r] = -INFINITY;
+        }
+      }
+      float tmax = acc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
+      const float m_new = fmaxf(m, tmax * c);
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s += fast_exp2(fmaf(acc[r], c, -m_new));
+      l = fmaf(l, fast_exp2(m - m_new), s);
+      m = m_new;
+    }
+  }
+  // lanes l and l ^ 32 saw disjoint key subsets of the same query row
+  const float m_o = __shfl_xor(m, 32), l_o = __shfl_xor(l, 32);
+  const float M2 = fmaxf(m, m_o);
+  const float L = l * fast_exp2(m - M2) + l_o * fast_exp2(m_o - M2);
+  if (lane < 32 && qrow < n) {
+    const float v = M2 + fast_log2(L);
+    lse2[(size_t)bh * n + qrow] = v;
+    if (lse_out) lse_out[(size_t)bh * n + qrow] = v * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------- sweep 2: column and band sums
+template <typename T, int D>
+__global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                      const float* __restrict__ lse2, float* __restrict__ cum,
+                                                      float* __restrict__ band, int Hq, int Hkv, int n, int n_kb,
+                                                      int w_l, float c) {
+  using M = Mfma<T>;
+  using op_t = typename M::op_t;
+  constexpr int NK = D / M::KS;
+  constexpr int kRB = D * (int)sizeof(T) + kPadBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char qtile[kRowTile * kRB];
+  __shared__ __attribute__((aligned(16))) float lse_t[kRowTile];
+
+  const int nbh = gridDim.x / n_kb;                      // B * Hkv
+  const int kb = (int)(blockIdx.x / nbh);                // key block 0 (most rows) first
+  const int bh = blockIdx.x % nbh;
+  const int b = bh / Hkv, h = bh % Hkv, G = Hq / Hkv;
+  const T* Kh = K + (size_t)bh * n * D;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j0 = kb * kKeysPerWG + wave * 32;            // this wave's first key
+  const int key = j0 + (lane & 31);
+
+  op_t kop[NK];
+  {
+    const int kr = key < n ? key : n - 1;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) kop[kk] = global_operand<T, D>(Kh + (size_t)kr * D, kk, lane);
+  }
+
+  float cum_acc = 0.f, band_acc = 0.f;
+  const int i_begin = kb * kKeysPerWG;
+  for (int g = 0; g < G; ++g) {
+    const size_t qh = (size_t)b * Hq + (size_t)h * G + g;
+    const T* Qg = Q + qh * n * D;
+    const float* lg = lse2 + qh * n;
+    float cum_g = 0.f, band_g = 0.f;
+    for (int i0 = i_begin; i0 < n; i0 += kRowTile) {
+      __syncthreads();
+      stage_rows<T, D, kRowTile>(qtile, Qg, i0, n);
+      for (int t = threadIdx.x; t < kRowTile; t += blockDim.x)
+        lse_t[t] = (i0 + t < n) ? lg[i0 + t] : INFINITY;   // rows past n get P = 0
+      __syncthreads();
+#pragma unroll
+      for (int sub = 0; sub < kRowTile / 32; ++sub) {
+        const int r0 = i0 + sub * 32;
+        if (r0 + 31 < j0 || r0 >= n) continue;            // rows all before this wave's keys
+        f32x16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+          acc = M::mac(lds_operand<T, D>(qtile, sub * 32 + (lane & 31), kk, lane), kop[kk], acc);
+        float lrow[16];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&lse_t[sub * 32 + 8 * a + 4 * (lane >> 5)]);
+          lrow[4 * a + 0] = v[0]; lrow[4 * a + 1] = v[1]; lrow[4 * a + 2] = v[2]; lrow[4 * a + 3] = v[3];
+        }
+        const bool diag = r0 < j0 + 32;
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(acc[r], c, -lrow[r]));
+        if (diag) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (r0 + acc_row(r, lane) < key) p[r] = 0.f;
+        }
+        float ts = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) ts += p[r] + p[r + 1];
+        cum_g += ts;
+        // local band: rows i with 0 <= i - key < w_l
+        if ((r0 + 31) - j0 < w_l) {
+          band_g += ts;                                   // every pair of the tile is inside the band
+        } else if (r0 - (j0 + 31) < w_l) {
+          float tb = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (r0 + acc_row(r, lane) - key < w_l) tb += p[r];
+          band_g += tb;
+        }
+      }
+    }
+    cum_acc += cum_g;
+    band_acc += band_g;
+  }
+  cum_acc += __shfl_xor(cum_acc, 32);
+  band_acc += __shfl_xor(band_acc, 32);
+  if (lane < 32 && key < n) {
+    cum[(size_t)bh * n + key] = cum_acc;
+    band[(size_t)bh * n + key] = band_acc;
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_profile_sweeps_t(const ProfileArgs& a, hipStream_t st) {
+  const int n_rb = (a.n + kRowsPerWG - 1) / kRowsPerWG;
+  const int n_kb = (a.n + kKeysPerWG - 1) / kKeysPerWG;
+  const float c = kLog2e / sqrtf((float)D);
+  timed_begin(FG_K_ROWSTATS, st);
+  rowstats_kernel<T, D><<<dim3(a.B * a.Hq * n_rb), dim3(256), 0, st>>>(
+      (const T*)a.Q, (const T*)a.K, a.lse2, a.lse_out, a.Hq, a.Hkv, a.n, n_rb, c);
+  timed_end(st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  timed_begin(FG_K_COLSUMS, st);
+  colsums_kernel<T, D><<<dim3(a.B * a.Hkv * n_kb), dim3(256), 0, st>>>(
+      (const T*)a.Q, (const T*)a.K, a.lse2, a.cum, a.band, a.Hq, a.Hkv, a.n, n_kb, a.w_l, c);
+  timed_end(st);
+  return hipGetLastError();
+}
+
+hipError_t launch_profile_sweeps(const ProfileArgs& a, hipStream_t st) {
+  if (a.dtype == FG_DTYPE_BF16) {
+    return a.D == 128 ? launch_profile_sweeps_t<__bf16, 128>(a, st) : launch_profile_sweeps_t<__bf16, 64>(a, st);
+  }
+  return a.D == 128 ? launch_profile_sweeps_t<float, 128>(a, st) : launch_profile_sweeps_t<float, 64>(a, st);
+}
+
+}  // namespace fg

@@ -1,0 +1,157 @@
+// Frequent-set selection, per-policy recovery and policy choice, one
+// workgroup per (batch entry, KV head).
+//
+// hyper.ai summary of "Model Tells You What to Discard", Method: the frequent
+// policy keeps the tokens with the largest cumulative attention, budgeted by a
+// ratio r_f (policy paragraph); the shortlist is the nested unions special,
+// +punct, +frequent, +local, full (shortlist equation); the chosen entry is
+// the cheapest whose reconstruction stays within 1 - T of the attention map
+// (constraint equation).
+//
+// * Top-k: radix select on the fp32 bit patterns of cum (non-negative, so the
+//   patterns order like the values), four 8-bit digits from the top, giving
+//   the exact k-th largest pattern; keys above it are taken, and among keys
+//   equal to it the lowest indices (a ballot / popcount prefix in index order).
+// * Recovery: every pair (i, j) falls at the first shortlist level that keeps
+//   it, so the mass a level adds is a column-sum identity over keys:
+//   special keys add cum_j at level 0, punct keys at level 1, frequent keys at
+//   level 2, and every other key adds only its local band sum at level 3.
+//   The O(n) reduction runs in fp64.
+#include "fg_common.h"
+#include "fg_internal.h"
+
+namespace fg {
+
+constexpr int kSelThreads = 1024;
+
+__device__ __forceinline__ double block_sum(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0)
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  return t;   // valid in thread 0
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ cum, const float* __restrict__ band,
+                                                             const uint8_t* __restrict__ cls, int Hkv, int n, int G,
+                                                             int k_f, double T, uint32_t* __restrict__ fmask,
+                                                             float* __restrict__ recovery, uint8_t* __restrict__ policy) {
+  __shared__ unsigned hist[256];
+  __shared__ unsigned s_sel, s_rem;
+  __shared__ int wave_cnt[kSelThreads / 64];
+  __shared__ double red[kSelThreads / 64];
+
+  const int bh = blockIdx.x, b = bh / Hkv;
+  const float* cu = cum + (size_t)bh * n;
+  const float* bd = band + (size_t)bh * n;
+  const uint8_t* cl = cls + (size_t)b * n;
+  const int nw = (n + 31) / 32;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n_waves = blockDim.x >> 6;
+
+  // mode 0: nothing selected, 1: everything, 2: threshold + ties
+  const int mode = k_f <= 0 ? 0 : (k_f >= n ? 1 : 2);
+  uint32_t thr = 0;
+  int take_eq = 0;
+  if (mode == 2) {
+    uint32_t prefix = 0, pmask = 0;
+    int remaining = k_f;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
+      __syncthreads();
+      for (int j = tid; j < n; j += blockDim.x) {
+        const uint32_t u = __float_as_uint(cu[j]);
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int acc = 0;
+        for (int bin = 255; bin >= 0; --bin) {
+          const int h = (int)hist[bin];
+          if (acc + h >= remaining) { s_sel = (unsigned)bin; s_rem = (unsigned)(remaining - acc); break; }
+          acc += h;
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_sel << shift;
+      pmask |= 0xFFu << shift;
+      remaining = (int)s_rem;
+      __syncthreads();
+    }
+    thr = prefix;
+    take_eq = remaining;
+  }
+
+  double m_s = 0.0, m_p = 0.0, m_f = 0.0, m_b = 0.0;
+  int run = 0;                                   // equal-to-threshold keys seen at lower indices
+  for (int base = 0; base < n; base += blockDim.x) {
+    const int j = base + tid;
+    const bool valid = j < n;
+    const float v = valid ? cu[j] : 0.f;
+    const uint32_t u = __float_as_uint(v);
+    bool sel = (mode == 1) && valid;
+    if (mode == 2) {
+      const bool eq = valid && u == thr;
+      const unsigned long long bal = __ballot(eq);
+      if (lane == 0) wave_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      int before = 0, total = 0;
+      for (int w = 0; w < n_waves; ++w) {
+        const int cw = wave_cnt[w];
+        before += (w < wave) ? cw : 0;
+        total += cw;
+      }
+      const int rank = run + before + __popcll(bal & ((1ull << lane) - 1ull));
+      sel = (valid && u > thr) || (eq && rank < take_eq);
+      run += total;
+      __syncthreads();
+    }
+    const unsigned long long sb = __ballot(sel);
+    if (lane == 0) {
+      const int w0 = (base + wave * 64) / 32;
+      if (w0 < nw) fmask[(size_t)bh * nw + w0] = (uint32_t)(sb & 0xFFFFFFFFull);
+      if (w0 + 1 < nw) fmask[(size_t)bh * nw + w0 + 1] = (uint32_t)(sb >> 32);
+    }
+    if (valid) {
+      const uint8_t c = cl[j];
+      if (c == kSpecial) m_s += v;
+      else if (c == kPunct) m_p += v;
+      else if (sel) m_f += v;
+      else m_b += bd[j];
+    }
+  }
+  m_s = block_sum(m_s, red);
+  m_p = block_sum(m_p, red);
+  m_f = block_sum(m_f, red);
+  m_b = block_sum(m_b, red);
+  if (tid == 0) {
+    const double denom = (double)G * (double)n;
+    double R[5];
+    R[0] = m_s / denom;
+    R[1] = (m_s + m_p) / denom;
+    R[2] = (m_s + m_p + m_f) / denom;
+    R[3] = (m_s + m_p + m_f + m_b) / denom;
+    R[4] = 1.0;
+    int pol = 4;
+    for (int k = 0; k < 5; ++k)
+      if (R[k] >= T) { pol = k; break; }
+    for (int k = 0; k < 5; ++k) recovery[(size_t)bh * 5 + k] = (float)R[k];
+    policy[bh] = (uint8_t)pol;
+  }
+}
+
+hipError_t launch_select(const ProfileArgs& a, hipStream_t st) {
+  timed_begin(FG_K_SELECT, st);
+  select_kernel<<<dim3(a.B * a.Hkv), dim3(kSelThreads), 0, st>>>(a.cum, a.band, a.cls, a.Hkv, a.n, a.Hq / a.Hkv,
+                                                                  a.k_f, a.T, a.fmask, a.recovery, a.policy);
+  timed_end(st);
+  return hipGetLastError();
+}
+
+}  // namespace fg

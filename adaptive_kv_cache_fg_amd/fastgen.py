@@ -1,0 +1,283 @@
+"""Thin Python binding of libfastgen (ctypes).
+
+Argument marshalling only: torch tensors provide device memory and the current
+HIP stream; every step of profiling, compaction and decode runs in the HIP
+kernels behind the C ABI declared in include/fastgen.h.  If the shared library
+is missing this module raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from pathlib import Path
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+_HERE = Path(__file__).resolve().parent
+LIB_PATH = _HERE / "libfastgen.so"
+
+FG_OK = 0
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
+          4: "cache capacity exceeded", 5: "HIP error"}
+DTYPE = {torch.bfloat16: 0, torch.float32: 1}
+KERNEL_NAMES = ["profile_rowstats", "profile_colsums", "profile_select", "compact_plan", "compact_scan",
+                "compact_gather", "compact_worklist", "decode_partial", "decode_combine"]
+
+
+class FgShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class FgParams(ctypes.Structure):
+    _fields_ = [("r_l", ctypes.c_double), ("r_f", ctypes.c_double), ("T", ctypes.c_double)]
+
+
+class FgCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("row_offset", ctypes.c_void_p), ("len", ctypes.c_void_p), ("capacity", ctypes.c_void_p),
+                ("ring", ctypes.c_void_p), ("policy", ctypes.c_void_p), ("work_offset", ctypes.c_void_p),
+                ("work", ctypes.c_void_p), ("error_word", ctypes.c_void_p),
+                ("total_rows", ctypes.c_int64), ("n_work", ctypes.c_int64),
+                ("n_prompt", ctypes.c_int32), ("w_l", ctypes.c_int32), ("next_pos", ctypes.c_int32),
+                ("shape", FgShape)]
+
+
+class FastGenError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfastgen.so (built in-tree by ``python -m adaptive_kv_cache_fg_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m adaptive_kv_cache_fg_amd.build`")
+    L = ctypes.CDLL(str(LIB_PATH))
+    P, S, I32, I64, D = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    sh, pa, ca = ctypes.POINTER(FgShape), ctypes.POINTER(FgParams), ctypes.POINTER(FgCache)
+    L.fg_profile_workspace_size.argtypes, L.fg_profile_workspace_size.restype = [sh], S
+    L.fg_profile.argtypes = [sh, pa, P, P, P, P, P, P, P, P, P, P, S, P]
+    L.fg_profile.restype = ctypes.c_int
+    L.fg_compact_plan.argtypes = [sh, pa, P, P, P, I32, I32, P, P, P, P, P, P, P]
+    L.fg_compact_plan.restype = ctypes.c_int
+    L.fg_compact.argtypes = [sh, pa, P, P, P, P, P, ca, P]
+    L.fg_compact.restype = ctypes.c_int
+    L.fg_decode_workspace_size.argtypes, L.fg_decode_workspace_size.restype = [ca], S
+    L.fg_decode_step.argtypes = [ca, P, P, P, P, P, P, S, P]
+    L.fg_decode_step.restype = ctypes.c_int
+    L.fg_cache_error.argtypes = [ca, ctypes.POINTER(ctypes.c_uint32), P]
+    L.fg_cache_error.restype = ctypes.c_int
+    L.fg_status_string.argtypes, L.fg_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+    L.fg_last_error.argtypes, L.fg_last_error.restype = [], ctypes.c_char_p
+    L.fg_decode_chunk_rows.argtypes, L.fg_decode_chunk_rows.restype = [], I32
+    L.fg_kernel_timing_enable.argtypes, L.fg_kernel_timing_enable.restype = [ctypes.c_int], None
+    L.fg_kernel_timing_read.argtypes = [ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_float), I32]
+    L.fg_kernel_timing_read.restype = I32
+    L.fg_kernel_name.argtypes, L.fg_kernel_name.restype = [I32], ctypes.c_char_p
+    _ = D, I64
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != FG_OK:
+        raise FastGenError(status, where, lib().fg_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def make_shape(Q: torch.Tensor, K: torch.Tensor) -> FgShape:
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (B, Hkv, n, d):
+        raise ValueError(f"K shape {tuple(K.shape)} does not match Q {tuple(Q.shape)}")
+    if Q.dtype not in DTYPE or K.dtype != Q.dtype:
+        raise ValueError("Q and K must both be bf16 or both fp32")
+    return FgShape(B, Hq, Hkv, n, d, DTYPE[Q.dtype])
+
+
+@dataclass
+class Profile:
+    policy: torch.Tensor        # [B, Hkv] uint8
+    cum: torch.Tensor           # [B, Hkv, n] fp32
+    recovery: torch.Tensor      # [B, Hkv, 5] fp32
+    freq_mask: torch.Tensor     # [B, Hkv, ceil(n/32)] int32 (bit patterns of u32 words)
+    lse: Optional[torch.Tensor]   # [B, Hq, n] fp32 natural log-sum-exp
+    band: Optional[torch.Tensor]  # [B, Hkv, n] fp32
+    r_l: float
+    r_f: float
+    T: float
+
+    def frequent(self) -> np.ndarray:
+        """Host bool array [B, Hkv, n] of the frequent set (synchronises)."""
+        n = self.cum.shape[-1]
+        words = self.freq_mask.cpu().numpy().view(np.uint32)
+        bits = (words[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1
+        return bits.reshape(*words.shape[:-1], -1)[..., :n].astype(bool)
+
+
+def profile(Q: torch.Tensor, K: torch.Tensor, token_class: torch.Tensor, r_l: float, r_f: float, T: float,
+            want_lse: bool = False, want_band: bool = False) -> Profile:
+    """fg_profile: per (b, KV head) cumulative scores, frequent set, recovery R_0..R_4 and policy."""
+    _need(Q, "Q")
+    _need(K, "K")
+    _need(token_class, "token_class", torch.uint8)
+    shape = make_shape(Q, K)
+    B, Hq, n, _ = Q.shape
+    Hkv = K.shape[1]
+    dev = Q.device
+    policy = torch.empty((B, Hkv), dtype=torch.uint8, device=dev)
+    cum = torch.empty((B, Hkv, n), dtype=torch.float32, device=dev)
+    rec = torch.empty((B, Hkv, 5), dtype=torch.float32, device=dev)
+    fmask = torch.empty((B, Hkv, (n + 31) // 32), dtype=torch.int32, device=dev)
+    lse = torch.empty((B, Hq, n), dtype=torch.float32, device=dev) if want_lse else None
+    band = torch.empty((B, Hkv, n), dtype=torch.float32, device=dev) if want_band else None
+    L = lib()
+    ws_bytes = L.fg_profile_workspace_size(ctypes.byref(shape))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    params = FgParams(r_l, r_f, T)
+    _check(L.fg_profile(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), _ptr(K), _ptr(token_class),
+                        _ptr(policy), _ptr(cum), _ptr(rec), _ptr(fmask), _ptr(lse), _ptr(band),
+                        _ptr(ws), ws_bytes, _stream()), "fg_profile")
+    return Profile(policy, cum, rec, fmask, lse, band, r_l, r_f, T)
+
+
+class Cache:
+    """Head-specific ragged KV cache of one layer (owns its device tensors)."""
+
+    def __init__(self, shape: FgShape, tensors: dict, struct: FgCache, kept_count: torch.Tensor):
+        self.shape = shape
+        self.t = tensors
+        self.c = struct
+        self.kept_count = kept_count
+        self._ws = None
+
+    @property
+    def next_pos(self) -> int:
+        return self.c.next_pos
+
+    def decode_step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    new_class: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """fg_decode_step for the token at position next_pos; returns out [B, Hq, d] fp32."""
+        s = self.shape
+        dt = self.t["k"].dtype
+        _need(q, "q", dt)
+        _need(k_new, "k_new", dt)
+        _need(v_new, "v_new", dt)
+        if q.shape != (s.batch, s.n_q_heads, s.head_dim) or k_new.shape != (s.batch, s.n_kv_heads, s.head_dim) \
+                or v_new.shape != k_new.shape:
+            raise ValueError("decode input shapes do not match the cache")
+        if new_class is not None:
+            _need(new_class, "new_class", torch.uint8)
+            if new_class.shape != (s.batch,):
+                raise ValueError("new_class must be [B]")
+        if out is None:
+            out = torch.empty((s.batch, s.n_q_heads, s.head_dim), dtype=torch.float32, device=q.device)
+        L = lib()
+        if self._ws is None:
+            nb = L.fg_decode_workspace_size(ctypes.byref(self.c))
+            self._ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+        _check(L.fg_decode_step(ctypes.byref(self.c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(new_class),
+                                _ptr(out), _ptr(self._ws), self._ws.numel(), _stream()), "fg_decode_step")
+        return out
+
+    def kept_positions(self) -> List[np.ndarray]:
+        """Sorted kept-index list of every (b, KV head), from the device cache (synchronises)."""
+        ro = self.t["row_offset"].cpu().numpy()
+        ln = self.t["len"].cpu().numpy()
+        pos = self.t["pos"].cpu().numpy()
+        out = []
+        for h in range(len(ln)):
+            p = pos[ro[h]: ro[h] + ln[h]]
+            out.append(np.sort(p[p >= 0]).astype(np.int64))
+        return out
+
+    def rows(self, head: int):
+        """(pos, k, v) of the rows in use of one head, device order (synchronises)."""
+        ro = int(self.t["row_offset"][head].item())
+        ln = int(self.t["len"][head].item())
+        return (self.t["pos"][ro:ro + ln].cpu().numpy(), self.t["k"][ro:ro + ln], self.t["v"][ro:ro + ln])
+
+    def error_bits(self) -> int:
+        bits = ctypes.c_uint32(0)
+        st = lib().fg_cache_error(ctypes.byref(self.c), ctypes.byref(bits), _stream())
+        if st not in (FG_OK, 4):
+            _check(st, "fg_cache_error")
+        return int(bits.value)
+
+
+def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: Profile, n_q_heads: int,
+            max_new_tokens: int, max_new_kept: Optional[int] = None) -> Cache:
+    """fg_compact_plan + one read of the totals + fg_compact: the ragged cache of one layer."""
+    _need(K, "K")
+    _need(V, "V", K.dtype)
+    B, Hkv, n, d = K.shape
+    if V.shape != K.shape:
+        raise ValueError("V must match K")
+    shape = FgShape(B, n_q_heads, Hkv, n, d, DTYPE[K.dtype])
+    params = FgParams(prof.r_l, prof.r_f, prof.T)
+    max_new_kept = max_new_tokens if max_new_kept is None else max_new_kept
+    H = B * Hkv
+    dev = K.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    i64 = dict(dtype=torch.int64, device=dev)
+    kept_count, ring, capacity = torch.empty(H, **i32), torch.empty(H, **i32), torch.empty(H, **i32)
+    row_offset, work_offset, totals = torch.empty(H + 1, **i64), torch.empty(H + 1, **i64), torch.empty(2, **i64)
+    L = lib()
+    _check(L.fg_compact_plan(ctypes.byref(shape), ctypes.byref(params), _ptr(token_class), _ptr(prof.policy),
+                             _ptr(prof.freq_mask), int(max_new_tokens), int(max_new_kept), _ptr(kept_count),
+                             _ptr(ring), _ptr(capacity), _ptr(row_offset), _ptr(work_offset), _ptr(totals),
+                             _stream()), "fg_compact_plan")
+    total_rows, n_work = (int(x) for x in totals.cpu().tolist())     # the one host synchronisation
+    t = {
+        "k": torch.empty((max(total_rows, 1), d), dtype=K.dtype, device=dev),
+        "v": torch.empty((max(total_rows, 1), d), dtype=K.dtype, device=dev),
+        "pos": torch.empty(max(total_rows, 1), **i32),
+        "row_offset": row_offset, "len": torch.empty(H, **i32), "capacity": capacity, "ring": ring,
+        "policy": prof.policy.reshape(-1), "work_offset": work_offset,
+        "work": torch.empty(max(2 * n_work, 2), **i32), "error_word": torch.empty(1, **i32),
+    }
+    c = FgCache()
+    for name in ("k", "v", "pos", "row_offset", "len", "capacity", "ring", "policy", "work_offset", "work",
+                 "error_word"):
+        setattr(c, name, t[name].data_ptr())
+    c.total_rows, c.n_work = total_rows, n_work
+    _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),
+                        _ptr(prof.policy), _ptr(prof.freq_mask), ctypes.byref(c), _stream()), "fg_compact")
+    return Cache(shape, t, c, kept_count)
+
+
+def timing_enable(on: bool = True) -> None:
+    lib().fg_kernel_timing_enable(1 if on else 0)
+
+
+def timing_read(max_records: int = 1 << 16):
+    """[(kernel name, ms)] of the launches bracketed since the last read (synchronises)."""
+    ids = (ctypes.c_int32 * max_records)()
+    ms = (ctypes.c_float * max_records)()
+    k = lib().fg_kernel_timing_read(ids, ms, max_records)
+    return [(KERNEL_NAMES[ids[i]], float(ms[i])) for i in range(k)]

@@ -1,0 +1,231 @@
+/*
+ * libfastgen -- FastGen's head-wise attention profiling, KV compaction and
+ * compressed-cache decode on AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: the hyper.ai summary pages of "Model Tells You What to
+ * Discard: Adaptive KV Cache Compression for LLMs" (Ge et al., ICLR 2024),
+ * section Method.  The calls mirror its two-phase inference: profile every
+ * attention head while the prompt is encoded, build head-specific caches
+ * K_C, V_C = f(K, V, C), then generate with those caches, reusing the policy
+ * picked on the prompt for every new token.
+ *
+ * Conventions (every call):
+ *  - Pointers are DEVICE memory unless marked [host].  The caller owns all
+ *    memory; the library never allocates or frees device memory.  Size queries
+ *    tell the caller what to allocate.
+ *  - Every call only enqueues work on the given stream and returns; nothing is
+ *    synchronised except fg_cache_error (documented below).
+ *  - All argument checks run on the host before any launch.  On failure the
+ *    call returns a status, writes nothing and launches nothing; the reason is
+ *    available from fg_last_error() (thread-local string).
+ *  - A failed kernel launch returns FG_ERR_HIP.  No C++ exception crosses this
+ *    interface.
+ *  - Supported: head_dim in {64, 128}; dtype bf16 or fp32 (inputs and caches);
+ *    n_q_heads % n_kv_heads == 0 with group G = n_q_heads / n_kv_heads <= 8;
+ *    seq_len >= 1; 0 < T <= 1; 0 <= r_l, r_f <= 1.  Tensors are contiguous,
+ *    row-major, 16-byte aligned.
+ *
+ * Notation: B batch, Hq / Hkv query / KV heads, n prompt length, d head_dim,
+ * k_f = floor(r_f * n) frequent keys, w_l = floor(r_l * n) local window
+ * (both in fp64).  Levels / policies: 0 special, 1 special+punct,
+ * 2 special+punct+frequent, 3 special+punct+frequent+local, 4 full.
+ */
+#ifndef FASTGEN_H
+#define FASTGEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FG_OK = 0,
+  FG_ERR_INVALID_ARG = 1,   /* bad pointer, shape or parameter */
+  FG_ERR_UNSUPPORTED = 2,   /* valid but not supported (head_dim, dtype, G > 8) */
+  FG_ERR_WORKSPACE = 3,     /* workspace missing or too small */
+  FG_ERR_CAPACITY = 4,      /* a cache ran out of rows (see fg_cache_error) */
+  FG_ERR_HIP = 5            /* a HIP runtime call or launch failed */
+} fg_status;
+
+typedef enum { FG_DTYPE_BF16 = 0, FG_DTYPE_F32 = 1 } fg_dtype;
+
+enum { FG_TOKEN_NORMAL = 0, FG_TOKEN_SPECIAL = 1, FG_TOKEN_PUNCT = 2 };
+
+enum {
+  FG_POLICY_SPECIAL = 0,
+  FG_POLICY_SPECIAL_PUNCT = 1,
+  FG_POLICY_SPF = 2,
+  FG_POLICY_SPFL = 3,
+  FG_POLICY_FULL = 4
+};
+
+/* [host] shape of one attention layer's prompt */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, seq_len, head_dim;
+  int32_t dtype; /* fg_dtype */
+} fg_shape;
+
+/* [host] budgets and recover ratio (Method, policy paragraph and constraint equation) */
+typedef struct {
+  double r_l, r_f, T;
+} fg_params;
+
+/* ------------------------------------------------------------------ profiling */
+
+/* Bytes of workspace fg_profile needs: per-row log-sum-exp [B*Hq*n] fp32 and
+ * the banded column sums [B*Hkv*n] fp32. */
+size_t fg_profile_workspace_size(const fg_shape* shape);
+
+/*
+ * fg_profile -- head-wise profiling of one layer's prompt (Method, second
+ * paragraph: the attention map A = softmax(Q K^T) and the policy argmin under
+ * |A - softmax(Q K_C^T)| <= 1 - T; policy paragraph; shortlist equation).
+ *
+ * Per (batch entry b, KV head h) with query heads g of its group:
+ *   A^g_ij   = softmax_j(q^g_i . k_j / sqrt(d)) over j <= i (causal);
+ *   cum[j]   = sum_g sum_{i >= j} A^g_ij   (cumulative attention score);
+ *   F        = the k_f keys with the largest cum, ties to the lower index;
+ *   level(i, j) = 0 special(j), 1 punct(j), 2 j in F, 3 i - j < w_l, else 4;
+ *   R_k      = (1 / (G n)) sum_g sum_i sum_{j : level(i,j) <= k} A^g_ij
+ *              (retained share of attention; per row this is one minus half
+ *              the L1 distance of the constraint), R_4 = 1;
+ *   policy   = min { k : R_k >= T }.
+ *
+ * Q [B,Hq,n,d], K [B,Hkv,n,d] (dtype of shape), post-rotary.
+ * token_class [B,n] u8 (FG_TOKEN_*).
+ * Outputs: policy [B*Hkv] u8; cum_score [B*Hkv*n] fp32; recovery [B*Hkv*5] fp32;
+ *          freq_mask [B*Hkv*ceil(n/32)] u32, bit (j % 32) of word j / 32 set
+ *          iff j in F.
+ * Optional outputs (NULL to skip): lse_out [B*Hq*n] fp32, natural-log
+ *          log-sum-exp of each row's scaled scores; band_out [B*Hkv*n] fp32,
+ *          sum_g sum_{j <= i < j + w_l} A^g_ij.
+ * workspace: at least fg_profile_workspace_size(shape) bytes.
+ */
+fg_status fg_profile(const fg_shape* shape, const fg_params* params,
+                     const void* Q, const void* K, const uint8_t* token_class,
+                     uint8_t* policy, float* cum_score, float* recovery, uint32_t* freq_mask,
+                     float* lse_out, float* band_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ compaction */
+
+/*
+ * Ragged per-(b, KV head) cache: a POD view of caller-owned buffers.  Head
+ * hd = b * Hkv + h owns rows [row_offset[hd], row_offset[hd+1]).  The first
+ * ring[hd] rows are the local window's ring (policy 3 only: w_l - 1 slots,
+ * slot = position mod (w_l - 1)); after them come the permanent rows in the
+ * order they were kept.  Rows [0, len[hd]) are in use; a row whose pos is -1
+ * is empty.  The kept-index list of a head is the sorted set of pos >= 0 over
+ * its rows in use.
+ */
+typedef struct {
+  void* k;                 /* [total_rows, d] cache dtype */
+  void* v;                 /* [total_rows, d] */
+  int32_t* pos;            /* [total_rows] absolute token position, -1 = empty */
+  const int64_t* row_offset;  /* [B*Hkv + 1] */
+  int32_t* len;            /* [B*Hkv] rows in use (ring + permanent) */
+  const int32_t* capacity; /* [B*Hkv] */
+  const int32_t* ring;     /* [B*Hkv] ring slots */
+  const uint8_t* policy;   /* [B*Hkv] */
+  const int64_t* work_offset; /* [B*Hkv + 1] decode work items per head (prefix) */
+  int32_t* work;           /* [n_work * 2] decode work items: (head, first row) */
+  uint32_t* error_word;    /* [1] sticky device error bits: 1 = capacity overflow */
+  int64_t total_rows;      /* [host] rows allocated */
+  int64_t n_work;          /* [host] work items */
+  int32_t n_prompt;        /* [host] n */
+  int32_t w_l;             /* [host] local window */
+  int32_t next_pos;        /* [host] position of the next generated token (starts at n) */
+  fg_shape shape;          /* [host] */
+} fg_cache;
+
+/* Rows of decode work per item (the split-K chunk of fg_decode_step). */
+int32_t fg_decode_chunk_rows(void);
+
+/*
+ * fg_compact_plan -- size the head-specific caches (Method, second paragraph:
+ * K_C, V_C = f(K, V, C)).  Per head: the prompt keys that the first generated
+ * token keeps, {j < n : level(n, j) <= policy}, split into permanent rows
+ * (special, punct, frequent, or everything for policy 4) and ring rows
+ * (policy 3: normal keys inside the local window).
+ * Inputs from fg_profile: policy, freq_mask.  max_new_tokens: generated tokens
+ * the caches must hold room for; max_new_kept (<= max_new_tokens): upper bound
+ * on generated special/punct tokens (room for heads with policy < 4).
+ * Outputs: kept_count [B*Hkv] prompt keys kept; ring [B*Hkv]; capacity [B*Hkv]
+ * = ring + permanent prompt rows + (policy 4 ? max_new_tokens : max_new_kept);
+ * row_offset [B*Hkv+1] and work_offset [B*Hkv+1] (exclusive prefix sums);
+ * totals [2] = {total rows, total work items}.  The caller reads totals to the
+ * host (the one synchronisation of the path) to allocate the cache.
+ */
+fg_status fg_compact_plan(const fg_shape* shape, const fg_params* params,
+                          const uint8_t* token_class, const uint8_t* policy,
+                          const uint32_t* freq_mask, int32_t max_new_tokens, int32_t max_new_kept,
+                          int32_t* kept_count, int32_t* ring, int32_t* capacity,
+                          int64_t* row_offset, int64_t* work_offset, int64_t* totals,
+                          hipStream_t stream);
+
+/*
+ * fg_compact -- gather the kept K/V rows of every head into the cache,
+ * permanent rows in ascending position; fill pos, len, the decode work list,
+ * and clear error_word.  cache must hold the buffers sized from
+ * fg_compact_plan (k, v, pos with total_rows rows; work with n_work items)
+ * and its row_offset, capacity, ring, policy, work_offset arrays; n_prompt,
+ * w_l and next_pos are set by this call.  Rows are byte copies.
+ */
+fg_status fg_compact(const fg_shape* shape, const fg_params* params,
+                     const void* K, const void* V, const uint8_t* token_class,
+                     const uint8_t* policy, const uint32_t* freq_mask,
+                     fg_cache* cache, hipStream_t stream);
+
+/* ------------------------------------------------------------------ decode */
+
+/* Workspace bytes for fg_decode_step: n_work * G * (d + 2) fp32 partials. */
+size_t fg_decode_workspace_size(const fg_cache* cache);
+
+/*
+ * fg_decode_step -- one generated token at position p = cache->next_pos for
+ * every (b, KV head) (Method, first paragraph: generation with head-specific
+ * caches; stability paragraph: the prompt's policy is reused).
+ *   attend set  = cache rows in use with pos >= 0, plus the new token itself
+ *                 when level(p, p) <= policy;
+ *   out^g       = softmax(q^g . k_j / sqrt(d)) weighted sum of v_j over it
+ *                 (zeros if empty);
+ *   afterwards the cache holds {j <= p : level(p + 1, j) <= policy}: the new
+ *   row is appended (special; punct if policy >= 1; normal if policy 4) or
+ *   written to ring slot p mod (w_l - 1) (normal, policy 3), and the ring slot
+ *   of position p + 1 - w_l is freed.
+ * q [B,Hq,d], k_new / v_new [B,Hkv,d] (cache dtype); new_class [B] u8 or NULL
+ * (all normal); out [B,Hq,d] fp32.  An append beyond capacity is skipped and
+ * sets bit 1 of error_word.  Increments cache->next_pos.
+ */
+fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
+                         const uint8_t* new_class, float* out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Synchronises the stream and reads error_word: FG_OK, or FG_ERR_CAPACITY
+ * when an append was dropped.  *bits_out [host] receives the raw bits if not NULL. */
+fg_status fg_cache_error(const fg_cache* cache, uint32_t* bits_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------ diagnostics */
+
+const char* fg_status_string(fg_status status);
+const char* fg_last_error(void);
+
+/* Kernel timing: when enabled, every launch is bracketed by HIP events on its
+ * stream.  fg_kernel_timing_read synchronises those events and returns up to
+ * max records (kernel id, milliseconds) accumulated since the last read. */
+enum {
+  FG_K_ROWSTATS = 0, FG_K_COLSUMS = 1, FG_K_SELECT = 2, FG_K_PLAN = 3, FG_K_SCAN = 4,
+  FG_K_GATHER = 5, FG_K_WORKLIST = 6, FG_K_DECODE_PARTIAL = 7, FG_K_DECODE_COMBINE = 8,
+  FG_K_COUNT = 9
+};
+void fg_kernel_timing_enable(int enable);
+int32_t fg_kernel_timing_read(int32_t* kernel_ids, float* ms, int32_t max);
+const char* fg_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FASTGEN_H */

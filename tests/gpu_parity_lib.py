@@ -1,0 +1,189 @@
+"""Shared machinery of the GPU parity tests: upload seeded inputs, run the HIP
+path through the C ABI, run the oracle on the same inputs, compare.
+
+Tolerances (fixed by the parity contract, written once here):
+* kept-index lists, frequent sets, policies: exact, except heads the oracle
+  flags -- a recovery within 1e-4 of T (near-T) or a k-th cumulative score whose
+  relative gap to the next is below TIE_TAU (top-k tie); flagged heads get the
+  weaker checks below and the downstream steps run in forced mode (the oracle
+  takes the GPU's policy and frequent set);
+* recovery: 1e-4 absolute;
+* decode outputs: max |gpu - oracle| <= 2e-3 * max |oracle| per output vector for
+  bf16 inputs, 1e-5 for fp32;
+* the cache after every decode step: the exact set of kept positions.
+"""
+from __future__ import annotations
+
+import math
+import sys
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from adaptive_kv_cache_fg_amd import fastgen as fg
+from oracle import fastgen_ref as ref
+from synth import inputs as syn
+
+TIE_TAU = 3e-5
+REC_TOL = 1e-4
+DEC_TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+def upload(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        bits = syn.bf16_bits(x)
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class HeadReport:
+    b: int
+    h: int
+    kind: str
+    policy_gpu: int
+    policy_ref: int
+    near_T: bool
+    topk_tie: bool
+    rec_err: float
+    cum_rel_err: float
+    lse_err: float
+
+
+@dataclass
+class CaseReport:
+    heads: List[HeadReport] = field(default_factory=list)
+    dec_err: float = 0.0
+    flagged: int = 0
+
+
+def allowed_policies(R: np.ndarray, T: float, ref_policy: int) -> set:
+    ok = {ref_policy}
+    for k in range(4):
+        if abs(R[k] - T) <= ref.NEAR_T_WINDOW:
+            ok.add(k)
+            ok.add(k + 1)
+    return ok
+
+
+def eps_topk_ok(cum_ref: np.ndarray, F_gpu: np.ndarray, k_f: int, tau: float) -> bool:
+    """Every chosen key scores at least the k-th minus the window, every rejected one at most
+    the (k+1)-th plus the window (oracle scores)."""
+    if F_gpu.sum() != min(max(k_f, 0), len(cum_ref)):
+        return False
+    if k_f <= 0 or k_f >= len(cum_ref):
+        return True
+    s = np.sort(cum_ref)[::-1]
+    sk, sk1 = s[k_f - 1], s[k_f]
+    w = tau * sk + 2.0 ** -100
+    return bool(np.all(cum_ref[F_gpu] >= sk - w) and np.all(cum_ref[~F_gpu] <= sk1 + w))
+
+
+def run_case(spec: syn.ConfigSpec, layer: int = 0, T: Optional[float] = None, steps: Optional[int] = None,
+             batch=None, seed=None, check_decode: bool = True) -> CaseReport:
+    T = spec.T[0] if T is None else T
+    steps = spec.decode_steps if steps is None else steps
+    log(f"[case] cfg={spec.cfg_id} {spec.name} B={spec.batch} Hq={spec.n_q_heads} Hkv={spec.n_kv_heads} "
+        f"n={spec.seq_len} d={spec.head_dim} {spec.dtype} T={T} steps={steps}")
+    li = syn.make_layer(spec, layer, batch=batch, seed=seed)
+    B, Hq, n, d = li.Q.shape
+    Hkv = li.K.shape[1]
+    G = Hq // Hkv
+    Qd, Kd, Vd = upload(li.Q, spec.dtype), upload(li.K, spec.dtype), upload(li.V, spec.dtype)
+    cls_d = torch.from_numpy(li.token_class).cuda()
+    prof = fg.profile(Qd, Kd, cls_d, spec.r_l, spec.r_f, T, want_lse=True, want_band=True)
+    torch.cuda.synchronize()
+    pol_g = prof.policy.cpu().numpy()
+    cum_g = prof.cum.cpu().numpy().astype(np.float64)
+    band_g = prof.band.cpu().numpy().astype(np.float64)
+    lse_g = prof.lse.cpu().numpy().astype(np.float64)
+    rec_g = prof.recovery.cpu().numpy().astype(np.float64)
+    F_g = prof.frequent()
+    rep = CaseReport()
+    forced = {}
+    for b in range(B):
+        for h in range(Hkv):
+            pr = ref.profile_head(li.Q[b, h * G:(h + 1) * G], li.K[b, h], li.token_class[b], spec.r_l, spec.r_f, T,
+                                  tau=TIE_TAU)
+            lse_err = float(np.max(np.abs(lse_g[b, h * G:(h + 1) * G] - pr.lse)))
+            cum_rel = float(np.max(np.abs(cum_g[b, h] - pr.cum) / np.maximum(pr.cum, 1e-30)))
+            rec_err = float(np.max(np.abs(rec_g[b, h] - pr.R)))
+            # checks
+            assert lse_err <= 2e-4 + 2e-6 * float(np.max(np.abs(pr.lse))), (b, h, lse_err)
+            assert np.allclose(cum_g[b, h], pr.cum, rtol=2e-4, atol=1e-6 * G), (b, h, cum_rel)
+            assert np.allclose(band_g[b, h], pr.band, rtol=2e-4, atol=1e-6 * G), (b, h)
+            assert rec_err <= REC_TOL, (b, h, rec_g[b, h], pr.R)
+            assert np.all(np.diff(rec_g[b, h]) >= -1e-6) and rec_g[b, h, 4] == 1.0
+            if pr.topk_tie:
+                assert eps_topk_ok(pr.cum, F_g[b, h], pr.k_f, TIE_TAU), (b, h)
+            else:
+                assert np.array_equal(F_g[b, h], pr.F), (b, h, np.flatnonzero(F_g[b, h] != pr.F)[:10])
+            if pr.near_T or pr.topk_tie:
+                rep.flagged += 1
+                assert int(pol_g[b, h]) in allowed_policies(pr.R, T, pr.policy) or pr.topk_tie, (b, h)
+            else:
+                assert int(pol_g[b, h]) == pr.policy, (b, h, rec_g[b, h], pr.R)
+            # the GPU's own decision follows from its own recovery values
+            own = next(k for k in range(5) if rec_g[b, h, k] >= T or k == 4)
+            if not np.any(np.abs(rec_g[b, h, :4] - T) < 1e-6):
+                assert int(pol_g[b, h]) == own, (b, h, rec_g[b, h])
+            forced[(b, h)] = (int(pol_g[b, h]), F_g[b, h].copy(), pr)
+            rep.heads.append(HeadReport(b, h, li.types[h], int(pol_g[b, h]), pr.policy, pr.near_T, pr.topk_tie,
+                                        rec_err, cum_rel, lse_err))
+    max_new = steps
+    cache = fg.compact(Kd, Vd, cls_d, prof, Hq, max_new_tokens=max_new, max_new_kept=max_new)
+    kept_g = cache.kept_positions()
+    for (b, h), (pol, Fg_, pr) in forced.items():
+        want = ref.kept_positions(li.token_class[b], Fg_, pr.w_l, pol)
+        assert np.array_equal(kept_g[b * Hkv + h], want), (b, h, pol)
+        if pol == pr.policy and not pr.topk_tie:
+            assert np.array_equal(want, pr.kept)
+    # compacted bytes equal the source rows
+    for hd in range(B * Hkv):
+        pos, kc, vc = cache.rows(hd)
+        sel = pos >= 0
+        b, h = divmod(hd, Hkv)
+        assert torch.equal(kc[torch.from_numpy(sel).cuda()], Kd[b, h][torch.from_numpy(pos[sel]).cuda().long()])
+        assert torch.equal(vc[torch.from_numpy(sel).cuda()], Vd[b, h][torch.from_numpy(pos[sel]).cuda().long()])
+    if not check_decode or steps == 0:
+        return rep
+    ds = syn.make_decode_stream(spec, layer, steps, batch=batch, seed=seed)
+    outs = []
+    caches = []
+    for t in range(steps):
+        q = upload(ds.q[t], spec.dtype)
+        kn = upload(ds.k[t], spec.dtype)
+        vn = upload(ds.v[t], spec.dtype)
+        nc = torch.from_numpy(ds.new_class[t].copy()).cuda()
+        outs.append(cache.decode_step(q, kn, vn, nc).cpu().numpy())
+        if t < 8 or t == steps - 1 or t % 16 == 0:
+            caches.append((t, cache.kept_positions()))
+    assert cache.error_bits() == 0
+    outs = np.stack(outs)                                   # [steps, B, Hq, d]
+    tol = DEC_TOL[spec.dtype]
+    worst = 0.0
+    for (b, h), (pol, Fg_, pr) in forced.items():
+        o_ref, c_ref = ref.decode_incremental(li.K[b, h], li.V[b, h], li.token_class[b], Fg_, pr.w_l, pol,
+                                              ds.q[:, b, h * G:(h + 1) * G], ds.k[:, b, h], ds.v[:, b, h],
+                                              ds.new_class[:, b])
+        o_gpu = outs[:, b, h * G:(h + 1) * G]
+        scale = np.maximum(np.max(np.abs(o_ref), axis=-1), 1e-30)
+        err = np.max(np.abs(o_gpu - o_ref), axis=-1) / scale
+        worst = max(worst, float(err.max()))
+        assert err.max() <= tol, (b, h, pol, float(err.max()))
+        for t, kept in caches:
+            assert np.array_equal(kept[b * Hkv + h], c_ref[t]), (b, h, t)
+    rep.dec_err = worst
+    log(f"[case] ok: heads={len(rep.heads)} flagged={rep.flagged} "
+        f"max rec err={max(x.rec_err for x in rep.heads):.2e} "
+        f"max cum rel err={max(x.cum_rel_err for x in rep.heads):.2e} "
+        f"max lse err={max(x.lse_err for x in rep.heads):.2e} dec err={worst:.2e} "
+        f"policies={np.bincount([x.policy_gpu for x in rep.heads], minlength=5).tolist()}")
+    return rep
