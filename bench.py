@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of FastGen's hot path on one MI355X.
+
+One step = the whole path over one synthetic Llama-1-7B attention layer
+(32 heads, head_dim 128, prompt 2048, batch 1, bf16, T = 0.95, r_l = r_f = 0.3):
+  fg_profile  (row statistics sweep, column-sum sweep, top-k + recovery + policy)
+  fg_compact  (plan, one read of the totals, gather into the ragged cache)
+  256 x fg_decode_step over that cache (split-K partials + combine/append/evict).
+Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints ONE JSON line.  ``value`` is profile+compact prompt tokens/s; decode
+tokens/s, per-kernel durations (HIP events on the launch stream, over the timed
+region), the roofline of the dominant kernel and the CPU oracle timed on the
+host cores are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synth import inputs as syn  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+# ---------------------------------------------------------------- CPU baseline (the oracle)
+def _oracle_head(args):
+    """Profile + compact (and optionally decode) one KV head with the oracle, 1 BLAS thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import fastgen_ref as ref
+    spec_id, h, do_decode = args
+    spec = syn.CONFIGS[spec_id]
+    with threadpool_limits(1):
+        li = syn.make_layer(spec, 0, heads=[h])
+        G = spec.group
+        t0 = time.perf_counter()
+        pr = ref.profile_head(li.Q[0, :G], li.K[0, 0], li.token_class[0], spec.r_l, spec.r_f, spec.T[0])
+        ref.compact_head(li.K[0, 0], li.V[0, 0], pr.kept)
+        t1 = time.perf_counter()
+        td = 0.0
+        if do_decode:
+            ds = syn.make_decode_stream(spec, 0, heads=[h])
+            t2 = time.perf_counter()
+            ref.decode_incremental(li.K[0, 0], li.V[0, 0], li.token_class[0], pr.F, pr.w_l, pr.policy,
+                                   ds.q[:, 0, :G], ds.k[:, 0, 0], ds.v[:, 0, 0], ds.new_class[:, 0])
+            td = time.perf_counter() - t2
+    return t1 - t0, td
+
+
+def cpu_baseline(spec: syn.ConfigSpec, sample_heads: int) -> dict:
+    """Time the oracle on a sample of KV heads over a fork pool (run before the GPU is touched)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    cores = min(16, len(os.sched_getaffinity(0)))
+    heads = list(range(min(sample_heads, spec.n_kv_heads)))
+    ctx = mp.get_context("fork")
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
+        t0 = time.perf_counter()
+        res = list(ex.map(_oracle_head, [(spec.cfg_id, h, False) for h in heads]))
+        w_prompt = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        res_d = list(ex.map(_oracle_head, [(spec.cfg_id, h, True) for h in heads]))
+        w_both = time.perf_counter() - t0
+    scale = spec.batch * spec.n_kv_heads / len(heads)
+    prompt_tok_s = spec.batch * spec.seq_len / (w_prompt * scale)
+    w_dec = max(w_both - w_prompt, 1e-9)
+    decode_tok_s = spec.batch * spec.decode_steps / (w_dec * scale)
+    return {"value": prompt_tok_s, "unit": "prompt tok/s (profile+compact)", "cores": cores, "kind": "oracle",
+            "decode_tok_s": decode_tok_s,
+            "sample": f"{len(heads)} of {spec.n_kv_heads} KV heads of the layer (profile+compact, then also "
+                      f"{spec.decode_steps} decode steps), fp64 numpy oracle with 1 BLAS thread per worker over "
+                      f"{cores} forked workers; wall times scaled by {scale:g} to the whole layer",
+            "cpu_seconds": float(sum(a + b for a, b in res_d) + sum(a for a, _ in res))}
+
+
+# ---------------------------------------------------------------- GPU path
+def upload(torch, x, dtype):
+    if dtype == "bf16":
+        bits = syn.bf16_bits(x)
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=1, help="workload id (1 = Llama-1-7B layer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        return 2
+    spec = syn.CONFIGS[args.config]
+    if spec.layers != 1:
+        spec = syn.custom_spec(spec, layers=1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, args.cpu_sample_heads)     # before any GPU call (fork pool)
+
+    import torch
+    from adaptive_kv_cache_fg_amd import fastgen as fg
+
+    li = syn.make_layer(spec, 0)
+    ds = syn.make_decode_stream(spec, 0)
+    steps_dec = spec.decode_steps
+    Qd, Kd, Vd = upload(torch, li.Q, spec.dtype), upload(torch, li.K, spec.dtype), upload(torch, li.V, spec.dtype)
+    cls = torch.from_numpy(li.token_class).cuda()
+    qs = upload(torch, ds.q, spec.dtype)
+    ks = upload(torch, ds.k, spec.dtype)
+    vs = upload(torch, ds.v, spec.dtype)
+    ncs = torch.from_numpy(ds.new_class).cuda()
+    outs = torch.empty((steps_dec, spec.batch, spec.n_q_heads, spec.head_dim), dtype=torch.float32, device="cuda")
+    max_new_kept = int(max(np.count_nonzero(ds.new_class[:, b]) for b in range(spec.batch)))
+    T = spec.T[0]
+    B, Hq, n, d = li.Q.shape
+
+    def one_step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        prof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T)
+        cache = fg.compact(Kd, Vd, cls, prof, Hq, max_new_tokens=steps_dec, max_new_kept=max_new_kept)
+        if ev is not None:
+            ev[1].record()
+        for t in range(steps_dec):
+            cache.decode_step(qs[t], ks[t], vs[t], ncs[t], out=outs[t])
+        if ev is not None:
+            ev[2].record()
+        return prof, cache
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    fg.timing_read()                                         # drop anything pending
+    fg.timing_enable(True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    last = None
+    for s in range(args.steps):
+        last = one_step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fg.timing_enable(False)
+    recs = fg.timing_read()
+
+    prompt_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][1]) for s in range(args.steps)]))
+    decode_ms = float(np.mean([evs[s][1].elapsed_time(evs[s][2]) for s in range(args.steps)]))
+    ms_per_step = wall * 1e3 / args.steps
+    prompt_tok_s = B * n / (prompt_ms * 1e-3)
+    decode_tok_s = B * steps_dec / (decode_ms * 1e-3)
+
+    # per-kernel averages over the timed region
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    kstats = {k: {"launches_per_step": len(v) / args.steps, "avg_us": 1e3 * float(np.mean(v)),
+                  "total_us_per_step": 1e3 * float(np.sum(v)) / args.steps} for k, v in per.items()}
+
+    # algorithmic work per launch
+    prof, cache = last
+    e = 2 if spec.dtype == "bf16" else 4
+    pairs = n * (n + 1) // 2
+    sweep_flops = B * Hq * 2 * d * pairs
+    kept = cache.kept_count.cpu().numpy().astype(np.int64)
+    pol = prof.policy.cpu().numpy().reshape(-1)
+    gather_bytes = int(np.sum(kept * (2 * d * e) * 2 + 4 * kept) + B * spec.n_kv_heads * (n + n / 8))
+    # decode: cache rows in use grow by the appended tokens; mean over the steps
+    len_start = kept.copy()
+    cls_new = ds.new_class
+    grow = np.zeros_like(len_start, dtype=np.float64)
+    for hd in range(len(pol)):
+        b = hd // spec.n_kv_heads
+        p = int(pol[hd])
+        nc = cls_new[:, b]
+        if p == 4:
+            add = np.arange(steps_dec)
+        elif p == 3:
+            add = np.cumsum(nc != 0) - (nc != 0)                 # punct appended; ring size fixed
+        elif p >= 1:
+            add = np.cumsum(nc != 0) - (nc != 0)
+        else:
+            add = np.cumsum(nc == 1) - (nc == 1)
+        grow[hd] = float(np.mean(add))
+    mean_rows = float(np.sum(len_start + grow))
+    dec_bytes = mean_rows * (2 * d * e + 4) + B * Hq * d * e
+    kinfo = {
+        "profile_rowstats": ("mfma", sweep_flops, "TFLOP/s"),
+        "profile_colsums": ("mfma", sweep_flops, "TFLOP/s"),
+        "compact_gather": ("hbm", gather_bytes, "GB/s"),
+        "decode_partial": ("hbm", dec_bytes, "GB/s"),
+    }
+    peak_mfma = BF16_MFMA_PEAK_TFLOPS if spec.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    for k, (bound, units, unit) in kinfo.items():
+        if k not in kstats:
+            continue
+        avg_s = kstats[k]["avg_us"] * 1e-6
+        if bound == "mfma":
+            ach = units / avg_s / 1e12
+            kstats[k].update(bound="mfma", achieved=ach, peak=peak_mfma, unit=unit, frac=ach / peak_mfma,
+                             algorithmic_flops=units)
+        else:
+            ach = units / avg_s / 1e9
+            kstats[k].update(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit=unit, frac=ach / HBM_PEAK_GBS,
+                             algorithmic_bytes=units)
+    dominant = max((k for k in kinfo if k in kstats), key=lambda k: kstats[k]["total_us_per_step"])
+    dk = kstats[dominant]
+    roofline = {"bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"], "unit": dk["unit"],
+                "frac": dk["frac"], "traffic": None, "kernel": dominant}
+
+    result = {
+        "metric": "profile+compact prompt tok/s & decode tok/s on 1 MI355X; % MFMA / HBM peak",
+        "value": prompt_tok_s,
+        "unit": "prompt tok/s (profile+compact)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+        "data": "synthetic (seeded Llama-shaped post-RoPE Q/K/V with planted head types)",
+        "config": {"workload": f"{spec.name}: 1 attention layer, B={B}, Hq={Hq}, Hkv={spec.n_kv_heads}, "
+                               f"n={n}, d={d}, {spec.dtype}, T={T}, r_l={spec.r_l}, r_f={spec.r_f}, "
+                               f"{steps_dec} decode steps",
+                   "batch": B, "seq_len": n, "decode_steps": steps_dec},
+        "decode_tok_s": decode_tok_s,
+        "prompt_ms": prompt_ms, "decode_ms": decode_ms,
+        "policy_histogram": np.bincount(pol, minlength=5).tolist(),
+        "kept_fraction": float(kept.sum() / (B * spec.n_kv_heads * n)),
+        "roofline": roofline,
+        "kernels": kstats,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
