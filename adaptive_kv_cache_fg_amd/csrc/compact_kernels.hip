@@ -78,7 +78,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
     const int i = base + threadIdx.x;
     const long long cap = i < H ? capacity[i] : 0;
     sr[threadIdx.x] = cap;
-    sw[threadIdx.x] = (cap + chunk - 1) / chunk;
+    sw[threadIdx.x] = i < H ? max(1LL, (cap + chunk - 1) / chunk) : 0;   // every head gets an item
     __syncthreads();
     for (int o = 1; o < (int)blockDim.x; o <<= 1) {          // inclusive Hillis-Steele scan
       const long long ar = threadIdx.x >= (unsigned)o ? sr[threadIdx.x - o] : 0;
@@ -180,8 +180,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, co
 }
 
 __global__ __launch_bounds__(256) void worklist_kernel(const int64_t* __restrict__ work_offset, int chunk,
-                                                       int32_t* __restrict__ work) {
+                                                       int32_t* __restrict__ work, int32_t* __restrict__ arrive) {
   const int hd = blockIdx.x;
+  if (threadIdx.x == 0) arrive[hd] = 0;
   const int64_t w0 = work_offset[hd], w1 = work_offset[hd + 1];
   for (int64_t w = w0 + threadIdx.x; w < w1; w += blockDim.x) {
     work[2 * w] = hd;
@@ -215,7 +216,7 @@ static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timed_begin(FG_K_WORKLIST, st);
-  worklist_kernel<<<dim3(H), dim3(256), 0, st>>>(a.work_offset, a.chunk_rows, a.work);
+  worklist_kernel<<<dim3(H), dim3(256), 0, st>>>(a.work_offset, a.chunk_rows, a.work, a.arrive);
   timed_end(st);
   return hipGetLastError();
 }

@@ -3,19 +3,19 @@
 // Discard", Method, first paragraph: generation keeps head-specific caches;
 // stability paragraph: the policy chosen on the prompt is reused).
 //
-// Split-K over the cache: every work item is a 64-row chunk of one head's
-// rows.  A workgroup streams its chunk with 16-byte loads (one row is spread
-// over D*size/16 lanes; a wave covers several rows per pass), reduces the
-// G query heads' dot products with cross-lane shuffles, and keeps an online
-// softmax (running max, sum, weighted V) per query head; it writes one partial
-// (max, sum, acc[D]) per query head.  Items that start past a head's rows in
-// use exit at once, so the static work list covers the cache's whole capacity.
-//
-// The combine workgroup of each head merges its partials, adds the new token
-// when the policy lets it attend to itself, writes the fp32 output, and then
-// updates the cache: append (special; punct when policy >= 1; every token
-// under policy 4), or ring slot p mod (w_l - 1) (normal tokens under policy
-// 3), freeing the slot of the key that leaves the window.
+// One launch per step, split-K over the cache: every work item is a 128-row
+// chunk of one head.  A workgroup issues each 64-row half's 16-byte K/V loads
+// up front (one row is spread over D*size/16 lanes; a wave covers several rows
+// per pass), reduces the G query heads' dot products with cross-lane shuffles
+// and keeps an online softmax (running max, sum, weighted V) per query head.
+// It stores one partial (max, sum, acc[D]) per query head and signals a
+// per-head arrival counter; the last workgroup of the head to arrive merges
+// the partials, adds the new token when the policy lets it attend to itself,
+// writes the fp32 output and updates the cache: append (special; punct when
+// policy >= 1; every token under policy 4) or ring slot p mod (w_l - 1)
+// (normal tokens under policy 3), freeing the slot of the key that leaves the
+// window.  Items past a head's rows in use only signal, so the static work
+// list covers the cache's whole capacity.
 #include "fg_common.h"
 #include "fg_internal.h"
 
@@ -24,200 +24,274 @@ namespace fg {
 template <typename T> struct Vec16;
 template <> struct Vec16<__bf16> {
   static constexpr int N = 8;
-  static __device__ __forceinline__ void load(const __bf16* p, float* out) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+  using raw_t = bf16x8;
+  static __device__ __forceinline__ void cvt(const raw_t& v, float* out) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
   }
 };
 template <> struct Vec16<float> {
   static constexpr int N = 4;
-  static __device__ __forceinline__ void load(const float* p, float* out) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  using raw_t = f32x4;
+  static __device__ __forceinline__ void cvt(const raw_t& v, float* out) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[e] = v[e];
   }
 };
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void decode_partial_kernel(const T* __restrict__ q, const T* __restrict__ Kc,
-                                                             const T* __restrict__ Vc, const int32_t* __restrict__ pos,
-                                                             const int64_t* __restrict__ row_offset,
-                                                             const int32_t* __restrict__ len,
-                                                             const int32_t* __restrict__ work, int Hkv, float c,
-                                                             float* __restrict__ part) {
-  constexpr int E = Vec16<T>::N;            // elements per lane per row
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
+    const uint8_t* __restrict__ new_class, float* __restrict__ out, float* __restrict__ part,
+    const int32_t* __restrict__ work, const int64_t* __restrict__ work_offset, T* __restrict__ Kc,
+    T* __restrict__ Vc, int32_t* __restrict__ pos, const int64_t* __restrict__ row_offset, int32_t* __restrict__ len,
+    const int32_t* __restrict__ capacity, const int32_t* __restrict__ ring, const uint8_t* __restrict__ policy,
+    int32_t* __restrict__ arrive, uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, float c) {
+  using V16 = Vec16<T>;
+  using raw_t = typename V16::raw_t;
+  constexpr int E = V16::N;                 // elements per lane per row
   constexpr int LPR = D / E;                // lanes per row
   constexpr int RPP = kWave / LPR;          // rows per wave pass
   constexpr int kWaves = 4;
+  constexpr int kSubRows = kDecodeChunk;    // rows whose loads are issued together
+  constexpr int RPW = kSubRows / kWaves;    // rows per wave per pass
+  constexpr int NP = RPW / RPP;             // passes per wave
+  constexpr int GD = G * D;
+  constexpr int NGRP = GD >= 256 ? 1 : 256 / GD;   // item groups in the combine
   __shared__ float sm[kWaves][G], sl[kWaves][G];
   __shared__ float sacc[kWaves][G][D];
+  constexpr int kMaxItemsLds = 512 / G;   // items whose weights are staged in LDS
+  __shared__ float cs[NGRP][GD], ca[NGRP][GD];
+  __shared__ float s_wt[kMaxItemsLds * G], s_lw[kMaxItemsLds * G];
+  __shared__ float s_self[G], s_max[G];
+  __shared__ int s_last;
 
   const int item = blockIdx.x;
   const int hd = work[2 * item], start = work[2 * item + 1];
   const int L = len[hd];
-  if (start >= L) return;                    // whole workgroup: nothing in use here
   const int end = min(start + kDecodeChunk, L);
   const int64_t base = row_offset[hd];
-  const int b = hd / Hkv, h = hd % Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sub = lane / LPR, sl_ = lane % LPR;
+  float* mypart = part + (size_t)item * G * (D + 2);
 
-  float qv[G][E];
+  if (start < L) {
+    // ---- partial softmax state of this chunk
+    float qv[G][E];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-    Vec16<T>::load(q + ((size_t)(b * Hkv + h) * G + g) * D + sl_ * E, qv[g]);
-
-  float m[G], l[G], acc[G][E];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNegBig;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
-  }
-
-  for (int r0 = start + wave * RPP; r0 < end; r0 += kWaves * RPP) {   // wave-uniform trip count
-    const int row = r0 + sub;
-    const bool in = row < end;
-    const int64_t gr = base + (in ? row : start);
-    const bool valid = in && pos[gr] >= 0;
-    float kv[E], vv[E];
-    Vec16<T>::load(Kc + gr * D + sl_ * E, kv);
-    Vec16<T>::load(Vc + gr * D + sl_ * E, vv);
+    for (int g = 0; g < G; ++g) V16::cvt(*reinterpret_cast<const raw_t*>(q + ((size_t)hd * G + g) * D + sl_ * E), qv[g]);
+    float m[G], l[G], acc[G][E];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float s = 0.f;
+      m[g] = kNegBig;
+      l[g] = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) s = fmaf(qv[g][e], kv[e], s);
+      for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+    }
+    for (int r0 = start; r0 < end; r0 += kSubRows) {    // wave-uniform
+    raw_t kr[NP], vr[NP];
+    bool valid[NP];
 #pragma unroll
-      for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
-      if (valid) {
-        const float x = s * c;
-        const float mn = fmaxf(m[g], x);
-        const float al = fast_exp2(m[g] - mn), p = fast_exp2(x - mn);
-        l[g] = fmaf(l[g], al, p);
+    for (int i = 0; i < NP; ++i) {                     // every load of the sub-batch in flight at once
+      const int row = r0 + wave * RPW + i * RPP + sub;
+      const bool in = row < end;
+      const int64_t gr = base + (in ? row : start);
+      kr[i] = *reinterpret_cast<const raw_t*>(Kc + gr * D + sl_ * E);
+      vr[i] = *reinterpret_cast<const raw_t*>(Vc + gr * D + sl_ * E);
+      valid[i] = in && pos[gr] >= 0;
+    }
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[g][e] = fmaf(acc[g][e], al, p * vv[e]);
+    for (int i = 0; i < NP; ++i) {
+      float kv[E], vv[E];
+      V16::cvt(kr[i], kv);
+      V16::cvt(vr[i], vv);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) s = fmaf(qv[g][e], kv[e], s);
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
+        if (valid[i]) {
+          const float x = s * c;
+          const float mn = fmaxf(m[g], x);
+          const float al = fast_exp2(m[g] - mn), pw = fast_exp2(x - mn);
+          l[g] = fmaf(l[g], al, pw);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(acc[g][e], al, pw * vv[e]);
+          m[g] = mn;
+        }
+      }
+    }
+    }
+    // merge the RPP row groups of the wave (lanes with equal sl_)
+#pragma unroll
+    for (int o = LPR; o < kWave; o <<= 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mo = __shfl_xor(m[g], o), lo = __shfl_xor(l[g], o);
+        const float mn = fmaxf(m[g], mo);
+        const float a1 = fast_exp2(m[g] - mn), a2 = fast_exp2(mo - mn);
+        l[g] = l[g] * a1 + lo * a2;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float ao = __shfl_xor(acc[g][e], o);
+          acc[g][e] = acc[g][e] * a1 + ao * a2;
+        }
         m[g] = mn;
       }
     }
-  }
-  // merge the RPP row groups of the wave (lanes with equal sl_)
+    if (sub == 0) {
 #pragma unroll
-  for (int o = LPR; o < kWave; o <<= 1) {
+      for (int g = 0; g < G; ++g) {
+        if (sl_ == 0) { sm[wave][g] = m[g]; sl[wave][g] = l[g]; }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], o), lo = __shfl_xor(l[g], o);
-      const float mn = fmaxf(m[g], mo);
-      const float a1 = fast_exp2(m[g] - mn), a2 = fast_exp2(mo - mn);
-      l[g] = l[g] * a1 + lo * a2;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float ao = __shfl_xor(acc[g][e], o);
-        acc[g][e] = acc[g][e] * a1 + ao * a2;
+        for (int e = 0; e < E; ++e) sacc[wave][g][sl_ * E + e] = acc[g][e];
       }
-      m[g] = mn;
     }
+    __syncthreads();
+    for (int t = tid; t < GD; t += blockDim.x) {        // merge the 4 waves
+      const int g = t / D, dd = t % D;
+      float mx = sm[0][g];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm[w][g]);
+      float ls = 0.f, as = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float a = fast_exp2(sm[w][g] - mx);
+        ls += sl[w][g] * a;
+        as += sacc[w][g][dd] * a;
+      }
+      mypart[(size_t)g * (D + 2) + 2 + dd] = as;
+      if (dd == 0) { mypart[(size_t)g * (D + 2)] = mx; mypart[(size_t)g * (D + 2) + 1] = ls; }
+    }
+  } else if (tid < G) {                                  // nothing in use here: an empty state
+    mypart[(size_t)tid * (D + 2)] = kNegBig;
+    mypart[(size_t)tid * (D + 2) + 1] = 0.f;
   }
-  if (sub == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (sl_ == 0) { sm[wave][g] = m[g]; sl[wave][g] = l[g]; }
-#pragma unroll
-      for (int e = 0; e < E; ++e) sacc[wave][g][sl_ * E + e] = acc[g][e];
-    }
+
+  // ---- arrival: the last workgroup of the head merges and updates the cache.
+  // Every wave waits for its partial stores to complete, the barrier orders
+  // them before thread 0's device-scope release (L2 write-back), and the last
+  // arriver acquires (L1/L2 invalidate) before anyone reads the partials.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int n_items = (int)(work_offset[hd + 1] - work_offset[hd]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int prev = __hip_atomic_fetch_add(&arrive[hd], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == n_items - 1;
+    if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
-  // merge the 4 waves: thread t handles (g, dim) pairs
-  float* out = part + (size_t)item * G * (D + 2);
-  for (int t = tid; t < G * D; t += blockDim.x) {
-    const int g = t / D, dd = t % D;
-    float mx = sm[0][g];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm[w][g]);
-    float ls = 0.f, as = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float a = fast_exp2(sm[w][g] - mx);
-      ls += sl[w][g] * a;
-      as += sacc[w][g][dd] * a;
-    }
-    out[(size_t)g * (D + 2) + 2 + dd] = as;
-    if (dd == 0) { out[(size_t)g * (D + 2)] = mx; out[(size_t)g * (D + 2) + 1] = ls; }
-  }
-}
+  if (!s_last) return;
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
-    const uint8_t* __restrict__ new_class, float* __restrict__ out, const float* __restrict__ part,
-    const int32_t* __restrict__ work, const int64_t* __restrict__ work_offset, T* __restrict__ Kc, T* __restrict__ Vc,
-    int32_t* __restrict__ pos, const int64_t* __restrict__ row_offset, int32_t* __restrict__ len,
-    const int32_t* __restrict__ capacity, const int32_t* __restrict__ ring, const uint8_t* __restrict__ policy,
-    uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, float c) {
-  __shared__ float s_self[G];
-  __shared__ float s_kn[D], s_vn[D];
-  const int hd = blockIdx.x, b = hd / Hkv, h = hd % Hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int L = len[hd];
+  const int b = hd / Hkv;
   const int pol = policy[hd];
   const uint8_t cls = new_class ? new_class[b] : kNormal;
   const int lvl_self = cls == kSpecial ? 0 : (cls == kPunct ? 1 : (w_l >= 1 ? 3 : 4));
   const bool att_self = lvl_self <= pol;
-
   const T* kn = k_new + (size_t)hd * D;
   const T* vn = v_new + (size_t)hd * D;
-  for (int t = tid; t < D; t += blockDim.x) { s_kn[t] = to_f32(kn[t]); s_vn[t] = to_f32(vn[t]); }
-  __syncthreads();
-  // the new token's scores: wave w handles query heads w, w + 4, ...
-  for (int g = wave; g < G; g += 4) {
+  for (int g = wave; g < G; g += kWaves) {              // the new token's scores
     const T* qg = q + ((size_t)hd * G + g) * D;
     float s = 0.f;
-    for (int t = lane; t < D; t += kWave) s = fmaf(to_f32(qg[t]), s_kn[t], s);
+    for (int t = lane; t < D; t += kWave) s = fmaf(to_f32(qg[t]), to_f32(kn[t]), s);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
     if (lane == 0) s_self[g] = s * c;
   }
-  __syncthreads();
-
-  const int64_t w0 = work_offset[hd], w1 = work_offset[hd + 1];
-  for (int t = tid; t < G * D; t += blockDim.x) {
-    const int g = t / D, dd = t % D;
-    float mx = att_self ? s_self[g] : kNegBig;
-    for (int64_t w = w0; w < w1; ++w) {
-      if (work[2 * w + 1] >= L) break;                     // items past the rows in use wrote nothing
-      mx = fmaxf(mx, part[((size_t)w * G + g) * (D + 2)]);
+  const int64_t w0 = work_offset[hd];
+  const int n_items = (int)(work_offset[hd + 1] - w0);
+  __syncthreads();                                      // s_self visible
+  // (a) every item's (max, sum) per query head into LDS, one thread per item: global max M_g
+  float mloc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) mloc[g] = kNegBig;
+  for (int w = tid; w < n_items; w += blockDim.x) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float* pp = part + ((size_t)(w0 + w) * G + g) * (D + 2);
+      const float mw = pp[0], lw = pp[1];
+      if (lw > 0.f) mloc[g] = fmaxf(mloc[g], mw);
+      if (w < kMaxItemsLds) { s_wt[w * G + g] = mw; s_lw[w * G + g] = lw; }
     }
-    float ls = 0.f, as = 0.f;
-    for (int64_t w = w0; w < w1; ++w) {
-      if (work[2 * w + 1] >= L) break;
-      const float* pp = part + ((size_t)w * G + g) * (D + 2);
-      const float a = fast_exp2(pp[0] - mx);
-      ls = fmaf(pp[1], a, ls);
-      as = fmaf(pp[2 + dd], a, as);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mloc[g] = fmaxf(mloc[g], __shfl_xor(mloc[g], o));
+    if (lane == 0) sm[wave][g] = mloc[g];
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = att_self ? s_self[tid] : kNegBig;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w][tid]);
+    s_max[tid] = M;
+  }
+  __syncthreads();
+  // (b) per-item weights 2^(m_w - M_g), zero for empty items, in place
+  for (int w = tid; w < min(n_items, kMaxItemsLds); w += blockDim.x) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float a = s_lw[w * G + g] > 0.f ? fast_exp2(s_wt[w * G + g] - s_max[g]) : 0.f;
+      s_wt[w * G + g] = a;
+    }
+  }
+  __syncthreads();
+  // (c) weighted sums: item groups over threads, independent loads
+  {
+    const int grp = tid / GD;
+    if (grp < NGRP) {
+      for (int o = tid % GD; o < GD; o += 256) {
+        const int g = o / D, dd = o % D;
+        float Ls = 0.f, As = 0.f;
+#pragma unroll 4
+        for (int w = grp; w < n_items; w += NGRP) {
+          const float* pp = part + ((size_t)(w0 + w) * G + g) * (D + 2);
+          float a, lw;
+          if (w < kMaxItemsLds) {
+            a = s_wt[w * G + g];
+            lw = s_lw[w * G + g];
+          } else {
+            lw = pp[1];
+            a = lw > 0.f ? fast_exp2(pp[0] - s_max[g]) : 0.f;
+          }
+          Ls = fmaf(lw, a, Ls);
+          As = fmaf(pp[2 + dd], a, As);
+        }
+        cs[grp][o] = Ls;
+        ca[grp][o] = As;
+      }
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < GD; o += blockDim.x) {
+    const int g = o / D, dd = o % D;
+    float Ls = 0.f, As = 0.f;
+#pragma unroll
+    for (int r = 0; r < NGRP; ++r) {
+      Ls += cs[r][o];
+      As += ca[r][o];
     }
     if (att_self) {
-      const float a = fast_exp2(s_self[g] - mx);
-      ls += a;
-      as = fmaf(a, s_vn[dd], as);
+      const float a = fast_exp2(s_self[g] - s_max[g]);
+      Ls += a;
+      As = fmaf(a, to_f32(vn[dd]), As);
     }
-    out[((size_t)hd * G + g) * D + dd] = ls > 0.f ? as / ls : 0.f;
+    out[((size_t)hd * G + g) * D + dd] = Ls > 0.f ? As / Ls : 0.f;
   }
 
-  // cache update: after this step the cache holds {j <= p : level(p + 1, j) <= policy}
+  // cache update: afterwards the cache holds {j <= p : level(p + 1, j) <= policy}
   const int R = ring[hd];
-  const int64_t base = row_offset[hd];
+  const int64_t base_h = row_offset[hd];
   const bool to_ring = (cls == kNormal) && pol == 3 && w_l >= 2 && R > 0;
   const bool to_perm = cls == kSpecial || (cls == kPunct && pol >= 1) || (cls == kNormal && pol == 4);
   const int slot = R > 0 ? p % R : 0;
   int64_t dst = -1;
-  if (to_ring) {
-    dst = base + slot;
-  } else if (to_perm) {
-    if (L < capacity[hd]) dst = base + L;
-  }
-  __syncthreads();   // every thread has read len / partials before it changes
+  if (to_ring) dst = base_h + slot;
+  else if (to_perm && L < capacity[hd]) dst = base_h + L;
   if (dst >= 0) {
     for (int t = tid; t < D; t += blockDim.x) {
       Kc[dst * D + t] = kn[t];
@@ -225,31 +299,24 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     }
   }
   if (tid == 0) {
-    if (pol == 3 && R > 0 && !to_ring) pos[base + slot] = -1;   // key p + 1 - w_l leaves the window
+    if (pol == 3 && R > 0 && !to_ring) pos[base_h + slot] = -1;   // key p + 1 - w_l leaves the window
     if (dst >= 0) pos[dst] = p;
     if (to_perm) {
       if (dst >= 0) len[hd] = L + 1;
       else atomicOr(error_word, 1u);
     }
+    arrive[hd] = 0;
   }
 }
 
 template <typename T, int D, int G>
 static hipError_t launch_decode_tg(const DecodeArgs& a, hipStream_t st) {
   const float c = kLog2e / sqrtf((float)D);
-  const int H = a.B * a.Hkv;
-  timed_begin(FG_K_DECODE_PARTIAL, st);
-  if (a.n_work > 0)
-    decode_partial_kernel<T, D, G><<<dim3((unsigned)a.n_work), dim3(256), 0, st>>>(
-        (const T*)a.q, (const T*)a.Kc, (const T*)a.Vc, a.pos, a.row_offset, a.len, a.work, a.Hkv, c, a.part);
-  timed_end(st);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  timed_begin(FG_K_DECODE_COMBINE, st);
-  decode_combine_kernel<T, D, G><<<dim3(H), dim3(256), 0, st>>>(
+  timed_begin(FG_K_DECODE, st);
+  decode_step_kernel<T, D, G><<<dim3((unsigned)a.n_work), dim3(256), 0, st>>>(
       (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work, a.work_offset,
-      (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.error_word, a.Hkv, a.w_l, a.p,
-      c);
+      (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.arrive, a.error_word, a.Hkv,
+      a.w_l, a.p, c);
   timed_end(st);
   return hipGetLastError();
 }

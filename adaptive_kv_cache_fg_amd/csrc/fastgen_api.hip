@@ -124,9 +124,9 @@ const char* fg_status_string(fg_status s) {
 const char* fg_last_error(void) { return g_last_error.c_str(); }
 
 const char* fg_kernel_name(int32_t id) {
-  static const char* names[FG_K_COUNT] = {"profile_rowstats", "profile_colsums", "profile_select", "compact_plan",
-                                          "compact_scan",     "compact_gather",  "compact_worklist",
-                                          "decode_partial",   "decode_combine"};
+  static const char* names[FG_K_COUNT] = {"profile_rowstats", "profile_colsums", "profile_select",
+                                          "compact_plan",     "compact_scan",    "compact_gather",
+                                          "compact_worklist", "decode_step"};
   return (id >= 0 && id < FG_K_COUNT) ? names[id] : "unknown";
 }
 
@@ -247,7 +247,7 @@ fg_status fg_compact_plan(const fg_shape* shape, const fg_params* params, const 
 static fg_status check_cache_views(const fg_cache* c) {
   if (!c) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
   if (!c->k || !c->v || !c->pos || !c->row_offset || !c->len || !c->capacity || !c->ring || !c->policy ||
-      !c->work_offset || !c->error_word || (c->n_work > 0 && !c->work))
+      !c->work_offset || !c->arrive || !c->error_word || (c->n_work > 0 && !c->work))
     return fail(FG_ERR_INVALID_ARG, "a cache buffer is NULL");
   if (!aligned16(c->k) || !aligned16(c->v)) return fail(FG_ERR_INVALID_ARG, "cache k and v must be 16-byte aligned");
   if (c->total_rows < 0 || c->n_work < 0 || c->n_work > 0x7fffffff)
@@ -285,6 +285,7 @@ fg_status fg_compact(const fg_shape* shape, const fg_params* params, const void*
   a.pos = cache->pos;
   a.len = cache->len;
   a.work = cache->work;
+  a.arrive = cache->arrive;
   a.error_word = cache->error_word;
   a.chunk_rows = fg::kDecodeChunk;
   hipError_t e = fg::launch_gather(a, stream);
@@ -339,6 +340,7 @@ fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, cons
   a.policy = cache->policy;
   a.work_offset = cache->work_offset;
   a.work = cache->work;
+  a.arrive = cache->arrive;
   a.error_word = cache->error_word;
   a.chunk_rows = fg::kDecodeChunk;
   hipError_t e = fg::launch_decode(a, stream);

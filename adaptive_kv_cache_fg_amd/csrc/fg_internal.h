@@ -62,6 +62,7 @@ struct GatherArgs {
   int32_t* pos;
   int32_t* len;
   int32_t* work;
+  int32_t* arrive;
   uint32_t* error_word;
   int chunk_rows;
 };
@@ -86,12 +87,13 @@ struct DecodeArgs {
   const uint8_t* policy;
   const int64_t* work_offset;
   const int32_t* work;
+  int32_t* arrive;
   uint32_t* error_word;
   int chunk_rows;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
-constexpr int kDecodeChunk = 64;   // cache rows per decode work item
+constexpr int kDecodeChunk = 128;  // cache rows per decode work item
 constexpr int kMaxGroup = 8;       // query heads per KV head supported by decode
 
 }  // namespace fg

@@ -10,7 +10,8 @@
 // retained mass follows in O(n), so A is never stored:
 //
 //   sweep 1 (row statistics): one workgroup per 128 query rows, streaming key
-//     tiles through LDS, keeps an online max / sum of exp2 per query row and
+//     tiles through double-buffered LDS (next tile's loads in flight during
+//     the current tile's MFMAs), keeps an online max / sum of exp2 per query row and
 //     writes lse2_i = log2 sum_j 2^{x_ij} with x_ij = S_ij * log2(e).
 //   sweep 2 (column sums): one workgroup per 128 keys (all query heads of the
 //     KV group), streaming query tiles through LDS, recomputes S, forms
@@ -34,22 +35,39 @@ constexpr int kKeysPerWG = 128;   // sweep 2: 4 waves x 32 keys
 constexpr int kRowTile = 64;      // sweep 2: query rows staged per LDS tile
 constexpr int kPadBytes = 16;     // LDS row padding against bank conflicts
 
-// Cooperative copy of `rows` rows of D elements (row r0 onward, zero past n)
-// into an LDS tile whose rows are padded to RB bytes.
+// Staging of a tile of ROWS rows x D elements through LDS in two halves so
+// that the global loads of tile t+1 are in flight while tile t is computed:
+// prefetch() issues 16-byte loads into registers (zeros past row n), commit()
+// writes them into an LDS buffer whose rows are padded against bank conflicts.
 template <typename T, int D, int ROWS>
-__device__ __forceinline__ void stage_rows(unsigned char* lds, const T* src, int r0, int n) {
-  constexpr int kRowBytes = D * (int)sizeof(T);
-  constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per row
-  constexpr int kRB = kRowBytes + kPadBytes;
-  constexpr int kTotal = ROWS * kChunks;
-  for (int c = threadIdx.x; c < kTotal; c += blockDim.x) {
-    const int r = c / kChunks, q = c % kChunks;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r0 + r < n) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(src) +
-                                                         (size_t)(r0 + r) * kRowBytes + q * 16);
-    *reinterpret_cast<uint4*>(lds + r * kRB + q * 16) = v;
+struct Stager {
+  static constexpr int kRowBytes = D * (int)sizeof(T);
+  static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
+  static constexpr int kRB = kRowBytes + kPadBytes;
+  static constexpr int kPer = ROWS * kChunks / 256;       // chunks per thread (256 threads)
+  static constexpr int kBytes = ROWS * kRB;
+  uint4 r[kPer];
+
+  __device__ __forceinline__ void prefetch(const T* src, int r0, int n) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = threadIdx.x + i * 256;
+      const int row = c / kChunks, q = c % kChunks;
+      r[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (r0 + row < n)
+        r[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(src) +
+                                               (size_t)(r0 + row) * kRowBytes + q * 16);
+    }
   }
-}
+  __device__ __forceinline__ void commit(unsigned char* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = threadIdx.x + i * 256;
+      const int row = c / kChunks, q = c % kChunks;
+      *reinterpret_cast<uint4*>(lds + row * kRB + q * 16) = r[i];
+    }
+  }
+};
 
 template <typename T, int D>
 __device__ __forceinline__ typename Mfma<T>::op_t lds_operand(const unsigned char* lds, int row, int kk, int lane) {
@@ -75,7 +93,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
   using op_t = typename M::op_t;
   constexpr int NK = D / M::KS;
   constexpr int kRB = D * (int)sizeof(T) + kPadBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char ktile[kKeyTile * kRB];
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kKeyTile * kRB];
 
   const int nbh = gridDim.x / n_rb;                      // B * Hq
   const int rb = n_rb - 1 - (int)(blockIdx.x / nbh);     // heaviest row blocks first
@@ -97,10 +115,15 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
 
   float m = kNegBig, l = 0.f;
   const int kend = min(n, (rb + 1) * kRowsPerWG);
-  for (int k0 = 0; k0 < kend; k0 += kKeyTile) {
-    __syncthreads();
-    stage_rows<T, D, kKeyTile>(ktile, Kh, k0, n);
-    __syncthreads();
+  const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
+  Stager<T, D, kKeyTile> stg;
+  stg.prefetch(Kh, 0, n);
+  stg.commit(ktile[0]);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * kKeyTile;
+    if (t + 1 < ntiles) stg.prefetch(Kh, k0 + kKeyTile, n);   // in flight during the MFMAs below
+    const unsigned char* kt = ktile[t & 1];
 #pragma unroll
     for (int sub = 0; sub < kKeyTile / 32; ++sub) {
       const int key0 = k0 + sub * 32;
@@ -108,7 +131,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
       f32x16 acc = {};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        acc = M::mac(lds_operand<T, D>(ktile, sub * 32 + (lane & 31), kk, lane), qop[kk], acc);
+        acc = M::mac(lds_operand<T, D>(kt, sub * 32 + (lane & 31), kk, lane), qop[kk], acc);
       const bool edge = (key0 + 31 > q0) || (key0 + 32 > n);
       if (edge) {
 #pragma unroll
@@ -127,6 +150,8 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
       l = fmaf(l, fast_exp2(m - m_new), s);
       m = m_new;
     }
+    if (t + 1 < ntiles) stg.commit(ktile[(t + 1) & 1]);
+    __syncthreads();
   }
   // lanes l and l ^ 32 saw disjoint key subsets of the same query row
   const float m_o = __shfl_xor(m, 32), l_o = __shfl_xor(l, 32);
@@ -149,8 +174,8 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   using op_t = typename M::op_t;
   constexpr int NK = D / M::KS;
   constexpr int kRB = D * (int)sizeof(T) + kPadBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char qtile[kRowTile * kRB];
-  __shared__ __attribute__((aligned(16))) float lse_t[kRowTile];
+  __shared__ __attribute__((aligned(16))) unsigned char qtile[2][kRowTile * kRB];
+  __shared__ __attribute__((aligned(16))) float lse_t[2][kRowTile];
 
   const int nbh = gridDim.x / n_kb;                      // B * Hkv
   const int kb = (int)(blockIdx.x / nbh);                // key block 0 (most rows) first
@@ -171,58 +196,75 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
 
   float cum_acc = 0.f, band_acc = 0.f;
   const int i_begin = kb * kKeysPerWG;
-  for (int g = 0; g < G; ++g) {
+  const int ntiles = (n - i_begin + kRowTile - 1) / kRowTile;   // query tiles per query head
+  const int total = G * ntiles;
+  Stager<T, D, kRowTile> stg;
+  float lpre = 0.f;
+  auto issue = [&](int u) {                                      // tile u of the (g, tile) sequence
+    const int g = u / ntiles, i0 = i_begin + (u % ntiles) * kRowTile;
     const size_t qh = (size_t)b * Hq + (size_t)h * G + g;
-    const T* Qg = Q + qh * n * D;
-    const float* lg = lse2 + qh * n;
-    float cum_g = 0.f, band_g = 0.f;
-    for (int i0 = i_begin; i0 < n; i0 += kRowTile) {
-      __syncthreads();
-      stage_rows<T, D, kRowTile>(qtile, Qg, i0, n);
-      for (int t = threadIdx.x; t < kRowTile; t += blockDim.x)
-        lse_t[t] = (i0 + t < n) ? lg[i0 + t] : INFINITY;   // rows past n get P = 0
-      __syncthreads();
+    stg.prefetch(Q + qh * n * D, i0, n);
+    if (threadIdx.x < kRowTile) lpre = (i0 + (int)threadIdx.x < n) ? lse2[qh * n + i0 + threadIdx.x] : INFINITY;
+  };
+  auto commit = [&](int buf) {
+    stg.commit(qtile[buf]);
+    if (threadIdx.x < kRowTile) lse_t[buf][threadIdx.x] = lpre;     // rows past n get P = 0
+  };
+  issue(0);
+  commit(0);
+  __syncthreads();
+  float cum_g = 0.f, band_g = 0.f;
+  for (int u = 0; u < total; ++u) {
+    if (u + 1 < total) issue(u + 1);
+    const int i0 = i_begin + (u % ntiles) * kRowTile;
+    const unsigned char* qt = qtile[u & 1];
+    const float* lt = lse_t[u & 1];
 #pragma unroll
-      for (int sub = 0; sub < kRowTile / 32; ++sub) {
-        const int r0 = i0 + sub * 32;
-        if (r0 + 31 < j0 || r0 >= n) continue;            // rows all before this wave's keys
-        f32x16 acc = {};
+    for (int sub = 0; sub < kRowTile / 32; ++sub) {
+      const int r0 = i0 + sub * 32;
+      if (r0 + 31 < j0 || r0 >= n) continue;            // rows all before this wave's keys
+      f32x16 acc = {};
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk)
-          acc = M::mac(lds_operand<T, D>(qtile, sub * 32 + (lane & 31), kk, lane), kop[kk], acc);
-        float lrow[16];
+      for (int kk = 0; kk < NK; ++kk)
+        acc = M::mac(lds_operand<T, D>(qt, sub * 32 + (lane & 31), kk, lane), kop[kk], acc);
+      float lrow[16];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(&lse_t[sub * 32 + 8 * a + 4 * (lane >> 5)]);
-          lrow[4 * a + 0] = v[0]; lrow[4 * a + 1] = v[1]; lrow[4 * a + 2] = v[2]; lrow[4 * a + 3] = v[3];
-        }
-        const bool diag = r0 < j0 + 32;
-        float p[16];
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&lt[sub * 32 + 8 * a + 4 * (lane >> 5)]);
+        lrow[4 * a + 0] = v[0]; lrow[4 * a + 1] = v[1]; lrow[4 * a + 2] = v[2]; lrow[4 * a + 3] = v[3];
+      }
+      const bool diag = r0 < j0 + 32;
+      float p[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(acc[r], c, -lrow[r]));
-        if (diag) {
+      for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(acc[r], c, -lrow[r]));
+      if (diag) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (r0 + acc_row(r, lane) < key) p[r] = 0.f;
-        }
-        float ts = 0.f;
+        for (int r = 0; r < 16; ++r)
+          if (r0 + acc_row(r, lane) < key) p[r] = 0.f;
+      }
+      float ts = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) ts += p[r] + p[r + 1];
-        cum_g += ts;
-        // local band: rows i with 0 <= i - key < w_l
-        if ((r0 + 31) - j0 < w_l) {
-          band_g += ts;                                   // every pair of the tile is inside the band
-        } else if (r0 - (j0 + 31) < w_l) {
-          float tb = 0.f;
+      for (int r = 0; r < 16; r += 2) ts += p[r] + p[r + 1];
+      cum_g += ts;
+      // local band: rows i with 0 <= i - key < w_l
+      if ((r0 + 31) - j0 < w_l) {
+        band_g += ts;                                   // every pair of the tile is inside the band
+      } else if (r0 - (j0 + 31) < w_l) {
+        float tb = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (r0 + acc_row(r, lane) - key < w_l) tb += p[r];
-          band_g += tb;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (r0 + acc_row(r, lane) - key < w_l) tb += p[r];
+        band_g += tb;
       }
     }
-    cum_acc += cum_g;
-    band_acc += band_g;
+    if ((u + 1) % ntiles == 0) {                        // end of one query head's rows
+      cum_acc += cum_g;
+      band_acc += band_g;
+      cum_g = 0.f;
+      band_g = 0.f;
+    }
+    if (u + 1 < total) commit((u + 1) & 1);
+    __syncthreads();
   }
   cum_acc += __shfl_xor(cum_acc, 32);
   band_acc += __shfl_xor(band_acc, 32);

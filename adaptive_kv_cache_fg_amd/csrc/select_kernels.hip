@@ -70,12 +70,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        int acc = 0;
-        for (int bin = 255; bin >= 0; --bin) {
-          const int h = (int)hist[bin];
-          if (acc + h >= remaining) { s_sel = (unsigned)bin; s_rem = (unsigned)(remaining - acc); break; }
-          acc += h;
+      if (wave == 0) {
+        // lane l holds bins 255-4l .. 252-4l (descending); a prefix over lanes finds the
+        // bin where the count of larger-or-equal digits reaches `remaining`
+        int h[4], tot = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { h[e] = (int)hist[255 - 4 * lane - e]; tot += h[e]; }
+        int incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o);
+          if (lane >= o) incl += t;
+        }
+        const int excl = incl - tot;
+        if (excl < remaining && remaining <= incl) {
+          int acc = excl;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (acc + h[e] >= remaining) { s_sel = (unsigned)(255 - 4 * lane - e); s_rem = (unsigned)(remaining - acc); break; }
+            acc += h[e];
+          }
         }
       }
       __syncthreads();

@@ -23,7 +23,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
           4: "cache capacity exceeded", 5: "HIP error"}
 DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 KERNEL_NAMES = ["profile_rowstats", "profile_colsums", "profile_select", "compact_plan", "compact_scan",
-                "compact_gather", "compact_worklist", "decode_partial", "decode_combine"]
+                "compact_gather", "compact_worklist", "decode_step"]
 
 
 class FgShape(ctypes.Structure):
@@ -39,7 +39,7 @@ class FgCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
                 ("row_offset", ctypes.c_void_p), ("len", ctypes.c_void_p), ("capacity", ctypes.c_void_p),
                 ("ring", ctypes.c_void_p), ("policy", ctypes.c_void_p), ("work_offset", ctypes.c_void_p),
-                ("work", ctypes.c_void_p), ("error_word", ctypes.c_void_p),
+                ("work", ctypes.c_void_p), ("arrive", ctypes.c_void_p), ("error_word", ctypes.c_void_p),
                 ("total_rows", ctypes.c_int64), ("n_work", ctypes.c_int64),
                 ("n_prompt", ctypes.c_int32), ("w_l", ctypes.c_int32), ("next_pos", ctypes.c_int32),
                 ("shape", FgShape)]
@@ -231,8 +231,12 @@ class Cache:
 
 
 def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: Profile, n_q_heads: int,
-            max_new_tokens: int, max_new_kept: Optional[int] = None) -> Cache:
-    """fg_compact_plan + one read of the totals + fg_compact: the ragged cache of one layer."""
+            max_new_tokens: int, max_new_kept: Optional[int] = None, reuse: Optional[Cache] = None) -> Cache:
+    """fg_compact_plan + one read of the totals + fg_compact: the ragged cache of one layer.
+
+    With ``reuse``, the plan must fit that cache's buffers, which are refilled in place
+    (same device addresses, so a captured decode graph stays valid).
+    """
     _need(K, "K")
     _need(V, "V", K.dtype)
     B, Hkv, n, d = K.shape
@@ -245,29 +249,46 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
     dev = K.device
     i32 = dict(dtype=torch.int32, device=dev)
     i64 = dict(dtype=torch.int64, device=dev)
-    kept_count, ring, capacity = torch.empty(H, **i32), torch.empty(H, **i32), torch.empty(H, **i32)
-    row_offset, work_offset, totals = torch.empty(H + 1, **i64), torch.empty(H + 1, **i64), torch.empty(2, **i64)
+    if reuse is not None:
+        if (reuse.shape.batch, reuse.shape.n_kv_heads, reuse.shape.seq_len, reuse.shape.head_dim,
+                reuse.shape.n_q_heads) != (B, Hkv, n, d, n_q_heads) or reuse.t["k"].dtype != K.dtype:
+            raise ValueError("reuse: cache shape does not match")
+        kept_count, ring, capacity = reuse.kept_count, reuse.t["ring"], reuse.t["capacity"]
+        row_offset, work_offset, totals = reuse.t["row_offset"], reuse.t["work_offset"], reuse.t["totals"]
+    else:
+        kept_count, ring, capacity = torch.empty(H, **i32), torch.empty(H, **i32), torch.empty(H, **i32)
+        row_offset, work_offset = torch.empty(H + 1, **i64), torch.empty(H + 1, **i64)
+        totals = torch.empty(2, **i64)
     L = lib()
     _check(L.fg_compact_plan(ctypes.byref(shape), ctypes.byref(params), _ptr(token_class), _ptr(prof.policy),
                              _ptr(prof.freq_mask), int(max_new_tokens), int(max_new_kept), _ptr(kept_count),
                              _ptr(ring), _ptr(capacity), _ptr(row_offset), _ptr(work_offset), _ptr(totals),
                              _stream()), "fg_compact_plan")
     total_rows, n_work = (int(x) for x in totals.cpu().tolist())     # the one host synchronisation
+    if reuse is not None:
+        c = reuse.c
+        if total_rows > c.total_rows or n_work != c.n_work:
+            raise ValueError("reuse: the new plan does not fit the cache's buffers")
+        reuse.t["policy"].copy_(prof.policy.reshape(-1))
+        _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),
+                            _ptr(reuse.t["policy"]), _ptr(prof.freq_mask), ctypes.byref(c), _stream()), "fg_compact")
+        return reuse
     t = {
         "k": torch.empty((max(total_rows, 1), d), dtype=K.dtype, device=dev),
         "v": torch.empty((max(total_rows, 1), d), dtype=K.dtype, device=dev),
         "pos": torch.empty(max(total_rows, 1), **i32),
         "row_offset": row_offset, "len": torch.empty(H, **i32), "capacity": capacity, "ring": ring,
-        "policy": prof.policy.reshape(-1), "work_offset": work_offset,
-        "work": torch.empty(max(2 * n_work, 2), **i32), "error_word": torch.empty(1, **i32),
+        "policy": prof.policy.reshape(-1).clone(), "work_offset": work_offset, "totals": totals,
+        "work": torch.empty(max(2 * n_work, 2), **i32), "arrive": torch.empty(H, **i32),
+        "error_word": torch.empty(1, **i32),
     }
     c = FgCache()
     for name in ("k", "v", "pos", "row_offset", "len", "capacity", "ring", "policy", "work_offset", "work",
-                 "error_word"):
+                 "arrive", "error_word"):
         setattr(c, name, t[name].data_ptr())
     c.total_rows, c.n_work = total_rows, n_work
     _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),
-                        _ptr(prof.policy), _ptr(prof.freq_mask), ctypes.byref(c), _stream()), "fg_compact")
+                        _ptr(t["policy"]), _ptr(prof.freq_mask), ctypes.byref(c), _stream()), "fg_compact")
     return Cache(shape, t, c, kept_count)
 
 

@@ -99,6 +99,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=1, help="workload id (1 = Llama-1-7B layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=16)
+    ap.add_argument("--decode-mode", choices=["graph", "eager"], default="graph",
+                    help="graph: the decode loop captured once as a HIP graph and replayed")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -128,22 +130,53 @@ def main() -> int:
     T = spec.T[0]
     B, Hq, n, d = li.Q.shape
 
+    def prompt_phase(reuse=None):
+        prof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T)
+        cache = fg.compact(Kd, Vd, cls, prof, Hq, max_new_tokens=steps_dec, max_new_kept=max_new_kept,
+                           reuse=reuse)
+        return prof, cache
+
+    def decode_eager(cache):
+        for t in range(steps_dec):
+            cache.decode_step(qs[t], ks[t], vs[t], ncs[t], out=outs[t])
+
+    # one eager pass allocates the cache and the decode workspace
+    prof, cache = prompt_phase()
+    decode_eager(cache)
+    graph = None
+    if args.decode_mode == "graph":
+        # the whole 256-token decode loop as one HIP graph over the (reused) cache buffers
+        prof, cache = prompt_phase(reuse=cache)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode_eager(cache)
+        torch.cuda.synchronize()
+
     def one_step(ev=None):
         if ev is not None:
             ev[0].record()
-        prof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T)
-        cache = fg.compact(Kd, Vd, cls, prof, Hq, max_new_tokens=steps_dec, max_new_kept=max_new_kept)
+        res = prompt_phase(reuse=cache)
         if ev is not None:
             ev[1].record()
-        for t in range(steps_dec):
-            cache.decode_step(qs[t], ks[t], vs[t], ncs[t], out=outs[t])
+        if graph is not None:
+            graph.replay()
+        else:
+            decode_eager(cache)
         if ev is not None:
             ev[2].record()
-        return prof, cache
+        return res
 
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
+    # correctness guard on the timed configuration: the last decode output equals an eager rerun
+    ref_out = outs.clone()
+    prompt_phase(reuse=cache)
+    decode_eager(cache)
+    torch.cuda.synchronize()
+    if not torch.equal(ref_out, outs):
+        raise RuntimeError("graph replay and eager decode disagree")
     fg.timing_read()                                         # drop anything pending
     fg.timing_enable(True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -163,10 +196,13 @@ def main() -> int:
     prompt_tok_s = B * n / (prompt_ms * 1e-3)
     decode_tok_s = B * steps_dec / (decode_ms * 1e-3)
 
-    # per-kernel averages over the timed region
+    # per-kernel averages over the timed region (decode inside the graph: the replay's
+    # events divided by its launches, i.e. kernel time plus the graph's launch gaps)
     per = {}
     for name, ms in recs:
         per.setdefault(name, []).append(ms)
+    if graph is not None:
+        per["decode_step"] = [decode_ms / steps_dec] * (steps_dec * args.steps)
     kstats = {k: {"launches_per_step": len(v) / args.steps, "avg_us": 1e3 * float(np.mean(v)),
                   "total_us_per_step": 1e3 * float(np.sum(v)) / args.steps} for k, v in per.items()}
 
@@ -201,7 +237,7 @@ def main() -> int:
         "profile_rowstats": ("mfma", sweep_flops, "TFLOP/s"),
         "profile_colsums": ("mfma", sweep_flops, "TFLOP/s"),
         "compact_gather": ("hbm", gather_bytes, "GB/s"),
-        "decode_partial": ("hbm", dec_bytes, "GB/s"),
+        "decode_step": ("hbm", dec_bytes, "GB/s"),
     }
     peak_mfma = BF16_MFMA_PEAK_TFLOPS if spec.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
     for k, (bound, units, unit) in kinfo.items():
@@ -232,7 +268,7 @@ def main() -> int:
                                f"n={n}, d={d}, {spec.dtype}, T={T}, r_l={spec.r_l}, r_f={spec.r_f}, "
                                f"{steps_dec} decode steps",
                    "batch": B, "seq_len": n, "decode_steps": steps_dec},
-        "decode_tok_s": decode_tok_s,
+        "decode_tok_s": decode_tok_s, "decode_mode": args.decode_mode,
         "prompt_ms": prompt_ms, "decode_ms": decode_ms,
         "policy_histogram": np.bincount(pol, minlength=5).tolist(),
         "kept_fraction": float(kept.sum() / (B * spec.n_kv_heads * n)),

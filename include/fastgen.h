@@ -132,6 +132,8 @@ typedef struct {
   const uint8_t* policy;   /* [B*Hkv] */
   const int64_t* work_offset; /* [B*Hkv + 1] decode work items per head (prefix) */
   int32_t* work;           /* [n_work * 2] decode work items: (head, first row) */
+  int32_t* arrive;         /* [B*Hkv] per-head arrival counters of fg_decode_step;
+                              zeroed by fg_compact, left at zero by every step */
   uint32_t* error_word;    /* [1] sticky device error bits: 1 = capacity overflow */
   int64_t total_rows;      /* [host] rows allocated */
   int64_t n_work;          /* [host] work items */
@@ -155,7 +157,8 @@ int32_t fg_decode_chunk_rows(void);
  * on generated special/punct tokens (room for heads with policy < 4).
  * Outputs: kept_count [B*Hkv] prompt keys kept; ring [B*Hkv]; capacity [B*Hkv]
  * = ring + permanent prompt rows + (policy 4 ? max_new_tokens : max_new_kept);
- * row_offset [B*Hkv+1] and work_offset [B*Hkv+1] (exclusive prefix sums);
+ * row_offset [B*Hkv+1] and work_offset [B*Hkv+1] (exclusive prefix sums; a
+ * head has max(1, ceil(capacity / fg_decode_chunk_rows())) work items);
  * totals [2] = {total rows, total work items}.  The caller reads totals to the
  * host (the one synchronisation of the path) to allocate the cache.
  */
@@ -198,7 +201,10 @@ size_t fg_decode_workspace_size(const fg_cache* cache);
  *   of position p + 1 - w_l is freed.
  * q [B,Hq,d], k_new / v_new [B,Hkv,d] (cache dtype); new_class [B] u8 or NULL
  * (all normal); out [B,Hq,d] fp32.  An append beyond capacity is skipped and
- * sets bit 1 of error_word.  Increments cache->next_pos.
+ * sets bit 1 of error_word.  Increments cache->next_pos.  One kernel launch:
+ * every work item writes a partial softmax state, and the last item of a head
+ * to arrive (per-head counter) merges them and updates that head's cache.
+ * Steps on one cache must be issued in order on one stream.
  */
 fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
                          const uint8_t* new_class, float* out,
@@ -218,8 +224,7 @@ const char* fg_last_error(void);
  * max records (kernel id, milliseconds) accumulated since the last read. */
 enum {
   FG_K_ROWSTATS = 0, FG_K_COLSUMS = 1, FG_K_SELECT = 2, FG_K_PLAN = 3, FG_K_SCAN = 4,
-  FG_K_GATHER = 5, FG_K_WORKLIST = 6, FG_K_DECODE_PARTIAL = 7, FG_K_DECODE_COMBINE = 8,
-  FG_K_COUNT = 9
+  FG_K_GATHER = 5, FG_K_WORKLIST = 6, FG_K_DECODE = 7, FG_K_COUNT = 8
 };
 void fg_kernel_timing_enable(int enable);
 int32_t fg_kernel_timing_read(int32_t* kernel_ids, float* ms, int32_t max);

@@ -110,7 +110,7 @@ def test_decode_rejects_uncompacted_cache():
     c = fgb.FgCache()
     assert L.fg_decode_step(ctypes.byref(c), None, None, None, None, None, None, 0, None) == 1
     for name in ("k", "v", "pos", "row_offset", "len", "capacity", "ring", "policy", "work_offset", "work",
-                 "error_word"):
+                 "arrive", "error_word"):
         setattr(c, name, 0x1000)
     c.shape = fgb.FgShape(1, 4, 4, 16, 128, 0)
     c.n_prompt, c.next_pos = 16, 3          # next_pos before the prompt end
@@ -125,5 +125,5 @@ def test_status_strings_and_kernel_names():
     L = fgb.lib()
     assert L.fg_status_string(0) == b"ok"
     assert L.fg_status_string(4) == b"cache capacity exceeded"
-    assert [L.fg_kernel_name(i).decode() for i in range(9)] == fgb.KERNEL_NAMES
-    assert L.fg_decode_chunk_rows() == 64
+    assert [L.fg_kernel_name(i).decode() for i in range(8)] == fgb.KERNEL_NAMES
+    assert L.fg_decode_chunk_rows() == 128

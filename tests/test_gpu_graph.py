@@ -1,0 +1,61 @@
+"""Decode steps captured in a HIP graph replay exactly like eager launches.
+
+The decode loop is launch-bound at small shapes, so callers capture it; this
+checks that replays (each after an eager re-compaction into the same buffers,
+with synchronisations in between) reproduce the eager outputs bit for bit and
+leave the same cache."""
+import numpy as np
+import pytest
+import torch
+
+from adaptive_kv_cache_fg_amd import fastgen as fg
+from synth import inputs as syn
+
+pytestmark = pytest.mark.gpu
+
+
+def _upload(x, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(syn.bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2)])
+def test_decode_graph_replay_matches_eager(hq, hkv):
+    types = ("special", "punct", "heavy", "local", "none", "none", "none", "none")[:hkv]
+    spec = syn.custom_spec(syn.CONFIGS[1], seq_len=700, n_q_heads=hq, n_kv_heads=hkv, mix="fixed",
+                           fixed_types=types, batch=2)
+    steps = 24
+    print(f"[graph] hq={hq} hkv={hkv} n={spec.seq_len} steps={steps}", flush=True)
+    li = syn.make_layer(spec, 0)
+    ds = syn.make_decode_stream(spec, 0, steps)
+    Q, K, V = (_upload(x, spec.dtype) for x in (li.Q, li.K, li.V))
+    cls = torch.from_numpy(li.token_class).cuda()
+    qs, ks, vs = (_upload(x, spec.dtype) for x in (ds.q, ds.k, ds.v))
+    ncs = torch.from_numpy(ds.new_class).cuda()
+    outs = torch.empty((steps, 2, hq, spec.head_dim), dtype=torch.float32, device="cuda")
+
+    prof = fg.profile(Q, K, cls, spec.r_l, spec.r_f, spec.T[0])
+    cache = fg.compact(K, V, cls, prof, hq, max_new_tokens=steps)
+    for t in range(steps):
+        cache.decode_step(qs[t], ks[t], vs[t], ncs[t], out=outs[t])
+    torch.cuda.synchronize()
+    eager = outs.clone()
+    eager_kept = cache.kept_positions()
+
+    fg.compact(K, V, cls, prof, hq, max_new_tokens=steps, reuse=cache)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(steps):
+            cache.decode_step(qs[t], ks[t], vs[t], ncs[t], out=outs[t])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        outs.zero_()
+        fg.compact(K, V, cls, prof, hq, max_new_tokens=steps, reuse=cache)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs, eager), rep
+        kept = cache.kept_positions()
+        assert all(np.array_equal(a, b) for a, b in zip(kept, eager_kept)), rep
