@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   const int L = len[hd];
   const int end = min(start + kDecodeChunk, L);
   const int64_t base = row_offset[hd];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int sub = lane / LPR, sl_ = lane % LPR;
   float* mypart = part + (size_t)item * G * (D + 2);
 

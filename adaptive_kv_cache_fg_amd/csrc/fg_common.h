@@ -44,6 +44,10 @@ template <> struct Mfma<float> {
 // Row (within the 32x32 tile) held by accumulator r of this lane.
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// Index of this thread's wave in the workgroup, as a scalar (wave-uniform) value so
+// that branches on it stay scalar branches instead of exec-masked regions.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 

@@ -69,6 +69,23 @@ struct Stager {
   }
 };
 
+// Pairwise (tree) reductions of an accumulator tile: depth 4 instead of a
+// 16-long dependent chain, so a wave keeps several VALU ops in flight.
+__device__ __forceinline__ float tree_max16(const f32x16& a) {
+  const float b0 = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+  const float b1 = fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7]));
+  const float b2 = fmaxf(fmaxf(a[8], a[9]), fmaxf(a[10], a[11]));
+  const float b3 = fmaxf(fmaxf(a[12], a[13]), fmaxf(a[14], a[15]));
+  return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
+}
+__device__ __forceinline__ float tree_sum16(const float* p) {
+  const float b0 = (p[0] + p[1]) + (p[2] + p[3]);
+  const float b1 = (p[4] + p[5]) + (p[6] + p[7]);
+  const float b2 = (p[8] + p[9]) + (p[10] + p[11]);
+  const float b3 = (p[12] + p[13]) + (p[14] + p[15]);
+  return (b0 + b1) + (b2 + b3);
+}
+
 template <typename T, int D>
 __device__ __forceinline__ typename Mfma<T>::op_t lds_operand(const unsigned char* lds, int row, int kk, int lane) {
   using M = Mfma<T>;
@@ -102,7 +119,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
   const T* Qh = Q + (size_t)bh * n * D;
   const T* Kh = K + ((size_t)b * Hkv + hq / G) * n * D;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int q0 = rb * kRowsPerWG + wave * 32;
   const int qrow = q0 + (lane & 31);
 
@@ -124,30 +141,46 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
     const int k0 = t * kKeyTile;
     if (t + 1 < ntiles) stg.prefetch(Kh, k0 + kKeyTile, n);   // in flight during the MFMAs below
     const unsigned char* kt = ktile[t & 1];
+    // both 32-key halves of the tile: MFMAs first, then one max / rescale / exp pass
+    const bool act0 = k0 <= q0 + 31 && k0 < n;                  // wave-uniform
+    const bool act1 = k0 + 32 <= q0 + 31 && k0 + 32 < n;
+    if (act0) {
+      // all LDS operand reads of the tile first, so the MFMA chains never wait on LDS latency
+      op_t a0[NK], a1[NK];
 #pragma unroll
-    for (int sub = 0; sub < kKeyTile / 32; ++sub) {
-      const int key0 = k0 + sub * 32;
-      if (key0 > q0 + 31 || key0 >= n) continue;          // wave-uniform: tile entirely in the future
-      f32x16 acc = {};
+      for (int kk = 0; kk < NK; ++kk) {
+        a0[kk] = lds_operand<T, D>(kt, (lane & 31), kk, lane);
+        a1[kk] = lds_operand<T, D>(kt, 32 + (lane & 31), kk, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 acc0 = {}, acc1 = {};
+      if (act1) {                                                // two independent MFMA chains
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-        acc = M::mac(lds_operand<T, D>(kt, sub * 32 + (lane & 31), kk, lane), qop[kk], acc);
-      const bool edge = (key0 + 31 > q0) || (key0 + 32 > n);
-      if (edge) {
+        for (int kk = 0; kk < NK; ++kk) {
+          acc0 = M::mac(a0[kk], qop[kk], acc0);
+          acc1 = M::mac(a1[kk], qop[kk], acc1);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) acc0 = M::mac(a0[kk], qop[kk], acc0);
+      }
+      if (k0 + 63 > q0 || k0 + 64 > n) {                         // diagonal or ragged tile
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + acc_row(r, lane);
-          if (key > qrow || key >= n) acc[r] = -INFINITY;
+          const int key = k0 + acc_row(r, lane);
+          if (key > qrow || key >= n) acc0[r] = -INFINITY;
+          if (!act1 || key + 32 > qrow || key + 32 >= n) acc1[r] = -INFINITY;
         }
       }
-      float tmax = acc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
+      const float tmax = fmaxf(tree_max16(acc0), tree_max16(acc1));
       const float m_new = fmaxf(m, tmax * c);
-      float s = 0.f;
+      float e0[16], e1[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s += fast_exp2(fmaf(acc[r], c, -m_new));
-      l = fmaf(l, fast_exp2(m - m_new), s);
+      for (int r = 0; r < 16; ++r) {
+        e0[r] = fast_exp2(fmaf(acc0[r], c, -m_new));
+        e1[r] = fast_exp2(fmaf(acc1[r], c, -m_new));
+      }
+      l = fmaf(l, fast_exp2(m - m_new), tree_sum16(e0) + tree_sum16(e1));
       m = m_new;
     }
     if (t + 1 < ntiles) stg.commit(ktile[(t + 1) & 1]);
@@ -183,7 +216,7 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   const int b = bh / Hkv, h = bh % Hkv, G = Hq / Hkv;
   const T* Kh = K + (size_t)bh * n * D;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int j0 = kb * kKeysPerWG + wave * 32;            // this wave's first key
   const int key = j0 + (lane & 31);
 
@@ -219,42 +252,67 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
     const int i0 = i_begin + (u % ntiles) * kRowTile;
     const unsigned char* qt = qtile[u & 1];
     const float* lt = lse_t[u & 1];
+    // both 32-row halves of the tile: MFMAs first, then P = 2^(x - lse2) and tree sums
+    const bool act0 = i0 + 31 >= j0 && i0 < n;                 // wave-uniform
+    const bool act1 = i0 + 63 >= j0 && i0 + 32 < n;
+    if (act0 || act1) {
+      // all LDS operand reads of the tile first, so the MFMA chains never wait on LDS latency
+      op_t a0[NK], a1[NK];
 #pragma unroll
-    for (int sub = 0; sub < kRowTile / 32; ++sub) {
-      const int r0 = i0 + sub * 32;
-      if (r0 + 31 < j0 || r0 >= n) continue;            // rows all before this wave's keys
-      f32x16 acc = {};
+      for (int kk = 0; kk < NK; ++kk) {
+        a0[kk] = lds_operand<T, D>(qt, (lane & 31), kk, lane);
+        a1[kk] = lds_operand<T, D>(qt, 32 + (lane & 31), kk, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 acc0 = {}, acc1 = {};
+      if (act0 && act1) {                                        // two independent MFMA chains
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-        acc = M::mac(lds_operand<T, D>(qt, sub * 32 + (lane & 31), kk, lane), kop[kk], acc);
-      float lrow[16];
+        for (int kk = 0; kk < NK; ++kk) {
+          acc0 = M::mac(a0[kk], kop[kk], acc0);
+          acc1 = M::mac(a1[kk], kop[kk], acc1);
+        }
+      } else if (act0) {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) acc0 = M::mac(a0[kk], kop[kk], acc0);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) acc1 = M::mac(a1[kk], kop[kk], acc1);
+      }
+      float p0[16], p1[16];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&lt[sub * 32 + 8 * a + 4 * (lane >> 5)]);
-        lrow[4 * a + 0] = v[0]; lrow[4 * a + 1] = v[1]; lrow[4 * a + 2] = v[2]; lrow[4 * a + 3] = v[3];
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(&lt[8 * a + 4 * (lane >> 5)]);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(&lt[32 + 8 * a + 4 * (lane >> 5)]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p0[4 * a + e] = act0 ? fast_exp2(fmaf(acc0[4 * a + e], c, -v0[e])) : 0.f;
+          p1[4 * a + e] = act1 ? fast_exp2(fmaf(acc1[4 * a + e], c, -v1[e])) : 0.f;
+        }
       }
-      const bool diag = r0 < j0 + 32;
-      float p[16];
+      if (i0 < j0 + 32) {                                        // diagonal: rows above the key get 0
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(acc[r], c, -lrow[r]));
-      if (diag) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (r0 + acc_row(r, lane) < key) p[r] = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + acc_row(r, lane);
+          if (row < key) p0[r] = 0.f;
+          if (row + 32 < key) p1[r] = 0.f;
+        }
       }
-      float ts = 0.f;
+      const float ts0 = tree_sum16(p0), ts1 = tree_sum16(p1);
+      cum_g += ts0 + ts1;
+      // local band: rows i with 0 <= i - key < w_l, decided per 32-row half
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) ts += p[r] + p[r + 1];
-      cum_g += ts;
-      // local band: rows i with 0 <= i - key < w_l
-      if ((r0 + 31) - j0 < w_l) {
-        band_g += ts;                                   // every pair of the tile is inside the band
-      } else if (r0 - (j0 + 31) < w_l) {
-        float tb = 0.f;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int r0 = i0 + 32 * h2;
+        const float* ph = h2 ? p1 : p0;
+        if ((r0 + 31) - j0 < w_l) {
+          band_g += h2 ? ts1 : ts0;                              // every pair of the half is inside the band
+        } else if (r0 - (j0 + 31) < w_l) {
+          float tb = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (r0 + acc_row(r, lane) - key < w_l) tb += p[r];
-        band_g += tb;
+          for (int r = 0; r < 16; ++r)
+            if (r0 + acc_row(r, lane) - key < w_l) tb += ph[r];
+          band_g += tb;
+        }
       }
     }
     if ((u + 1) % ntiles == 0) {                        // end of one query head's rows
