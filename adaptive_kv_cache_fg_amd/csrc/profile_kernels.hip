@@ -9,11 +9,11 @@
 // local band).  With those two vectors and the token classes every policy's
 // retained mass follows in O(n), so A is never stored:
 //
-//   sweep 1 (row statistics): one workgroup per 128 query rows, streaming key
+//   sweep 1 (row statistics): one workgroup per 256 query rows, streaming key
 //     tiles through double-buffered LDS (next tile's loads in flight during
 //     the current tile's MFMAs), keeps an online max / sum of exp2 per query row and
 //     writes lse2_i = log2 sum_j 2^{x_ij} with x_ij = S_ij * log2(e).
-//   sweep 2 (column sums): one workgroup per 128 keys (all query heads of the
+//   sweep 2 (column sums): one workgroup per 256 keys (all query heads of the
 //     KV group), streaming query tiles through LDS, recomputes S, forms
 //     P_ij = 2^{x_ij - lse2_i} in fp32 and accumulates each key's column and
 //     band sums in registers -- no atomics, no partial buffers, a fixed
@@ -29,9 +29,11 @@
 
 namespace fg {
 
-constexpr int kRowsPerWG = 128;   // sweep 1: 4 waves x 32 query rows
+constexpr int kRowsPerWave = 64;  // sweep 1: query rows per wave (two MFMA column blocks)
+constexpr int kRowsPerWG = 256;   // sweep 1: 4 waves x 64 query rows
 constexpr int kKeyTile = 64;      // sweep 1: keys staged per LDS tile
-constexpr int kKeysPerWG = 128;   // sweep 2: 4 waves x 32 keys
+constexpr int kKeysPerWave = 64;  // sweep 2: keys per wave (two MFMA column blocks)
+constexpr int kKeysPerWG = 256;   // sweep 2: 4 waves x 64 keys
 constexpr int kRowTile = 64;      // sweep 2: query rows staged per LDS tile
 constexpr int kPadBytes = 16;     // LDS row padding against bank conflicts
 
@@ -102,6 +104,9 @@ __device__ __forceinline__ typename Mfma<T>::op_t global_operand(const T* rowptr
 }
 
 // ---------------------------------------------------------------- sweep 1: row statistics
+// A wave owns 64 query rows as two 32-column MFMA blocks (cb = 0, 1) whose B
+// operands stay in registers; every A operand (32 keys x KS dims) read from the
+// staged K tile feeds both blocks, halving LDS traffic per MFMA.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                        float* __restrict__ lse2, float* __restrict__ lse_out,
@@ -120,84 +125,102 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
   const T* Kh = K + ((size_t)b * Hkv + hq / G) * n * D;
 
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int q0 = rb * kRowsPerWG + wave * 32;
-  const int qrow = q0 + (lane & 31);
+  const int q0 = rb * kRowsPerWG + wave * kRowsPerWave;  // this wave's first query row
 
-  op_t qop[NK];
-  {
-    const int qr = qrow < n ? qrow : n - 1;             // clamp: row discarded below
+  op_t qop[2][NK];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) qop[kk] = global_operand<T, D>(Qh + (size_t)qr * D, kk, lane);
+  for (int cb = 0; cb < 2; ++cb) {
+    const int qr = min(q0 + 32 * cb + (lane & 31), n - 1);   // rows past n are discarded below
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qop[cb][kk] = global_operand<T, D>(Qh + (size_t)qr * D, kk, lane);
   }
 
-  float m = kNegBig, l = 0.f;
+  float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
   const int kend = min(n, (rb + 1) * kRowsPerWG);
   const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
+  const int qlast = q0 + kRowsPerWave - 1;
+
+  // One unit = 32 keys (half a staged tile) x this wave's 64 rows: 16 MFMAs into
+  // acc[cb], then an online-softmax update per query block.  Units are software
+  // pipelined: the MFMAs of unit u+1 are issued before the softmax of unit u, in
+  // one basic block, so the matrix cores and the VALU work at the same time.
+  auto unit_active = [&](int key0) { return key0 <= qlast && key0 < n; };   // wave-uniform
+  auto mfma_unit = [&](const unsigned char* kt, int kh, f32x16 (&acc)[2]) {
+    op_t a[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) a[kk] = lds_operand<T, D>(kt, 32 * kh + (lane & 31), kk, lane);
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      acc[0] = M::mac(a[kk], qop[0][kk], acc[0]);
+      acc[1] = M::mac(a[kk], qop[1][kk], acc[1]);
+    }
+  };
+  auto needs_mask = [&](int key0) { return key0 + 31 > q0 || key0 + 32 > n; };   // wave-uniform
+  auto softmax_unit = [&](int key0, f32x16 (&acc)[2]) {
+    if (needs_mask(key0)) {                                  // diagonal or ragged unit: mask
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int qrow = q0 + 32 * cb + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + acc_row(r, lane);
+          if (key > qrow || key >= n) acc[cb][r] = -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float m_new = fmaxf(m[cb], tree_max16(acc[cb]) * c);
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(acc[cb][r], c, -m_new));
+      l[cb] = fmaf(l[cb], fast_exp2(m[cb] - m_new), tree_sum16(e));
+      m[cb] = m_new;
+    }
+  };
+
   Stager<T, D, kKeyTile> stg;
   stg.prefetch(Kh, 0, n);
   stg.commit(ktile[0]);
   __syncthreads();
+  f32x16 accA[2], accB[2];
+  int pend_key = -1;                                         // unit whose softmax is pending in accB
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * kKeyTile;
     if (t + 1 < ntiles) stg.prefetch(Kh, k0 + kKeyTile, n);   // in flight during the MFMAs below
     const unsigned char* kt = ktile[t & 1];
-    // both 32-key halves of the tile: MFMAs first, then one max / rescale / exp pass
-    const bool act0 = k0 <= q0 + 31 && k0 < n;                  // wave-uniform
-    const bool act1 = k0 + 32 <= q0 + 31 && k0 + 32 < n;
-    if (act0) {
-      // all LDS operand reads of the tile first, so the MFMA chains never wait on LDS latency
-      op_t a0[NK], a1[NK];
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        a0[kk] = lds_operand<T, D>(kt, (lane & 31), kk, lane);
-        a1[kk] = lds_operand<T, D>(kt, 32 + (lane & 31), kk, lane);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 acc0 = {}, acc1 = {};
-      if (act1) {                                                // two independent MFMA chains
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-          acc0 = M::mac(a0[kk], qop[kk], acc0);
-          acc1 = M::mac(a1[kk], qop[kk], acc1);
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) acc0 = M::mac(a0[kk], qop[kk], acc0);
-      }
-      if (k0 + 63 > q0 || k0 + 64 > n) {                         // diagonal or ragged tile
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + acc_row(r, lane);
-          if (key > qrow || key >= n) acc0[r] = -INFINITY;
-          if (!act1 || key + 32 > qrow || key + 32 >= n) acc1[r] = -INFINITY;
-        }
-      }
-      const float tmax = fmaxf(tree_max16(acc0), tree_max16(acc1));
-      const float m_new = fmaxf(m, tmax * c);
-      float e0[16], e1[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e0[r] = fast_exp2(fmaf(acc0[r], c, -m_new));
-        e1[r] = fast_exp2(fmaf(acc1[r], c, -m_new));
-      }
-      l = fmaf(l, fast_exp2(m - m_new), tree_sum16(e0) + tree_sum16(e1));
-      m = m_new;
-    }
+    const bool act0 = unit_active(k0), act1 = unit_active(k0 + 32);
+    if (act0) mfma_unit(kt, 0, accA);
+    if (pend_key >= 0) softmax_unit(pend_key, accB);          // independent of the MFMAs above
+    pend_key = -1;
+    if (act1) mfma_unit(kt, 1, accB);
+    if (act0) softmax_unit(k0, accA);                          // independent of the MFMAs above
+    if (act1) pend_key = k0 + 32;
     if (t + 1 < ntiles) stg.commit(ktile[(t + 1) & 1]);
     __syncthreads();
   }
+  if (pend_key >= 0) softmax_unit(pend_key, accB);
   // lanes l and l ^ 32 saw disjoint key subsets of the same query row
-  const float m_o = __shfl_xor(m, 32), l_o = __shfl_xor(l, 32);
-  const float M2 = fmaxf(m, m_o);
-  const float L = l * fast_exp2(m - M2) + l_o * fast_exp2(m_o - M2);
-  if (lane < 32 && qrow < n) {
-    const float v = M2 + fast_log2(L);
-    lse2[(size_t)bh * n + qrow] = v;
-    if (lse_out) lse_out[(size_t)bh * n + qrow] = v * kLn2;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float m_o = __shfl_xor(m[cb], 32), l_o = __shfl_xor(l[cb], 32);
+    const float M2 = fmaxf(m[cb], m_o);
+    const float L = l[cb] * fast_exp2(m[cb] - M2) + l_o * fast_exp2(m_o - M2);
+    const int qrow = q0 + 32 * cb + (lane & 31);
+    if (lane < 32 && qrow < n) {
+      const float v = M2 + fast_log2(L);
+      lse2[(size_t)bh * n + qrow] = v;
+      if (lse_out) lse_out[(size_t)bh * n + qrow] = v * kLn2;
+    }
   }
 }
 
 // ---------------------------------------------------------------- sweep 2: column and band sums
+// A wave owns 64 keys as two 32-column MFMA blocks (kc = 0, 1) held in
+// registers; every A operand (32 query rows x KS dims) read from the staged Q
+// tile feeds both blocks.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                       const float* __restrict__ lse2, float* __restrict__ cum,
@@ -217,17 +240,18 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   const T* Kh = K + (size_t)bh * n * D;
 
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int j0 = kb * kKeysPerWG + wave * 32;            // this wave's first key
-  const int key = j0 + (lane & 31);
+  const int j0 = kb * kKeysPerWG + wave * kKeysPerWave;   // this wave's first key
 
-  op_t kop[NK];
-  {
-    const int kr = key < n ? key : n - 1;
+  op_t kop[2][NK];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) kop[kk] = global_operand<T, D>(Kh + (size_t)kr * D, kk, lane);
+  for (int kc = 0; kc < 2; ++kc) {
+    const int kr = min(j0 + 32 * kc + (lane & 31), n - 1);
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) kop[kc][kk] = global_operand<T, D>(Kh + (size_t)kr * D, kk, lane);
   }
 
-  float cum_acc = 0.f, band_acc = 0.f;
+  float cum_acc[2] = {0.f, 0.f}, band_acc[2] = {0.f, 0.f};
+  float cum_g[2] = {0.f, 0.f}, band_g[2] = {0.f, 0.f};
   const int i_begin = kb * kKeysPerWG;
   const int ntiles = (n - i_begin + kRowTile - 1) / kRowTile;   // query tiles per query head
   const int total = G * ntiles;
@@ -246,89 +270,79 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   issue(0);
   commit(0);
   __syncthreads();
-  float cum_g = 0.f, band_g = 0.f;
   for (int u = 0; u < total; ++u) {
     if (u + 1 < total) issue(u + 1);
     const int i0 = i_begin + (u % ntiles) * kRowTile;
     const unsigned char* qt = qtile[u & 1];
     const float* lt = lse_t[u & 1];
-    // both 32-row halves of the tile: MFMAs first, then P = 2^(x - lse2) and tree sums
-    const bool act0 = i0 + 31 >= j0 && i0 < n;                 // wave-uniform
-    const bool act1 = i0 + 63 >= j0 && i0 + 32 < n;
-    if (act0 || act1) {
-      // all LDS operand reads of the tile first, so the MFMA chains never wait on LDS latency
-      op_t a0[NK], a1[NK];
+    if (i0 + kRowTile - 1 >= j0 && i0 < n) {                    // wave-uniform: some pair is causal
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        a0[kk] = lds_operand<T, D>(qt, (lane & 31), kk, lane);
-        a1[kk] = lds_operand<T, D>(qt, 32 + (lane & 31), kk, lane);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 acc0 = {}, acc1 = {};
-      if (act0 && act1) {                                        // two independent MFMA chains
+      for (int rh = 0; rh < 2; ++rh) {                          // 32-row halves of the tile
+        const int r0 = i0 + 32 * rh;
+        if (r0 + 31 < j0 || r0 >= n) continue;                  // wave-uniform
+        op_t a[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) a[kk] = lds_operand<T, D>(qt, 32 * rh + (lane & 31), kk, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-          acc0 = M::mac(a0[kk], kop[kk], acc0);
-          acc1 = M::mac(a1[kk], kop[kk], acc1);
+          acc[0] = M::mac(a[kk], kop[0][kk], acc[0]);
+          acc[1] = M::mac(a[kk], kop[1][kk], acc[1]);
         }
-      } else if (act0) {
+        float lrow[16];
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) acc0 = M::mac(a0[kk], kop[kk], acc0);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) acc1 = M::mac(a1[kk], kop[kk], acc1);
-      }
-      float p0[16], p1[16];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(&lt[8 * a + 4 * (lane >> 5)]);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(&lt[32 + 8 * a + 4 * (lane >> 5)]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p0[4 * a + e] = act0 ? fast_exp2(fmaf(acc0[4 * a + e], c, -v0[e])) : 0.f;
-          p1[4 * a + e] = act1 ? fast_exp2(fmaf(acc1[4 * a + e], c, -v1[e])) : 0.f;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&lt[32 * rh + 8 * q4 + 4 * (lane >> 5)]);
+          lrow[4 * q4 + 0] = v[0]; lrow[4 * q4 + 1] = v[1]; lrow[4 * q4 + 2] = v[2]; lrow[4 * q4 + 3] = v[3];
         }
-      }
-      if (i0 < j0 + 32) {                                        // diagonal: rows above the key get 0
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i0 + acc_row(r, lane);
-          if (row < key) p0[r] = 0.f;
-          if (row + 32 < key) p1[r] = 0.f;
-        }
-      }
-      const float ts0 = tree_sum16(p0), ts1 = tree_sum16(p1);
-      cum_g += ts0 + ts1;
-      // local band: rows i with 0 <= i - key < w_l, decided per 32-row half
+        for (int kc = 0; kc < 2; ++kc) {
+          const int jc = j0 + 32 * kc;                          // first key of this column block
+          const int key = jc + (lane & 31);
+          float p[16];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int r0 = i0 + 32 * h2;
-        const float* ph = h2 ? p1 : p0;
-        if ((r0 + 31) - j0 < w_l) {
-          band_g += h2 ? ts1 : ts0;                              // every pair of the half is inside the band
-        } else if (r0 - (j0 + 31) < w_l) {
-          float tb = 0.f;
+          for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(acc[kc][r], c, -lrow[r]));
+          if (r0 < jc + 31) {                                   // diagonal: rows above the key get 0
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (r0 + acc_row(r, lane) - key < w_l) tb += ph[r];
-          band_g += tb;
+            for (int r = 0; r < 16; ++r)
+              if (r0 + acc_row(r, lane) < key) p[r] = 0.f;
+          }
+          const float ts = tree_sum16(p);
+          cum_g[kc] += ts;
+          if ((r0 + 31) - jc < w_l) {
+            band_g[kc] += ts;                                   // every pair of the half is in the band
+          } else if (r0 - (jc + 31) < w_l) {
+            float tb = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (r0 + acc_row(r, lane) - key < w_l) tb += p[r];
+            band_g[kc] += tb;
+          }
         }
       }
     }
-    if ((u + 1) % ntiles == 0) {                        // end of one query head's rows
-      cum_acc += cum_g;
-      band_acc += band_g;
-      cum_g = 0.f;
-      band_g = 0.f;
+    if ((u + 1) % ntiles == 0) {                                // end of one query head's rows
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        cum_acc[kc] += cum_g[kc];
+        band_acc[kc] += band_g[kc];
+        cum_g[kc] = 0.f;
+        band_g[kc] = 0.f;
+      }
     }
     if (u + 1 < total) commit((u + 1) & 1);
     __syncthreads();
   }
-  cum_acc += __shfl_xor(cum_acc, 32);
-  band_acc += __shfl_xor(band_acc, 32);
-  if (lane < 32 && key < n) {
-    cum[(size_t)bh * n + key] = cum_acc;
-    band[(size_t)bh * n + key] = band_acc;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const float cs = cum_acc[kc] + __shfl_xor(cum_acc[kc], 32);
+    const float bs = band_acc[kc] + __shfl_xor(band_acc[kc], 32);
+    const int key = j0 + 32 * kc + (lane & 31);
+    if (lane < 32 && key < n) {
+      cum[(size_t)bh * n + key] = cs;
+      band[(size_t)bh * n + key] = bs;
+    }
   }
 }
 

@@ -71,38 +71,38 @@ def budgets(n: int, r_l: float, r_f: float) -> tuple:
     return k_f, w_l
 
 
-def causal_attention_rows(q: np.ndarray, K: np.ndarray, row0: int) -> np.ndarray:
-    """Rows row0 .. row0+m-1 of A = softmax(q K^T / sqrt(d)) under the causal mask.
-
-    q: [m, d] query rows at positions row0.., K: [n, d].  Returns [m, n] fp64 with
-    zeros above the diagonal.  (Method, second paragraph: the attention map.)
-    """
-    q = np.asarray(q, dtype=np.float64)
-    K = np.asarray(K, dtype=np.float64)
-    m, d = q.shape
-    n = K.shape[0]
-    S = (q @ K.T) / math.sqrt(d)
-    i = row0 + np.arange(m)[:, None]
-    j = np.arange(n)[None, :]
-    S = np.where(j <= i, S, -np.inf)
-    mx = S.max(axis=1, keepdims=True)
-    E = np.exp(S - mx)
-    return E / E.sum(axis=1, keepdims=True)
-
-
-def _row_logsumexp(q: np.ndarray, K: np.ndarray, row0: int) -> np.ndarray:
+def _causal_scores(q: np.ndarray, K: np.ndarray, row0: int) -> np.ndarray:
+    """S_ij = q_i . k_j / sqrt(d) for query rows row0.., with -inf above the diagonal."""
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     m, d = q.shape
     S = (q @ K.T) / math.sqrt(d)
     i = row0 + np.arange(m)[:, None]
     j = np.arange(K.shape[0])[None, :]
-    S = np.where(j <= i, S, -np.inf)
-    mx = S.max(axis=1)
-    return mx + np.log(np.exp(S - mx[:, None]).sum(axis=1))
+    return np.where(j <= i, S, -np.inf)
 
 
-def column_scores(Qg: np.ndarray, K: np.ndarray, w_l: int) -> Dict[str, np.ndarray]:
+def causal_attention_rows(q: np.ndarray, K: np.ndarray, row0: int) -> np.ndarray:
+    """Rows row0 .. row0+m-1 of A = softmax(q K^T / sqrt(d)) under the causal mask.
+
+    q: [m, d] query rows at positions row0.., K: [n, d].  Returns [m, n] fp64 with
+    zeros above the diagonal.  (Method, second paragraph: the attention map.)
+    """
+    S = _causal_scores(q, K, row0)
+    mx = S.max(axis=1, keepdims=True)
+    E = np.exp(S - mx)
+    return E / E.sum(axis=1, keepdims=True)
+
+
+def _blocks(G: int, n: int):
+    return [(g, r0, min(n, r0 + ROW_BLOCK)) for g in range(G) for r0 in range(0, n, ROW_BLOCK)]
+
+
+def _map(fn, items, executor):
+    return list(executor.map(fn, items)) if executor is not None else [fn(x) for x in items]
+
+
+def column_scores(Qg: np.ndarray, K: np.ndarray, w_l: int, executor=None) -> Dict[str, np.ndarray]:
     """Per-key cumulative attention of one KV head and the per-row logsumexp.
 
     cum[j]  = sum_g sum_{i >= j} A^g_ij    (the cumulative attention score that
@@ -111,20 +111,30 @@ def column_scores(Qg: np.ndarray, K: np.ndarray, w_l: int) -> Dict[str, np.ndarr
               inside the local window contribute (a checked intermediate of
               the profiling kernels, not part of the method's definition);
     lse[g, i] = log sum_{j <= i} exp(q^g_i . k_j / sqrt(d)).
+    Row blocks are independent; ``executor`` (e.g. a thread pool) may run them
+    concurrently, their contributions are summed in block order.
     """
     G, n, _ = Qg.shape
+
+    def block(item):
+        g, r0, r1 = item
+        S = _causal_scores(Qg[g, r0:r1], K, r0)
+        mx = S.max(axis=1, keepdims=True)
+        E = np.exp(S - mx)
+        Z = E.sum(axis=1, keepdims=True)
+        A = E / Z
+        i = np.arange(r0, r1)[:, None]
+        j = np.arange(n)[None, :]
+        return (mx + np.log(Z))[:, 0], A.sum(axis=0), np.where((i - j >= 0) & (i - j < w_l), A, 0.0).sum(axis=0)
+
+    items = _blocks(G, n)
     cum = np.zeros(n, dtype=np.float64)
     band = np.zeros(n, dtype=np.float64)
     lse = np.zeros((G, n), dtype=np.float64)
-    for g in range(G):
-        for r0 in range(0, n, ROW_BLOCK):
-            r1 = min(n, r0 + ROW_BLOCK)
-            A = causal_attention_rows(Qg[g, r0:r1], K, r0)
-            cum += A.sum(axis=0)
-            i = np.arange(r0, r1)[:, None]
-            j = np.arange(n)[None, :]
-            band += np.where((i - j >= 0) & (i - j < w_l), A, 0.0).sum(axis=0)
-            lse[g, r0:r1] = _row_logsumexp(Qg[g, r0:r1], K, r0)
+    for (g, r0, r1), (l_blk, c_blk, b_blk) in zip(items, _map(block, items, executor)):
+        lse[g, r0:r1] = l_blk
+        cum += c_blk
+        band += b_blk
     return {"cum": cum, "band": band, "lse": lse}
 
 
@@ -158,17 +168,21 @@ def key_levels(cls: np.ndarray, F: np.ndarray, rows: np.ndarray, w_l: int) -> np
     return np.where(j <= i, lev, N_LEVELS)
 
 
-def row_bins(Qg: np.ndarray, K: np.ndarray, cls: np.ndarray, F: np.ndarray, w_l: int) -> np.ndarray:
+def row_bins(Qg: np.ndarray, K: np.ndarray, cls: np.ndarray, F: np.ndarray, w_l: int,
+             executor=None) -> np.ndarray:
     """bins[g, i, l] = attention mass row i of query head g puts on keys of level l."""
     G, n, _ = Qg.shape
+
+    def block(item):
+        g, r0, r1 = item
+        A = causal_attention_rows(Qg[g, r0:r1], K, r0)
+        lev = key_levels(cls, F, np.arange(r0, r1), w_l)
+        return np.stack([np.where(lev == lv, A, 0.0).sum(axis=1) for lv in range(N_LEVELS)], axis=1)
+
+    items = _blocks(G, n)
     bins = np.zeros((G, n, N_LEVELS), dtype=np.float64)
-    for g in range(G):
-        for r0 in range(0, n, ROW_BLOCK):
-            r1 = min(n, r0 + ROW_BLOCK)
-            A = causal_attention_rows(Qg[g, r0:r1], K, r0)
-            lev = key_levels(cls, F, np.arange(r0, r1), w_l)
-            for lv in range(N_LEVELS):
-                bins[g, r0:r1, lv] = np.where(lev == lv, A, 0.0).sum(axis=1)
+    for (g, r0, r1), b_blk in zip(items, _map(block, items, executor)):
+        bins[g, r0:r1] = b_blk
     return bins
 
 
@@ -241,15 +255,15 @@ def topk_tie_flag(cum: np.ndarray, k_f: int, tau: float) -> tuple:
 
 
 def profile_head(Qg: np.ndarray, K: np.ndarray, cls: np.ndarray, r_l: float, r_f: float, T: float,
-                 tau: float = TIE_TAU_DEFAULT) -> HeadProfile:
+                 tau: float = TIE_TAU_DEFAULT, executor=None) -> HeadProfile:
     """Profile one KV head from its G query heads' prompt rows and pick its policy."""
     Qg = np.asarray(Qg, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     G, n, _ = Qg.shape
     k_f, w_l = budgets(n, r_l, r_f)
-    cs = column_scores(Qg, K, w_l)
+    cs = column_scores(Qg, K, w_l, executor)
     F = frequent_set(cs["cum"], k_f)
-    bins = row_bins(Qg, K, cls, F, w_l)
+    bins = row_bins(Qg, K, cls, F, w_l, executor)
     R = recovery_from_bins(bins)
     policy = select_policy(R, T)
     kept = kept_positions(cls, F, w_l, policy)
@@ -315,23 +329,26 @@ def decode_incremental(K: np.ndarray, V: np.ndarray, cls: np.ndarray, F: np.ndar
 
 
 def decode_masked(K: np.ndarray, V: np.ndarray, cls: np.ndarray, F: np.ndarray, w_l: int, policy: int,
-                  q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, new_cls: np.ndarray):
+                  q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, new_cls: np.ndarray,
+                  steps_subset: Optional[Sequence[int]] = None):
     """The same generation computed in one shot: row p of the level-masked attention
     over the concatenated prompt + generated sequence.  Returns (out, caches) like
-    ``decode_incremental``; caches[t] = {j <= p : level(p + 1, j) <= policy}."""
+    ``decode_incremental``; caches[t] = {j <= p : level(p + 1, j) <= policy}.
+    With ``steps_subset`` only those steps are computed (outputs and caches in that order)."""
     n = len(cls)
     steps = q.shape[0]
+    ts = list(range(steps)) if steps_subset is None else [int(t) for t in steps_subset]
     K_all = np.concatenate([np.asarray(K, np.float64), np.asarray(k_new, np.float64)])
     V_all = np.concatenate([np.asarray(V, np.float64), np.asarray(v_new, np.float64)])
     cls_all = np.concatenate([cls, np.asarray(new_cls, dtype=cls.dtype)])
-    lev = key_levels(cls_all, F, n + np.arange(steps + 1), w_l)     # rows n .. n+steps
-    outs = np.zeros((steps, q.shape[1], q.shape[2]), dtype=np.float64)
+    outs = np.zeros((len(ts), q.shape[1], q.shape[2]), dtype=np.float64)
     caches = []
-    for t in range(steps):
+    for idx, t in enumerate(ts):
         p = n + t
-        att = np.flatnonzero(lev[t, : p + 1] <= policy)
-        outs[t] = _masked_softmax_out(np.asarray(q[t], np.float64), K_all[att], V_all[att])
-        caches.append(np.flatnonzero(lev[t + 1, : p + 1] <= policy).astype(np.int64))
+        lev = key_levels(cls_all[: p + 1], F, np.array([p, p + 1]), w_l)
+        att = np.flatnonzero(lev[0] <= policy)
+        outs[idx] = _masked_softmax_out(np.asarray(q[t], np.float64), K_all[att], V_all[att])
+        caches.append(np.flatnonzero(lev[1] <= policy).astype(np.int64))
     return outs, caches
 
 

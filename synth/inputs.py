@@ -27,6 +27,9 @@ corresponding slice of the full batch.  Nothing here computes attention.
 """
 from __future__ import annotations
 
+import functools
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence, Tuple
 
@@ -89,6 +92,18 @@ CONFIGS: Dict[int, ConfigSpec] = {
 _CANONICAL_SEED = {0: 2, 1: 0, 2: 0, 3: 0, 4: 0}
 
 
+def _parallel(fn, jobs) -> None:
+    """Run independent fill jobs on a thread pool (each job owns its RNG stream and output slice)."""
+    workers = min(16, os.cpu_count() or 1, max(1, len(jobs)))
+    if workers <= 1:
+        for j in jobs:
+            fn(j)
+        return
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for _ in ex.map(fn, jobs):
+            pass
+
+
 def _rng(*key: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(k) for k in key])))
 
@@ -111,7 +126,18 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return (b >> np.uint32(16)).astype(np.uint16)
 
 
+@functools.lru_cache(maxsize=16)
+def _rope_tables_cached(first: int, count: int, d: int) -> Tuple[np.ndarray, np.ndarray]:
+    half = d // 2
+    inv = ROPE_BASE ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = (first + np.arange(count, dtype=np.float64))[:, None] * inv[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
 def _rope_tables(positions: np.ndarray, d: int) -> Tuple[np.ndarray, np.ndarray]:
+    positions = np.asarray(positions)
+    if len(positions) and np.array_equal(positions, positions[0] + np.arange(len(positions))):
+        return _rope_tables_cached(int(positions[0]), len(positions), d)
     half = d // 2
     inv = ROPE_BASE ** (-2.0 * np.arange(half, dtype=np.float64) / d)
     ang = positions.astype(np.float64)[:, None] * inv[None, :]
@@ -212,39 +238,40 @@ def make_layer(spec: ConfigSpec, layer: int = 0, batch: Optional[Sequence[int]] 
     K = np.empty((B, Hk, n, d), dtype=np.float32)
     V = np.empty((B, Hk, n, d), dtype=np.float32)
     cls = np.stack([token_classes(spec, int(b), seed) for b in bidx]) if B else np.zeros((0, n), np.uint8)
-    for bi, b in enumerate(bidx):
-        for hi, h in enumerate(kv_heads):
-            kind = types_all[h]
-            kq = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_Q).standard_normal((G, n, d))
-            kk = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_K).standard_normal((n, d))
-            kv = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_V).standard_normal((n, d))
-            if kind == "local":
-                c = _local_center(seed, spec, layer, int(h))
-                kq = c + 0.3 * kq
-                kk = c + 0.3 * kk
-            if _uses_rope(spec, kind):
-                kq = _rope(kq, pos)
-                kk = _rope(kk, pos)
-            if kind in ("special", "punct", "heavy"):
-                u = _direction(seed, spec, layer, int(h))
-                kq = kq + u
-                if kind == "special":
-                    sel = cls[bi] == TOKEN_SPECIAL
-                elif kind == "punct":
-                    sel = cls[bi] == TOKEN_PUNCT
-                else:
-                    normal = np.flatnonzero(cls[bi] == TOKEN_NORMAL)
-                    pick = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_HEAVY).choice(
-                        normal, size=n // 20, replace=False)
-                    sel = np.zeros(n, dtype=bool)
-                    sel[pick] = True
-                kk = kk.copy()
-                kk[sel] += 6.0 * u
-            Q[bi, hi * G:(hi + 1) * G] = kq
-            K[bi, hi] = kk
-            V[bi, hi] = kv
-    if spec.dtype == "bf16":
-        Q, K, V = round_to_bf16(Q), round_to_bf16(K), round_to_bf16(V)
+    def fill(job):
+        bi, b, hi, h = job
+        kind = types_all[h]
+        kq = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_Q).standard_normal((G, n, d))
+        kk = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_K).standard_normal((n, d))
+        kv = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_V).standard_normal((n, d))
+        if kind == "local":
+            c = _local_center(seed, spec, layer, int(h))
+            kq = c + 0.3 * kq
+            kk = c + 0.3 * kk
+        if _uses_rope(spec, kind):
+            kq = _rope(kq, pos)
+            kk = _rope(kk, pos)
+        if kind in ("special", "punct", "heavy"):
+            u = _direction(seed, spec, layer, int(h))
+            kq = kq + u
+            if kind == "special":
+                sel = cls[bi] == TOKEN_SPECIAL
+            elif kind == "punct":
+                sel = cls[bi] == TOKEN_PUNCT
+            else:
+                normal = np.flatnonzero(cls[bi] == TOKEN_NORMAL)
+                pick = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_HEAVY).choice(
+                    normal, size=n // 20, replace=False)
+                sel = np.zeros(n, dtype=bool)
+                sel[pick] = True
+            kk = kk.copy()
+            kk[sel] += 6.0 * u
+        rnd = round_to_bf16 if spec.dtype == "bf16" else (lambda x: x)
+        Q[bi, hi * G:(hi + 1) * G] = rnd(kq.astype(np.float32))
+        K[bi, hi] = rnd(kk.astype(np.float32))
+        V[bi, hi] = rnd(kv.astype(np.float32))
+
+    _parallel(fill, [(bi, b, hi, h) for bi, b in enumerate(bidx) for hi, h in enumerate(kv_heads)])
     return LayerInputs(spec, layer, bidx, Q, K, V, cls, types)
 
 
@@ -282,30 +309,31 @@ def make_decode_stream(spec: ConfigSpec, layer: int = 0, steps: Optional[int] = 
     v = np.empty((steps, B, Hk, d), dtype=np.float32)
     ncls = np.stack([new_token_classes(spec, int(b), steps, seed) for b in bidx], axis=1) \
         if B else np.zeros((steps, 0), np.uint8)
-    for bi, b in enumerate(bidx):
-        for hi, h in enumerate(kv_heads):
-            kind = types_all[h]
-            dq = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_DQ).standard_normal((G, steps, d))
-            dk = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_DK).standard_normal((steps, d))
-            dv = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_DV).standard_normal((steps, d))
-            if kind == "local":
-                c = _local_center(seed, spec, layer, int(h))
-                dq = c + 0.3 * dq
-                dk = c + 0.3 * dk
-            if _uses_rope(spec, kind):
-                dq = _rope(dq, pos)
-                dk = _rope(dk, pos)
-            if kind in ("special", "punct", "heavy"):
-                u = _direction(seed, spec, layer, int(h))
-                dq = dq + u
-                if kind == "punct":
-                    dk = dk.copy()
-                    dk[ncls[:, bi] == TOKEN_PUNCT] += 6.0 * u
-            q[:, bi, hi * G:(hi + 1) * G] = np.transpose(dq, (1, 0, 2))
-            k[:, bi, hi] = dk
-            v[:, bi, hi] = dv
-    if spec.dtype == "bf16":
-        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    def fill(job):
+        bi, b, hi, h = job
+        kind = types_all[h]
+        dq = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_DQ).standard_normal((G, steps, d))
+        dk = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_DK).standard_normal((steps, d))
+        dv = _rng(seed, spec.cfg_id, layer, int(b), int(h), _K_DV).standard_normal((steps, d))
+        if kind == "local":
+            c = _local_center(seed, spec, layer, int(h))
+            dq = c + 0.3 * dq
+            dk = c + 0.3 * dk
+        if _uses_rope(spec, kind):
+            dq = _rope(dq, pos)
+            dk = _rope(dk, pos)
+        if kind in ("special", "punct", "heavy"):
+            u = _direction(seed, spec, layer, int(h))
+            dq = dq + u
+            if kind == "punct":
+                dk = dk.copy()
+                dk[ncls[:, bi] == TOKEN_PUNCT] += 6.0 * u
+        rnd = round_to_bf16 if spec.dtype == "bf16" else (lambda x: x)
+        q[:, bi, hi * G:(hi + 1) * G] = rnd(np.transpose(dq, (1, 0, 2)).astype(np.float32))
+        k[:, bi, hi] = rnd(dk.astype(np.float32))
+        v[:, bi, hi] = rnd(dv.astype(np.float32))
+
+    _parallel(fill, [(bi, b, hi, h) for bi, b in enumerate(bidx) for hi, h in enumerate(kv_heads)])
     return DecodeStream(spec, layer, bidx, q, k, v, ncls)
 
 

@@ -187,3 +187,134 @@ def run_case(spec: syn.ConfigSpec, layer: int = 0, T: Optional[float] = None, st
         f"max lse err={max(x.lse_err for x in rep.heads):.2e} dec err={worst:.2e} "
         f"policies={np.bincount([x.policy_gpu for x in rep.heads], minlength=5).tolist()}")
     return rep
+
+
+# ---------------------------------------------------------------- full-size layers, sampled heads
+
+def _oracle_heads(li, spec, heads, T, tau=TIE_TAU):
+    """Oracle profiles of the sampled (b, h) heads; each head's row blocks run on a thread
+    pool (numpy releases the GIL; BLAS limited to one thread per worker)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    G = spec.group
+    workers = min(16, len(os.sched_getaffinity(0)))
+    out = {}
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=workers) as ex:
+        for (b, h) in heads:
+            out[(b, h)] = ref.profile_head(li.Q[b, h * G:(h + 1) * G], li.K[b, h], li.token_class[b],
+                                           spec.r_l, spec.r_f, T, tau=tau, executor=ex)
+            log(f"[oracle] head b={b} h={h} done")
+    return out
+
+
+def run_fullsize(spec: syn.ConfigSpec, layer: int, sample: List[tuple], decode_sample: List[tuple],
+                 Ts=None, steps: Optional[int] = None) -> dict:
+    """One full-size layer on the GPU; oracle comparisons on sampled heads, forced-mode kept
+    lists for every head, decode outputs on sampled heads at sampled steps, and every head's
+    final cache."""
+    Ts = list(spec.T) if Ts is None else list(Ts)
+    steps = spec.decode_steps if steps is None else steps
+    log(f"[fullsize] cfg={spec.cfg_id} {spec.name} layer={layer} B={spec.batch} Hq={spec.n_q_heads} "
+        f"Hkv={spec.n_kv_heads} n={spec.seq_len} T={Ts} steps={steps} sample={len(sample)}")
+    li = syn.make_layer(spec, layer)
+    B, Hq, n, d = li.Q.shape
+    Hkv = li.K.shape[1]
+    G = Hq // Hkv
+    Qd, Kd, Vd = upload(li.Q, spec.dtype), upload(li.K, spec.dtype), upload(li.V, spec.dtype)
+    cls_d = torch.from_numpy(li.token_class).cuda()
+    orc = _oracle_heads(li, spec, sample, Ts[0])
+    report = {"flagged": 0, "checked": 0, "policies": {}}
+    prof_last = None
+    for T in Ts:
+        prof = fg.profile(Qd, Kd, cls_d, spec.r_l, spec.r_f, T, want_lse=True, want_band=True)
+        torch.cuda.synchronize()
+        pol_g = prof.policy.cpu().numpy()
+        rec_g = prof.recovery.cpu().numpy().astype(np.float64)
+        cum_g = prof.cum.cpu().numpy().astype(np.float64)
+        F_g = prof.frequent()
+        # properties of every head
+        k_f, w_l = ref.budgets(n, spec.r_l, spec.r_f)
+        assert np.allclose(cum_g.sum(axis=-1), G * n, rtol=1e-4), "column sums must total G*n"
+        assert np.all(np.diff(rec_g, axis=-1) >= -1e-6) and np.all(rec_g[..., 4] == 1.0)
+        assert np.all(F_g.sum(axis=-1) == min(k_f, n))
+        for b in range(B):
+            for h in range(Hkv):
+                if not np.any(np.abs(rec_g[b, h, :4] - T) < 1e-6):
+                    own = next(k for k in range(5) if rec_g[b, h, k] >= T or k == 4)
+                    assert int(pol_g[b, h]) == own, (b, h)
+        # sampled heads against the oracle
+        lse_g = prof.lse.cpu().numpy().astype(np.float64)
+        band_g = prof.band.cpu().numpy().astype(np.float64)
+        for (b, h), pr in orc.items():
+            R = pr.R
+            policy = ref.select_policy(R, T)
+            near = bool(np.any(np.abs(R[:4] - T) <= ref.NEAR_T_WINDOW))
+            assert np.max(np.abs(lse_g[b, h * G:(h + 1) * G] - pr.lse)) <= 2e-4 + 2e-6 * np.max(np.abs(pr.lse))
+            assert np.allclose(cum_g[b, h], pr.cum, rtol=2e-4, atol=1e-6 * G), (b, h)
+            assert np.allclose(band_g[b, h], pr.band, rtol=2e-4, atol=1e-6 * G), (b, h)
+            assert np.max(np.abs(rec_g[b, h] - R)) <= REC_TOL, (b, h, rec_g[b, h], R)
+            if pr.topk_tie:
+                assert eps_topk_ok(pr.cum, F_g[b, h], pr.k_f, TIE_TAU), (b, h)
+            else:
+                assert np.array_equal(F_g[b, h], pr.F), (b, h)
+            if near or pr.topk_tie:
+                report["flagged"] += 1
+                assert int(pol_g[b, h]) in allowed_policies(R, T, policy) or pr.topk_tie, (b, h)
+            else:
+                assert int(pol_g[b, h]) == policy, (b, h, rec_g[b, h], R)
+            report["checked"] += 1
+        report["policies"][T] = np.bincount(pol_g.reshape(-1), minlength=5).tolist()
+        log(f"[fullsize] T={T}: policies {report['policies'][T]}, sampled heads ok")
+        prof_last = prof
+    # compaction and decode with the last T
+    prof = prof_last
+    pol_g = prof.policy.cpu().numpy()
+    F_g = prof.frequent()
+    k_f, w_l = ref.budgets(n, spec.r_l, spec.r_f)
+    ds = syn.make_decode_stream(spec, layer, steps)
+    max_kept = int(max(np.count_nonzero(ds.new_class[:, b]) for b in range(B)))
+    cache = fg.compact(Kd, Vd, cls_d, prof, Hq, max_new_tokens=steps, max_new_kept=max_kept)
+    kept_g = cache.kept_positions()
+    for b in range(B):
+        for h in range(Hkv):
+            want = ref.kept_positions(li.token_class[b], F_g[b, h], w_l, int(pol_g[b, h]))
+            assert np.array_equal(kept_g[b * Hkv + h], want), (b, h)
+    for (b, h) in decode_sample:
+        pos, kc, vc = cache.rows(b * Hkv + h)
+        sel = torch.from_numpy(pos >= 0).cuda()
+        idx = torch.from_numpy(pos[pos >= 0]).cuda().long()
+        assert torch.equal(kc[sel], Kd[b, h][idx]) and torch.equal(vc[sel], Vd[b, h][idx])
+    check = sorted({0, 1, 2, 3, steps // 4, steps // 2, steps - 1})
+    qs, ks, vs = upload(ds.q, spec.dtype), upload(ds.k, spec.dtype), upload(ds.v, spec.dtype)
+    ncs = torch.from_numpy(ds.new_class).cuda()
+    got = {}
+    for t in range(steps):
+        o = cache.decode_step(qs[t], ks[t], vs[t], ncs[t])
+        if t in check:
+            got[t] = o.cpu().numpy()
+    torch.cuda.synchronize()
+    assert cache.error_bits() == 0
+    final = cache.kept_positions()
+    tol = DEC_TOL[spec.dtype]
+    worst = 0.0
+    for b in range(B):
+        for h in range(Hkv):
+            pol = int(pol_g[b, h])
+            sampled = (b, h) in decode_sample
+            sub = check if sampled else [steps - 1]
+            o_ref, c_ref = ref.decode_masked(li.K[b, h], li.V[b, h], li.token_class[b], F_g[b, h], w_l, pol,
+                                             ds.q[:, b, h * G:(h + 1) * G], ds.k[:, b, h], ds.v[:, b, h],
+                                             ds.new_class[:, b], steps_subset=sub)
+            assert np.array_equal(final[b * Hkv + h], c_ref[-1]), (b, h, "final cache")
+            if sampled:
+                for i, t in enumerate(sub):
+                    o_gpu = got[t][b, h * G:(h + 1) * G]
+                    scale = np.maximum(np.max(np.abs(o_ref[i]), axis=-1), 1e-30)
+                    err = float(np.max(np.max(np.abs(o_gpu - o_ref[i]), axis=-1) / scale))
+                    worst = max(worst, err)
+                    assert err <= tol, (b, h, t, err)
+    report["dec_err"] = worst
+    log(f"[fullsize] ok: checked={report['checked']} flagged={report['flagged']} dec err={worst:.2e} "
+        f"kept fraction={sum(len(k) for k in kept_g) / (B * Hkv * n):.3f}")
+    return report
