@@ -39,7 +39,114 @@ template <> struct Vec16<float> {
   }
 };
 
+// Merge of one head's partial states, the new token, the output and the cache
+// update (run by the last-arriving workgroup, or by the combine kernel).
 template <typename T, int D, int G>
+__device__ __forceinline__ void decode_tail(
+    int hd, int L, const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
+    const uint8_t* __restrict__ new_class, float* __restrict__ out, const float* __restrict__ part,
+    const int64_t* __restrict__ work_offset, T* __restrict__ Kc, T* __restrict__ Vc, int32_t* __restrict__ pos,
+    const int64_t* __restrict__ row_offset, int32_t* __restrict__ len, const int32_t* __restrict__ capacity,
+    const int32_t* __restrict__ ring, const uint8_t* __restrict__ policy, int32_t* __restrict__ arrive,
+    uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, float c) {
+  constexpr int kWaves = 4;
+  constexpr int GD = G * D;
+  constexpr int NGRP = GD >= 256 ? 1 : 256 / GD;   // item groups in the merge
+  __shared__ float cm[NGRP][GD], cs[NGRP][GD], ca[NGRP][GD];
+  __shared__ float s_self[G];
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int b = hd / Hkv;
+  const int pol = policy[hd];
+  const uint8_t cls = new_class ? new_class[b] : kNormal;
+  const int lvl_self = cls == kSpecial ? 0 : (cls == kPunct ? 1 : (w_l >= 1 ? 3 : 4));
+  const bool att_self = lvl_self <= pol;
+  const T* kn = k_new + (size_t)hd * D;
+  const T* vn = v_new + (size_t)hd * D;
+  for (int g = wave; g < G; g += kWaves) {              // the new token's scores
+    const T* qg = q + ((size_t)hd * G + g) * D;
+    float s = 0.f;
+    for (int t = lane; t < D; t += kWave) s = fmaf(to_f32(qg[t]), to_f32(kn[t]), s);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) s_self[g] = s * c;
+  }
+  const int64_t w0 = work_offset[hd];
+  const int n_items = (int)(work_offset[hd + 1] - w0);
+  __syncthreads();                                      // s_self visible
+  // one round of independent loads: thread (output o, item group grp) merges its
+  // items' partial states online; the groups are merged in LDS below
+  {
+    const int grp = tid / GD;
+    if (grp < NGRP) {
+      for (int o = tid % GD; o < GD; o += 256) {
+        const int g = o / D, dd = o % D;
+        float M = kNegBig, Ls = 0.f, As = 0.f;
+#pragma unroll 4
+        for (int w = grp; w < n_items; w += NGRP) {
+          const float* pp = part + ((size_t)(w0 + w) * G + g) * (D + 2);
+          const float mw = pp[0], lw = pp[1], aw = pp[2 + dd];
+          const bool live = lw > 0.f;                  // an empty item stored only (max, sum)
+          const float mn = live ? fmaxf(M, mw) : M;
+          const float s1 = fast_exp2(M - mn);
+          const float s2 = live ? fast_exp2(mw - mn) : 0.f;
+          Ls = fmaf(Ls, s1, live ? lw * s2 : 0.f);
+          As = fmaf(As, s1, live ? aw * s2 : 0.f);
+          M = mn;
+        }
+        cm[grp][o] = M;
+        cs[grp][o] = Ls;
+        ca[grp][o] = As;
+      }
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < GD; o += blockDim.x) {
+    const int g = o / D, dd = o % D;
+    float M = att_self ? s_self[g] : kNegBig;
+#pragma unroll
+    for (int r = 0; r < NGRP; ++r) M = fmaxf(M, cm[r][o]);
+    float Ls = 0.f, As = 0.f;
+#pragma unroll
+    for (int r = 0; r < NGRP; ++r) {
+      const float a = fast_exp2(cm[r][o] - M);
+      Ls = fmaf(cs[r][o], a, Ls);
+      As = fmaf(ca[r][o], a, As);
+    }
+    if (att_self) {
+      const float a = fast_exp2(s_self[g] - M);
+      Ls += a;
+      As = fmaf(a, to_f32(vn[dd]), As);
+    }
+    out[((size_t)hd * G + g) * D + dd] = Ls > 0.f ? As / Ls : 0.f;
+  }
+
+  // cache update: afterwards the cache holds {j <= p : level(p + 1, j) <= policy}
+  const int R = ring[hd];
+  const int64_t base_h = row_offset[hd];
+  const bool to_ring = (cls == kNormal) && pol == 3 && w_l >= 2 && R > 0;
+  const bool to_perm = cls == kSpecial || (cls == kPunct && pol >= 1) || (cls == kNormal && pol == 4);
+  const int slot = R > 0 ? p % R : 0;
+  int64_t dst = -1;
+  if (to_ring) dst = base_h + slot;
+  else if (to_perm && L < capacity[hd]) dst = base_h + L;
+  if (dst >= 0) {
+    for (int t = tid; t < D; t += blockDim.x) {
+      Kc[dst * D + t] = kn[t];
+      Vc[dst * D + t] = vn[t];
+    }
+  }
+  if (tid == 0) {
+    if (pol == 3 && R > 0 && !to_ring) pos[base_h + slot] = -1;   // key p + 1 - w_l leaves the window
+    if (dst >= 0) pos[dst] = p;
+    if (to_perm) {
+      if (dst >= 0) len[hd] = L + 1;
+      else atomicOr(error_word, 1u);
+    }
+    arrive[hd] = 0;
+  }
+}
+
+template <typename T, int D, int G, bool FUSED>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const uint8_t* __restrict__ new_class, float* __restrict__ out, float* __restrict__ part,
@@ -57,13 +164,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   constexpr int RPW = kSubRows / kWaves;    // rows per wave per pass
   constexpr int NP = RPW / RPP;             // passes per wave
   constexpr int GD = G * D;
-  constexpr int NGRP = GD >= 256 ? 1 : 256 / GD;   // item groups in the combine
   __shared__ float sm[kWaves][G], sl[kWaves][G];
   __shared__ float sacc[kWaves][G][D];
-  constexpr int kMaxItemsLds = 512 / G;   // items whose weights are staged in LDS
-  __shared__ float cs[NGRP][GD], ca[NGRP][GD];
-  __shared__ float s_wt[kMaxItemsLds * G], s_lw[kMaxItemsLds * G];
-  __shared__ float s_self[G], s_max[G];
   __shared__ int s_last;
 
   const int item = blockIdx.x;
@@ -110,8 +212,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) s = fmaf(qv[g][e], kv[e], s);
-#pragma unroll
-        for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
+        s = group_sum<LPR>(s);
         if (valid[i]) {
           const float x = s * c;
           const float mn = fmaxf(m[g], x);
@@ -170,6 +271,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     mypart[(size_t)tid * (D + 2) + 1] = 0.f;
   }
 
+  if (!FUSED) return;                                    // the combine kernel merges the partials
   // ---- arrival: the last workgroup of the head merges and updates the cache.
   // Every wave waits for its partial stores to complete, the barrier orders
   // them before thread 0's device-scope release (L2 write-back), and the last
@@ -186,139 +288,47 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   __syncthreads();
   if (!s_last) return;
 
-  const int b = hd / Hkv;
-  const int pol = policy[hd];
-  const uint8_t cls = new_class ? new_class[b] : kNormal;
-  const int lvl_self = cls == kSpecial ? 0 : (cls == kPunct ? 1 : (w_l >= 1 ? 3 : 4));
-  const bool att_self = lvl_self <= pol;
-  const T* kn = k_new + (size_t)hd * D;
-  const T* vn = v_new + (size_t)hd * D;
-  for (int g = wave; g < G; g += kWaves) {              // the new token's scores
-    const T* qg = q + ((size_t)hd * G + g) * D;
-    float s = 0.f;
-    for (int t = lane; t < D; t += kWave) s = fmaf(to_f32(qg[t]), to_f32(kn[t]), s);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    if (lane == 0) s_self[g] = s * c;
-  }
-  const int64_t w0 = work_offset[hd];
-  const int n_items = (int)(work_offset[hd + 1] - w0);
-  __syncthreads();                                      // s_self visible
-  // (a) every item's (max, sum) per query head into LDS, one thread per item: global max M_g
-  float mloc[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) mloc[g] = kNegBig;
-  for (int w = tid; w < n_items; w += blockDim.x) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float* pp = part + ((size_t)(w0 + w) * G + g) * (D + 2);
-      const float mw = pp[0], lw = pp[1];
-      if (lw > 0.f) mloc[g] = fmaxf(mloc[g], mw);
-      if (w < kMaxItemsLds) { s_wt[w * G + g] = mw; s_lw[w * G + g] = lw; }
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mloc[g] = fmaxf(mloc[g], __shfl_xor(mloc[g], o));
-    if (lane == 0) sm[wave][g] = mloc[g];
-  }
-  __syncthreads();
-  if (tid < G) {
-    float M = att_self ? s_self[tid] : kNegBig;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w][tid]);
-    s_max[tid] = M;
-  }
-  __syncthreads();
-  // (b) per-item weights 2^(m_w - M_g), zero for empty items, in place
-  for (int w = tid; w < min(n_items, kMaxItemsLds); w += blockDim.x) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float a = s_lw[w * G + g] > 0.f ? fast_exp2(s_wt[w * G + g] - s_max[g]) : 0.f;
-      s_wt[w * G + g] = a;
-    }
-  }
-  __syncthreads();
-  // (c) weighted sums: item groups over threads, independent loads
-  {
-    const int grp = tid / GD;
-    if (grp < NGRP) {
-      for (int o = tid % GD; o < GD; o += 256) {
-        const int g = o / D, dd = o % D;
-        float Ls = 0.f, As = 0.f;
-#pragma unroll 4
-        for (int w = grp; w < n_items; w += NGRP) {
-          const float* pp = part + ((size_t)(w0 + w) * G + g) * (D + 2);
-          float a, lw;
-          if (w < kMaxItemsLds) {
-            a = s_wt[w * G + g];
-            lw = s_lw[w * G + g];
-          } else {
-            lw = pp[1];
-            a = lw > 0.f ? fast_exp2(pp[0] - s_max[g]) : 0.f;
-          }
-          Ls = fmaf(lw, a, Ls);
-          As = fmaf(pp[2 + dd], a, As);
-        }
-        cs[grp][o] = Ls;
-        ca[grp][o] = As;
-      }
-    }
-  }
-  __syncthreads();
-  for (int o = tid; o < GD; o += blockDim.x) {
-    const int g = o / D, dd = o % D;
-    float Ls = 0.f, As = 0.f;
-#pragma unroll
-    for (int r = 0; r < NGRP; ++r) {
-      Ls += cs[r][o];
-      As += ca[r][o];
-    }
-    if (att_self) {
-      const float a = fast_exp2(s_self[g] - s_max[g]);
-      Ls += a;
-      As = fmaf(a, to_f32(vn[dd]), As);
-    }
-    out[((size_t)hd * G + g) * D + dd] = Ls > 0.f ? As / Ls : 0.f;
-  }
-
-  // cache update: afterwards the cache holds {j <= p : level(p + 1, j) <= policy}
-  const int R = ring[hd];
-  const int64_t base_h = row_offset[hd];
-  const bool to_ring = (cls == kNormal) && pol == 3 && w_l >= 2 && R > 0;
-  const bool to_perm = cls == kSpecial || (cls == kPunct && pol >= 1) || (cls == kNormal && pol == 4);
-  const int slot = R > 0 ? p % R : 0;
-  int64_t dst = -1;
-  if (to_ring) dst = base_h + slot;
-  else if (to_perm && L < capacity[hd]) dst = base_h + L;
-  if (dst >= 0) {
-    for (int t = tid; t < D; t += blockDim.x) {
-      Kc[dst * D + t] = kn[t];
-      Vc[dst * D + t] = vn[t];
-    }
-  }
-  if (tid == 0) {
-    if (pol == 3 && R > 0 && !to_ring) pos[base_h + slot] = -1;   // key p + 1 - w_l leaves the window
-    if (dst >= 0) pos[dst] = p;
-    if (to_perm) {
-      if (dst >= 0) len[hd] = L + 1;
-      else atomicOr(error_word, 1u);
-    }
-    arrive[hd] = 0;
-  }
+  decode_tail<T, D, G>(hd, L, q, k_new, v_new, new_class, out, part, work_offset, Kc, Vc, pos, row_offset, len,
+                       capacity, ring, policy, arrive, error_word, Hkv, w_l, p, c);
 }
+
+// Combine launch of the two-kernel decode step: one workgroup per head.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
+    const uint8_t* __restrict__ new_class, float* __restrict__ out, const float* __restrict__ part,
+    const int64_t* __restrict__ work_offset, T* __restrict__ Kc, T* __restrict__ Vc, int32_t* __restrict__ pos,
+    const int64_t* __restrict__ row_offset, int32_t* __restrict__ len, const int32_t* __restrict__ capacity,
+    const int32_t* __restrict__ ring, const uint8_t* __restrict__ policy, int32_t* __restrict__ arrive,
+    uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, float c) {
+  const int hd = blockIdx.x;
+  decode_tail<T, D, G>(hd, len[hd], q, k_new, v_new, new_class, out, part, work_offset, Kc, Vc, pos, row_offset,
+                       len, capacity, ring, policy, arrive, error_word, Hkv, w_l, p, c);
+}
+
+#ifndef FG_DECODE_FUSED
+#define FG_DECODE_FUSED 0
+#endif
 
 template <typename T, int D, int G>
 static hipError_t launch_decode_tg(const DecodeArgs& a, hipStream_t st) {
   const float c = kLog2e / sqrtf((float)D);
+  const int H = a.B * a.Hkv;
   timed_begin(FG_K_DECODE, st);
-  decode_step_kernel<T, D, G><<<dim3((unsigned)a.n_work), dim3(256), 0, st>>>(
+  decode_step_kernel<T, D, G, FG_DECODE_FUSED != 0><<<dim3((unsigned)a.n_work), dim3(256), 0, st>>>(
       (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work, a.work_offset,
       (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.arrive, a.error_word, a.Hkv,
       a.w_l, a.p, c);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && !FG_DECODE_FUSED) {
+    decode_combine_kernel<T, D, G><<<dim3(H), dim3(256), 0, st>>>(
+        (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work_offset,
+        (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.arrive, a.error_word,
+        a.Hkv, a.w_l, a.p, c);
+    e = hipGetLastError();
+  }
   timed_end(st);
-  return hipGetLastError();
+  return e;
 }
 
 template <typename T, int D>

@@ -48,6 +48,21 @@ __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 
 // that branches on it stay scalar branches instead of exec-masked regions.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// Sum over aligned groups of N lanes (N = 1..64, power of two); every lane of a
+// group receives the group's sum.  Groups up to 16 lanes use DPP lane permutes
+// on the VALU (quad_perm, row_half_mirror, row_mirror), wider ones fall back to
+// cross-lane shuffles.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if (N >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  if (N >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  if (N >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  if (N >= 16) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+  if (N >= 32) v += __shfl_xor(v, 16);
+  if (N >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
