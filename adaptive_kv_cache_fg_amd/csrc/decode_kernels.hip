@@ -41,7 +41,7 @@ template <> struct Vec16<float> {
 
 // Merge of one head's partial states, the new token, the output and the cache
 // update (run by the last-arriving workgroup, or by the combine kernel).
-template <typename T, int D, int G>
+template <typename T, int D, int G, int NT>
 __device__ __forceinline__ void decode_tail(
     int hd, int L, const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const uint8_t* __restrict__ new_class, float* __restrict__ out, const float* __restrict__ part,
@@ -51,7 +51,7 @@ __device__ __forceinline__ void decode_tail(
     uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, float c) {
   constexpr int kWaves = 4;
   constexpr int GD = G * D;
-  constexpr int NGRP = GD >= 256 ? 1 : 256 / GD;   // item groups in the merge
+  constexpr int NGRP = GD >= NT ? 1 : NT / GD;     // item groups in the merge
   __shared__ float cm[NGRP][GD], cs[NGRP][GD], ca[NGRP][GD];
   __shared__ float s_self[G];
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -62,7 +62,7 @@ __device__ __forceinline__ void decode_tail(
   const bool att_self = lvl_self <= pol;
   const T* kn = k_new + (size_t)hd * D;
   const T* vn = v_new + (size_t)hd * D;
-  for (int g = wave; g < G; g += kWaves) {              // the new token's scores
+  for (int g = wave; g < G; g += NT / kWave) {          // the new token's scores
     const T* qg = q + ((size_t)hd * G + g) * D;
     float s = 0.f;
     for (int t = lane; t < D; t += kWave) s = fmaf(to_f32(qg[t]), to_f32(kn[t]), s);
@@ -78,7 +78,7 @@ __device__ __forceinline__ void decode_tail(
   {
     const int grp = tid / GD;
     if (grp < NGRP) {
-      for (int o = tid % GD; o < GD; o += 256) {
+      for (int o = tid % GD; o < GD; o += NT) {
         const int g = o / D, dd = o % D;
         float M = kNegBig, Ls = 0.f, As = 0.f;
 #pragma unroll 4
@@ -288,13 +288,16 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   __syncthreads();
   if (!s_last) return;
 
-  decode_tail<T, D, G>(hd, L, q, k_new, v_new, new_class, out, part, work_offset, Kc, Vc, pos, row_offset, len,
+  decode_tail<T, D, G, 256>(hd, L, q, k_new, v_new, new_class, out, part, work_offset, Kc, Vc, pos, row_offset, len,
                        capacity, ring, policy, arrive, error_word, Hkv, w_l, p, c);
 }
 
-// Combine launch of the two-kernel decode step: one workgroup per head.
+// Combine launch of the two-kernel decode step: one workgroup per head, wide
+// enough that each thread merges only a few partial states.
+constexpr int kCombineThreads = 1024;
+
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const uint8_t* __restrict__ new_class, float* __restrict__ out, const float* __restrict__ part,
     const int64_t* __restrict__ work_offset, T* __restrict__ Kc, T* __restrict__ Vc, int32_t* __restrict__ pos,
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ ring, const uint8_t* __restrict__ policy, int32_t* __restrict__ arrive,
     uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, float c) {
   const int hd = blockIdx.x;
-  decode_tail<T, D, G>(hd, len[hd], q, k_new, v_new, new_class, out, part, work_offset, Kc, Vc, pos, row_offset,
+  decode_tail<T, D, G, kCombineThreads>(hd, len[hd], q, k_new, v_new, new_class, out, part, work_offset, Kc, Vc, pos, row_offset,
                        len, capacity, ring, policy, arrive, error_word, Hkv, w_l, p, c);
 }
 
@@ -321,7 +324,7 @@ static hipError_t launch_decode_tg(const DecodeArgs& a, hipStream_t st) {
       a.w_l, a.p, c);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && !FG_DECODE_FUSED) {
-    decode_combine_kernel<T, D, G><<<dim3(H), dim3(256), 0, st>>>(
+    decode_combine_kernel<T, D, G><<<dim3(H), dim3(kCombineThreads), 0, st>>>(
         (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work_offset,
         (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.arrive, a.error_word,
         a.Hkv, a.w_l, a.p, c);

@@ -83,6 +83,37 @@ def cpu_baseline(spec: syn.ConfigSpec, sample_heads: int) -> dict:
             "cpu_seconds": float(sum(a + b for a, b in res_d) + sum(a for a, _ in res))}
 
 
+# ---------------------------------------------------------------- HBM traffic from counters
+CALIB_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_sources_digest() -> str:
+    """Digest of the HIP sources; counter-derived traffic is reported only for the same sources."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "adaptive_kv_cache_fg_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` from profiles/traffic.json (FETCH_SIZE + WRITE_SIZE,
+    scaled by the calibration copy), or None when absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_digest") != kernel_sources_digest():
+        return None
+    v = t.get("bytes_per_launch", {}).get(kernel)
+    return float(v) if v is not None else None
+
+
 # ---------------------------------------------------------------- GPU path
 def upload(torch, x, dtype):
     if dtype == "bf16":
@@ -255,7 +286,15 @@ def main() -> int:
     dominant = max((k for k in kinfo if k in kstats), key=lambda k: kstats[k]["total_us_per_step"])
     dk = kstats[dominant]
     roofline = {"bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"], "unit": dk["unit"],
-                "frac": dk["frac"], "traffic": None, "kernel": dominant}
+                "frac": dk["frac"], "traffic": measured_traffic(dominant), "kernel": dominant}
+
+    # a plain copy of known size, outside the timed region: the reference that scales the
+    # FETCH_SIZE / WRITE_SIZE counters of the kernels above when this script runs under rocprofv3
+    calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     result = {
         "metric": "profile+compact prompt tok/s & decode tok/s on 1 MI355X; % MFMA / HBM peak",
