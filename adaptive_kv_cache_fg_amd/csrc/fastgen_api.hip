@@ -163,7 +163,9 @@ size_t fg_profile_workspace_size(const fg_shape* s) {
   if (check_shape(s) != FG_OK) return 0;
   const size_t rows_q = (size_t)s->batch * s->n_q_heads * s->seq_len;
   const size_t rows_k = (size_t)s->batch * s->n_kv_heads * s->seq_len;
-  return align256(rows_q * sizeof(float)) + align256(rows_k * sizeof(float));
+  const fg::SweepSplit sp = fg::sweep_split(s->batch, s->n_q_heads, s->n_kv_heads, s->seq_len);
+  return align256(rows_q * sizeof(float)) + align256(rows_k * sizeof(float)) + align256(sp.rs_bytes) +
+         align256(sp.cs_bytes);
 }
 
 fg_status fg_profile(const fg_shape* shape, const fg_params* params, const void* Q, const void* K,
@@ -193,7 +195,14 @@ fg_status fg_profile(const fg_shape* shape, const fg_params* params, const void*
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   a.lse2 = reinterpret_cast<float*>(ws);
   const size_t rows_q = (size_t)a.B * a.Hq * a.n;
+  const size_t rows_k = (size_t)a.B * a.Hkv * a.n;
   a.band = band_out ? band_out : reinterpret_cast<float*>(ws + align256(rows_q * sizeof(float)));
+  const fg::SweepSplit sp = fg::sweep_split(a.B, a.Hq, a.Hkv, a.n);
+  unsigned char* parts = ws + align256(rows_q * sizeof(float)) + align256(rows_k * sizeof(float));
+  a.kchunk = sp.kchunk;
+  a.rchunk = sp.rchunk;
+  a.rs_part = sp.rs_split ? reinterpret_cast<float2*>(parts) : nullptr;
+  a.cs_part = sp.cs_split ? reinterpret_cast<float2*>(parts + align256(sp.rs_bytes)) : nullptr;
   a.lse_out = lse_out;
   a.cum = cum_score;
   a.fmask = freq_mask;

@@ -26,7 +26,37 @@ struct ProfileArgs {
   uint32_t* fmask;   // [B*Hkv*ceil(n/32)]
   float* recovery;   // [B*Hkv*5]
   uint8_t* policy;   // [B*Hkv]
+  // small grids split the sweeps: key chunks of sweep 1 (partial max/sum per row,
+  // merged by a second launch) and row chunks of sweep 2 (partial column sums,
+  // added by the select pass); nullptr / chunk >= n means no split
+  int kchunk, rchunk;
+  float2* rs_part;   // [ceil(n/kchunk), B*Hq, n]
+  float2* cs_part;   // [ceil(n/rchunk), B*Hkv, n]
 };
+
+// Sweep tiling shared by the launcher and the workspace query.
+constexpr int kSweepRowsPerWG = 256;   // query rows per sweep-1 workgroup
+constexpr int kSweepKeysPerWG = 256;   // keys per sweep-2 workgroup
+constexpr int kSplitKeyChunk = 256;    // key chunk of a split sweep 1
+constexpr int kSplitRowChunk = 512;    // row chunk of a split sweep 2
+constexpr long long kSplitBelowGroups = 1024;  // split when the unsplit grid has fewer workgroups
+struct SweepSplit {
+  int kchunk, rchunk;
+  bool rs_split, cs_split;
+  size_t rs_bytes, cs_bytes;
+};
+inline SweepSplit sweep_split(int B, int Hq, int Hkv, int n) {
+  SweepSplit p{};
+  const int n_rb = (n + kSweepRowsPerWG - 1) / kSweepRowsPerWG;
+  const int n_kb = (n + kSweepKeysPerWG - 1) / kSweepKeysPerWG;
+  p.rs_split = (long long)B * Hq * n_rb < kSplitBelowGroups && n > kSplitKeyChunk;
+  p.cs_split = (long long)B * Hkv * n_kb < kSplitBelowGroups && n > kSplitRowChunk;
+  p.kchunk = p.rs_split ? kSplitKeyChunk : n_rb * kSweepRowsPerWG;
+  p.rchunk = p.cs_split ? kSplitRowChunk : n;
+  p.rs_bytes = p.rs_split ? (size_t)((n + p.kchunk - 1) / p.kchunk) * B * Hq * n * sizeof(float) * 2 : 0;
+  p.cs_bytes = p.cs_split ? (size_t)((n + p.rchunk - 1) / p.rchunk) * B * Hkv * n * sizeof(float) * 2 : 0;
+  return p;
+}
 
 hipError_t launch_profile_sweeps(const ProfileArgs& a, hipStream_t st);
 hipError_t launch_select(const ProfileArgs& a, hipStream_t st);

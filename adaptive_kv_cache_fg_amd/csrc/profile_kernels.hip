@@ -24,16 +24,18 @@
 // lane owns one key (column reductions stay in-lane).  The operand held in
 // registers is the one the workgroup owns (Q rows in sweep 1, K rows in
 // sweep 2); the streamed operand is staged in LDS once per workgroup.
+#include <algorithm>
+
 #include "fg_common.h"
 #include "fg_internal.h"
 
 namespace fg {
 
 constexpr int kRowsPerWave = 64;  // sweep 1: query rows per wave (two MFMA column blocks)
-constexpr int kRowsPerWG = 256;   // sweep 1: 4 waves x 64 query rows
+constexpr int kRowsPerWG = kSweepRowsPerWG;   // sweep 1: 4 waves x 64 query rows
 constexpr int kKeyTile = 64;      // sweep 1: keys staged per LDS tile
 constexpr int kKeysPerWave = 64;  // sweep 2: keys per wave (two MFMA column blocks)
-constexpr int kKeysPerWG = 256;   // sweep 2: 4 waves x 64 keys
+constexpr int kKeysPerWG = kSweepKeysPerWG;   // sweep 2: 4 waves x 64 keys
 constexpr int kRowTile = 64;      // sweep 2: query rows staged per LDS tile
 constexpr int kPadBytes = 16;     // LDS row padding against bank conflicts
 
@@ -110,16 +112,25 @@ __device__ __forceinline__ typename Mfma<T>::op_t global_operand(const T* rowptr
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                        float* __restrict__ lse2, float* __restrict__ lse_out,
-                                                       int Hq, int Hkv, int n, int n_rb, float c) {
+                                                       float2* __restrict__ rs_part, int Hq, int Hkv, int n,
+                                                       int n_rb, int kchunk, float c) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
   constexpr int NK = D / M::KS;
   constexpr int kRB = D * (int)sizeof(T) + kPadBytes;
   __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kKeyTile * kRB];
 
-  const int nbh = gridDim.x / n_rb;                      // B * Hq
-  const int rb = n_rb - 1 - (int)(blockIdx.x / nbh);     // heaviest row blocks first
-  const int bh = blockIdx.x % nbh;
+  const int nbh = Hq * (gridDim.y);                      // B * Hq (grid.y = batch)
+  const int bh = blockIdx.y * Hq + (int)(blockIdx.x % Hq);
+  // (row block, key chunk) of this workgroup, heaviest row blocks first; without
+  // splitting (rs_part == nullptr) every row block is one chunk
+  int rem = (int)(blockIdx.x / Hq), rb = n_rb - 1, ch = 0;
+  for (; rb > 0; --rb) {
+    const int nc = (min(n, (rb + 1) * kRowsPerWG) + kchunk - 1) / kchunk;
+    if (rem < nc) break;
+    rem -= nc;
+  }
+  ch = rem;
   const int b = bh / Hq, hq = bh % Hq, G = Hq / Hkv;
   const T* Qh = Q + (size_t)bh * n * D;
   const T* Kh = K + ((size_t)b * Hkv + hq / G) * n * D;
@@ -136,15 +147,16 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
   }
 
   float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
-  const int kend = min(n, (rb + 1) * kRowsPerWG);
-  const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
+  const int kbeg = ch * kchunk;                           // this chunk's keys [kbeg, kend)
+  const int kend = min(min(n, (rb + 1) * kRowsPerWG), kbeg + kchunk);
+  const int ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
   const int qlast = q0 + kRowsPerWave - 1;
 
   // One unit = 32 keys (half a staged tile) x this wave's 64 rows: 16 MFMAs into
   // acc[cb], then an online-softmax update per query block.  Units are software
   // pipelined: the MFMAs of unit u+1 are issued before the softmax of unit u, in
   // one basic block, so the matrix cores and the VALU work at the same time.
-  auto unit_active = [&](int key0) { return key0 <= qlast && key0 < n; };   // wave-uniform
+  auto unit_active = [&](int key0) { return key0 <= qlast && key0 < kend; };   // wave-uniform
   auto mfma_unit = [&](const unsigned char* kt, int kh, f32x16 (&acc)[2]) {
     op_t a[NK];
 #pragma unroll
@@ -157,7 +169,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
       acc[1] = M::mac(a[kk], qop[1][kk], acc[1]);
     }
   };
-  auto needs_mask = [&](int key0) { return key0 + 31 > q0 || key0 + 32 > n; };   // wave-uniform
+  auto needs_mask = [&](int key0) { return key0 + 31 > q0 || key0 + 32 > kend; };   // wave-uniform
   auto softmax_unit = [&](int key0, f32x16 (&acc)[2]) {
     if (needs_mask(key0)) {                                  // diagonal or ragged unit: mask
 #pragma unroll
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + acc_row(r, lane);
-          if (key > qrow || key >= n) acc[cb][r] = -INFINITY;
+          if (key > qrow || key >= kend) acc[cb][r] = -INFINITY;
         }
       }
     }
@@ -182,14 +194,14 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
   };
 
   Stager<T, D, kKeyTile> stg;
-  stg.prefetch(Kh, 0, n);
+  stg.prefetch(Kh, kbeg, kend);
   stg.commit(ktile[0]);
   __syncthreads();
   f32x16 accA[2], accB[2];
   int pend_key = -1;                                         // unit whose softmax is pending in accB
   for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * kKeyTile;
-    if (t + 1 < ntiles) stg.prefetch(Kh, k0 + kKeyTile, n);   // in flight during the MFMAs below
+    const int k0 = kbeg + t * kKeyTile;
+    if (t + 1 < ntiles) stg.prefetch(Kh, k0 + kKeyTile, kend);   // in flight during the MFMAs below
     const unsigned char* kt = ktile[t & 1];
     const bool act0 = unit_active(k0), act1 = unit_active(k0 + 32);
     if (act0) mfma_unit(kt, 0, accA);
@@ -210,11 +222,38 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
     const float L = l[cb] * fast_exp2(m[cb] - M2) + l_o * fast_exp2(m_o - M2);
     const int qrow = q0 + 32 * cb + (lane & 31);
     if (lane < 32 && qrow < n) {
-      const float v = M2 + fast_log2(L);
-      lse2[(size_t)bh * n + qrow] = v;
-      if (lse_out) lse_out[(size_t)bh * n + qrow] = v * kLn2;
+      if (rs_part) {                                       // one key chunk: keep (max, sum) for the merge
+        rs_part[((size_t)ch * nbh + bh) * n + qrow] = make_float2(M2, L);
+      } else {
+        const float v = M2 + fast_log2(L);
+        lse2[(size_t)bh * n + qrow] = v;
+        if (lse_out) lse_out[(size_t)bh * n + qrow] = v * kLn2;
+      }
     }
   }
+}
+
+// Merge of the key chunks' (max, sum) of each row into its log-sum-exp.
+__global__ __launch_bounds__(256) void rowstats_merge_kernel(const float2* __restrict__ rs_part,
+                                                             float* __restrict__ lse2, float* __restrict__ lse_out,
+                                                             int nbh, int n, int kchunk) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)nbh * n) return;
+  const int row = (int)(idx % n);
+  const int nc = (min(n, (row / kRowsPerWG + 1) * kRowsPerWG) + kchunk - 1) / kchunk;
+  float M = kNegBig;
+  for (int ch = 0; ch < nc; ++ch) {
+    const float2 v = rs_part[(size_t)ch * nbh * n + idx];
+    if (v.y > 0.f) M = fmaxf(M, v.x);
+  }
+  float L = 0.f;
+  for (int ch = 0; ch < nc; ++ch) {
+    const float2 v = rs_part[(size_t)ch * nbh * n + idx];
+    if (v.y > 0.f) L = fmaf(v.y, fast_exp2(v.x - M), L);
+  }
+  const float v = M + fast_log2(L);
+  lse2[idx] = v;
+  if (lse_out) lse_out[idx] = v * kLn2;
 }
 
 // ---------------------------------------------------------------- sweep 2: column and band sums
@@ -224,8 +263,9 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                       const float* __restrict__ lse2, float* __restrict__ cum,
-                                                      float* __restrict__ band, int Hq, int Hkv, int n, int n_kb,
-                                                      int w_l, float c) {
+                                                      float* __restrict__ band, float2* __restrict__ cs_part,
+                                                      int Hq, int Hkv, int n, int n_kb, int rchunk, int w_l,
+                                                      float c) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
   constexpr int NK = D / M::KS;
@@ -233,9 +273,17 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   __shared__ __attribute__((aligned(16))) unsigned char qtile[2][kRowTile * kRB];
   __shared__ __attribute__((aligned(16))) float lse_t[2][kRowTile];
 
-  const int nbh = gridDim.x / n_kb;                      // B * Hkv
-  const int kb = (int)(blockIdx.x / nbh);                // key block 0 (most rows) first
-  const int bh = blockIdx.x % nbh;
+  const int nbh = Hkv * (gridDim.y);                     // B * Hkv (grid.y = batch)
+  const int bh = blockIdx.y * Hkv + (int)(blockIdx.x % Hkv);
+  // (key block, row chunk) of this workgroup, key block 0 (most rows) first;
+  // without splitting (cs_part == nullptr) every key block is one chunk
+  int rem = (int)(blockIdx.x / Hkv), kb = 0;
+  for (; kb < n_kb - 1; ++kb) {
+    const int nc = (n - kb * kKeysPerWG + rchunk - 1) / rchunk;
+    if (rem < nc) break;
+    rem -= nc;
+  }
+  const int ch = rem;
   const int b = bh / Hkv, h = bh % Hkv, G = Hq / Hkv;
   const T* Kh = K + (size_t)bh * n * D;
 
@@ -252,16 +300,17 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
 
   float cum_acc[2] = {0.f, 0.f}, band_acc[2] = {0.f, 0.f};
   float cum_g[2] = {0.f, 0.f}, band_g[2] = {0.f, 0.f};
-  const int i_begin = kb * kKeysPerWG;
-  const int ntiles = (n - i_begin + kRowTile - 1) / kRowTile;   // query tiles per query head
+  const int i_begin = kb * kKeysPerWG + ch * rchunk;     // this chunk's query rows [i_begin, i_end)
+  const int i_end = min(n, i_begin + rchunk);
+  const int ntiles = (i_end - i_begin + kRowTile - 1) / kRowTile;   // query tiles per query head
   const int total = G * ntiles;
   Stager<T, D, kRowTile> stg;
   float lpre = 0.f;
   auto issue = [&](int u) {                                      // tile u of the (g, tile) sequence
     const int g = u / ntiles, i0 = i_begin + (u % ntiles) * kRowTile;
     const size_t qh = (size_t)b * Hq + (size_t)h * G + g;
-    stg.prefetch(Q + qh * n * D, i0, n);
-    if (threadIdx.x < kRowTile) lpre = (i0 + (int)threadIdx.x < n) ? lse2[qh * n + i0 + threadIdx.x] : INFINITY;
+    stg.prefetch(Q + qh * n * D, i0, i_end);
+    if (threadIdx.x < kRowTile) lpre = (i0 + (int)threadIdx.x < i_end) ? lse2[qh * n + i0 + threadIdx.x] : INFINITY;
   };
   auto commit = [&](int buf) {
     stg.commit(qtile[buf]);
@@ -275,11 +324,11 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
     const int i0 = i_begin + (u % ntiles) * kRowTile;
     const unsigned char* qt = qtile[u & 1];
     const float* lt = lse_t[u & 1];
-    if (i0 + kRowTile - 1 >= j0 && i0 < n) {                    // wave-uniform: some pair is causal
+    if (i0 + kRowTile - 1 >= j0 && i0 < i_end) {                // wave-uniform: some pair is causal
 #pragma unroll
       for (int rh = 0; rh < 2; ++rh) {                          // 32-row halves of the tile
         const int r0 = i0 + 32 * rh;
-        if (r0 + 31 < j0 || r0 >= n) continue;                  // wave-uniform
+        if (r0 + 31 < j0 || r0 >= i_end) continue;              // wave-uniform
         op_t a[NK];
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) a[kk] = lds_operand<T, D>(qt, 32 * rh + (lane & 31), kk, lane);
@@ -340,8 +389,12 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
     const float bs = band_acc[kc] + __shfl_xor(band_acc[kc], 32);
     const int key = j0 + 32 * kc + (lane & 31);
     if (lane < 32 && key < n) {
-      cum[(size_t)bh * n + key] = cs;
-      band[(size_t)bh * n + key] = bs;
+      if (cs_part) {                                      // one row chunk: partial sums for the select pass
+        cs_part[((size_t)ch * nbh + bh) * n + key] = make_float2(cs, bs);
+      } else {
+        cum[(size_t)bh * n + key] = cs;
+        band[(size_t)bh * n + key] = bs;
+      }
     }
   }
 }
@@ -351,15 +404,25 @@ static hipError_t launch_profile_sweeps_t(const ProfileArgs& a, hipStream_t st) 
   const int n_rb = (a.n + kRowsPerWG - 1) / kRowsPerWG;
   const int n_kb = (a.n + kKeysPerWG - 1) / kKeysPerWG;
   const float c = kLog2e / sqrtf((float)D);
+  // workgroups per (batch entry, head): key chunks of every row block / row chunks of every key block
+  long long rs_groups = 0, cs_groups = 0;
+  for (int rb = 0; rb < n_rb; ++rb) rs_groups += (std::min(a.n, (rb + 1) * kRowsPerWG) + a.kchunk - 1) / a.kchunk;
+  for (int kb = 0; kb < n_kb; ++kb) cs_groups += (a.n - kb * kKeysPerWG + a.rchunk - 1) / a.rchunk;
   timed_begin(FG_K_ROWSTATS, st);
-  rowstats_kernel<T, D><<<dim3(a.B * a.Hq * n_rb), dim3(256), 0, st>>>(
-      (const T*)a.Q, (const T*)a.K, a.lse2, a.lse_out, a.Hq, a.Hkv, a.n, n_rb, c);
-  timed_end(st);
+  rowstats_kernel<T, D><<<dim3((unsigned)(a.Hq * rs_groups), a.B), dim3(256), 0, st>>>(
+      (const T*)a.Q, (const T*)a.K, a.lse2, a.lse_out, a.rs_part, a.Hq, a.Hkv, a.n, n_rb, a.kchunk, c);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && a.rs_part) {
+    const size_t rows = (size_t)a.B * a.Hq * a.n;
+    rowstats_merge_kernel<<<dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st>>>(
+        a.rs_part, a.lse2, a.lse_out, a.B * a.Hq, a.n, a.kchunk);
+    e = hipGetLastError();
+  }
+  timed_end(st);
   if (e != hipSuccess) return e;
   timed_begin(FG_K_COLSUMS, st);
-  colsums_kernel<T, D><<<dim3(a.B * a.Hkv * n_kb), dim3(256), 0, st>>>(
-      (const T*)a.Q, (const T*)a.K, a.lse2, a.cum, a.band, a.Hq, a.Hkv, a.n, n_kb, a.w_l, c);
+  colsums_kernel<T, D><<<dim3((unsigned)(a.Hkv * cs_groups), a.B), dim3(256), 0, st>>>(
+      (const T*)a.Q, (const T*)a.K, a.lse2, a.cum, a.band, a.cs_part, a.Hq, a.Hkv, a.n, n_kb, a.rchunk, a.w_l, c);
   timed_end(st);
   return hipGetLastError();
 }

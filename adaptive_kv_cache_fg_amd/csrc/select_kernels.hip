@@ -37,7 +37,8 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   return t;   // valid in thread 0
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ cum, const float* __restrict__ band,
+__global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__ cum, float* __restrict__ band,
+                                                             const float2* __restrict__ cs_part, int rchunk,
                                                              const uint8_t* __restrict__ cls, int Hkv, int n, int G,
                                                              int k_f, double T, uint32_t* __restrict__ fmask,
                                                              float* __restrict__ recovery, uint8_t* __restrict__ policy) {
@@ -47,6 +48,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   __shared__ double red[kSelThreads / 64];
 
   const int bh = blockIdx.x, b = bh / Hkv;
+  if (cs_part) {
+    // the column sweep ran in row chunks: add each key's partial sums in chunk order
+    const int nbh = gridDim.x;
+    for (int j = threadIdx.x; j < n; j += blockDim.x) {
+      const int nc = (n - (j / kSweepKeysPerWG) * kSweepKeysPerWG + rchunk - 1) / rchunk;
+      float cs = 0.f, bs = 0.f;
+      for (int ch = 0; ch < nc; ++ch) {
+        const float2 v = cs_part[((size_t)ch * nbh + bh) * n + j];
+        cs += v.x;
+        bs += v.y;
+      }
+      cum[(size_t)bh * n + j] = cs;
+      band[(size_t)bh * n + j] = bs;
+    }
+    __syncthreads();
+  }
   const float* cu = cum + (size_t)bh * n;
   const float* bd = band + (size_t)bh * n;
   const uint8_t* cl = cls + (size_t)b * n;
@@ -162,8 +179,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
 
 hipError_t launch_select(const ProfileArgs& a, hipStream_t st) {
   timed_begin(FG_K_SELECT, st);
-  select_kernel<<<dim3(a.B * a.Hkv), dim3(kSelThreads), 0, st>>>(a.cum, a.band, a.cls, a.Hkv, a.n, a.Hq / a.Hkv,
-                                                                  a.k_f, a.T, a.fmask, a.recovery, a.policy);
+  select_kernel<<<dim3(a.B * a.Hkv), dim3(kSelThreads), 0, st>>>(a.cum, a.band, a.cs_part, a.rchunk, a.cls, a.Hkv,
+                                                                  a.n, a.Hq / a.Hkv, a.k_f, a.T, a.fmask,
+                                                                  a.recovery, a.policy);
   timed_end(st);
   return hipGetLastError();
 }

@@ -88,7 +88,8 @@ def test_profile_rejects_null_and_small_workspace():
     params = fgb.FgParams(0.3, 0.3, 0.95)
     assert _call_profile(shape, params, ptr=0) == 1
     need = fgb.lib().fg_profile_workspace_size(ctypes.byref(shape))
-    assert need == ((2 * 8 * 300 * 4 + 255) // 256) * 256 + ((2 * 2 * 300 * 4 + 255) // 256) * 256
+    # lse + band, plus the partial buffers of a small grid's split sweeps
+    assert need >= ((2 * 8 * 300 * 4 + 255) // 256) * 256 + ((2 * 2 * 300 * 4 + 255) // 256) * 256
     assert _call_profile(shape, params, ws_bytes=need - 1) == 3
     # misaligned Q
     assert _call_profile(shape, params, ptr=0x1004) == 1
