@@ -33,10 +33,10 @@ namespace fg {
 
 constexpr int kRowsPerWave = 64;  // sweep 1: query rows per wave (two MFMA column blocks)
 constexpr int kRowsPerWG = kSweepRowsPerWG;   // sweep 1: 4 waves x 64 query rows
-constexpr int kKeyTile = 64;      // sweep 1: keys staged per LDS tile
+constexpr int kKeyTile = 128;     // sweep 1: keys staged per LDS tile (4 units of 32 keys)
 constexpr int kKeysPerWave = 64;  // sweep 2: keys per wave (two MFMA column blocks)
 constexpr int kKeysPerWG = kSweepKeysPerWG;   // sweep 2: 4 waves x 64 keys
-constexpr int kRowTile = 64;      // sweep 2: query rows staged per LDS tile
+constexpr int kRowTile = 128;     // sweep 2: query rows staged per LDS tile (4 halves of 32 rows)
 constexpr int kPadBytes = 16;     // LDS row padding against bank conflicts
 
 // Staging of a tile of ROWS rows x D elements through LDS in two halves so
@@ -75,12 +75,11 @@ struct Stager {
 
 // Pairwise (tree) reductions of an accumulator tile: depth 4 instead of a
 // 16-long dependent chain, so a wave keeps several VALU ops in flight.
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }  // v_max3_f32
 __device__ __forceinline__ float tree_max16(const f32x16& a) {
-  const float b0 = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
-  const float b1 = fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7]));
-  const float b2 = fmaxf(fmaxf(a[8], a[9]), fmaxf(a[10], a[11]));
-  const float b3 = fmaxf(fmaxf(a[12], a[13]), fmaxf(a[14], a[15]));
-  return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
+  const float m0 = max3(a[0], a[1], a[2]), m1 = max3(a[3], a[4], a[5]), m2 = max3(a[6], a[7], a[8]);
+  const float m3 = max3(a[9], a[10], a[11]), m4 = max3(a[12], a[13], a[14]);
+  return fmaxf(max3(m0, m1, m2), max3(m3, m4, a[15]));
 }
 __device__ __forceinline__ float tree_sum16(const float* p) {
   const float b0 = (p[0] + p[1]) + (p[2] + p[3]);
@@ -197,23 +196,25 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
   stg.prefetch(Kh, kbeg, kend);
   stg.commit(ktile[0]);
   __syncthreads();
-  f32x16 accA[2], accB[2];
-  int pend_key = -1;                                         // unit whose softmax is pending in accB
+  f32x16 acc[2][2];                                          // [buffer][query block], one unit of 32 keys
+  int pend_key = -1;                                         // unit whose softmax is pending in acc[1]
+  constexpr int NU = kKeyTile / 32;                          // 32-key units per staged tile (even)
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = kbeg + t * kKeyTile;
     if (t + 1 < ntiles) stg.prefetch(Kh, k0 + kKeyTile, kend);   // in flight during the MFMAs below
     const unsigned char* kt = ktile[t & 1];
-    const bool act0 = unit_active(k0), act1 = unit_active(k0 + 32);
-    if (act0) mfma_unit(kt, 0, accA);
-    if (pend_key >= 0) softmax_unit(pend_key, accB);          // independent of the MFMAs above
-    pend_key = -1;
-    if (act1) mfma_unit(kt, 1, accB);
-    if (act0) softmax_unit(k0, accA);                          // independent of the MFMAs above
-    if (act1) pend_key = k0 + 32;
+#pragma unroll
+    for (int kh = 0; kh < NU; ++kh) {
+      const int key0 = k0 + 32 * kh;
+      const bool act = unit_active(key0);
+      if (act) mfma_unit(kt, kh, acc[kh & 1]);
+      if (pend_key >= 0) softmax_unit(pend_key, acc[(kh & 1) ^ 1]);   // independent of the MFMAs above
+      pend_key = act ? key0 : -1;
+    }
     if (t + 1 < ntiles) stg.commit(ktile[(t + 1) & 1]);
     __syncthreads();
   }
-  if (pend_key >= 0) softmax_unit(pend_key, accB);
+  if (pend_key >= 0) softmax_unit(pend_key, acc[(NU - 1) & 1]);
   // lanes l and l ^ 32 saw disjoint key subsets of the same query row
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
     const float* lt = lse_t[u & 1];
     if (i0 + kRowTile - 1 >= j0 && i0 < i_end) {                // wave-uniform: some pair is causal
 #pragma unroll
-      for (int rh = 0; rh < 2; ++rh) {                          // 32-row halves of the tile
+      for (int rh = 0; rh < kRowTile / 32; ++rh) {              // 32-row slices of the tile
         const int r0 = i0 + 32 * rh;
         if (r0 + 31 < j0 || r0 >= i_end) continue;              // wave-uniform
         op_t a[NK];
