@@ -39,39 +39,60 @@ constexpr int kKeysPerWG = kSweepKeysPerWG;   // sweep 2: 4 waves x 64 keys
 constexpr int kRowTile = 128;     // sweep 2: query rows staged per LDS tile (4 halves of 32 rows)
 constexpr int kPadBytes = 16;     // LDS row padding against bank conflicts
 
-// Staging of a tile of ROWS rows x D elements through LDS in two halves so
-// that the global loads of tile t+1 are in flight while tile t is computed:
-// prefetch() issues 16-byte loads into registers (zeros past row n), commit()
-// writes them into an LDS buffer whose rows are padded against bank conflicts.
+// Staging of a tile of ROWS rows x D elements into LDS with direct
+// global-to-LDS loads (global_load_lds_dwordx4): the data never passes through
+// registers, so the loads of tile t+1 run while tile t is computed at no VGPR
+// cost.  One wave-wide load writes 64 consecutive 16-byte LDS slots; the tile
+// is laid out as rows of kChunks data slots plus one pad slot (against bank
+// conflicts of the operand reads), so slot s holds row s / kSlotsPerRow and the
+// lanes that land on a pad slot load a dummy chunk.  Rows at or past n load
+// row n - 1 (finite values the callers mask).  The per-lane byte offsets of the
+// kPerWave loads do not depend on the tile and are computed once.
 template <typename T, int D, int ROWS>
-struct Stager {
+struct LdsLoader {
   static constexpr int kRowBytes = D * (int)sizeof(T);
-  static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
-  static constexpr int kRB = kRowBytes + kPadBytes;
-  static constexpr int kPer = ROWS * kChunks / 256;       // chunks per thread (256 threads)
-  static constexpr int kBytes = ROWS * kRB;
-  uint4 r[kPer];
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kSlotsPerRow = kChunks + kPadBytes / 16;
+  static constexpr int kWaveLoads = ROWS * kSlotsPerRow / 64;
+  static constexpr int kPerWave = (kWaveLoads + 3) / 4;   // 4 waves per workgroup
+  static_assert(ROWS * kSlotsPerRow % 64 == 0, "tile must be whole wave loads");
+  int row[kPerWave], off[kPerWave];                        // tile row and byte offset within it
 
-  __device__ __forceinline__ void prefetch(const T* src, int r0, int n) {
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = threadIdx.x + i * 256;
-      const int row = c / kChunks, q = c % kChunks;
-      r[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (r0 + row < n)
-        r[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(src) +
-                                               (size_t)(r0 + row) * kRowBytes + q * 16);
+    for (int j = 0; j < kPerWave; ++j) {
+      const int s = (4 * j + w) * 64 + lane;
+      const int r = s / kSlotsPerRow, pos = s - r * kSlotsPerRow;
+      row[j] = r;
+      off[j] = r * kRowBytes + (pos < kChunks ? pos : 0) * 16;
     }
   }
-  __device__ __forceinline__ void commit(unsigned char* lds) const {
+  // Issue the loads of rows [r0, r0 + ROWS) of src (n rows) into lds.
+  __device__ __forceinline__ void issue(const T* src, int r0, int n, unsigned char* lds, int w) const {
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(src) + (size_t)r0 * kRowBytes;
+    if (r0 + ROWS <= n) {                                  // wave-uniform: the whole tile exists
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = threadIdx.x + i * 256;
-      const int row = c / kChunks, q = c % kChunks;
-      *reinterpret_cast<uint4*>(lds + row * kRB + q * 16) = r[i];
+      for (int j = 0; j < kPerWave; ++j) load(base, (unsigned)off[j], lds, j, w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPerWave; ++j)
+        load(base, (unsigned)(off[j] - max(0, r0 + row[j] - (n - 1)) * kRowBytes), lds, j, w);
     }
+  }
+  // base is wave-uniform and o a 32-bit lane offset: the scalar-base + vector-offset form
+  static __device__ __forceinline__ void load(const unsigned char* base, unsigned o, unsigned char* lds, int j,
+                                              int w) {
+    if (kWaveLoads % 4 != 0 && j == kPerWave - 1 && 4 * j + w >= kWaveLoads) return;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + o),
+                                     reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                         reinterpret_cast<uintptr_t>(lds + (4 * j + w) * 1024)),
+                                     16, 0, 0);
   }
 };
+
+// Completion of this wave's direct LDS loads (their writes are then visible to
+// the workgroup after the barrier that follows).
+__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Pairwise (tree) reductions of an accumulator tile: depth 4 instead of a
 // 16-long dependent chain, so a wave keeps several VALU ops in flight.
@@ -169,6 +190,17 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
     }
   };
   auto needs_mask = [&](int key0) { return key0 + 31 > q0 || key0 + 32 > kend; };   // wave-uniform
+  auto softmax_update = [&](f32x16 (&acc)[2]) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float m_new = fmaxf(m[cb], tree_max16(acc[cb]) * c);
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(acc[cb][r], c, -m_new));
+      l[cb] = fmaf(l[cb], fast_exp2(m[cb] - m_new), tree_sum16(e));
+      m[cb] = m_new;
+    }
+  };
   auto softmax_unit = [&](int key0, f32x16 (&acc)[2]) {
     if (needs_mask(key0)) {                                  // diagonal or ragged unit: mask
 #pragma unroll
@@ -181,27 +213,19 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
         }
       }
     }
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const float m_new = fmaxf(m[cb], tree_max16(acc[cb]) * c);
-      float e[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(acc[cb][r], c, -m_new));
-      l[cb] = fmaf(l[cb], fast_exp2(m[cb] - m_new), tree_sum16(e));
-      m[cb] = m_new;
-    }
+    softmax_update(acc);
   };
-
-  Stager<T, D, kKeyTile> stg;
-  stg.prefetch(Kh, kbeg, kend);
-  stg.commit(ktile[0]);
+  LdsLoader<T, D, kKeyTile> ldr;
+  ldr.init(wave, lane);
+  ldr.issue(Kh, kbeg, n, ktile[0], wave);
+  wait_lds_loads();
   __syncthreads();
   f32x16 acc[2][2];                                          // [buffer][query block], one unit of 32 keys
   int pend_key = -1;                                         // unit whose softmax is pending in acc[1]
   constexpr int NU = kKeyTile / 32;                          // 32-key units per staged tile (even)
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = kbeg + t * kKeyTile;
-    if (t + 1 < ntiles) stg.prefetch(Kh, k0 + kKeyTile, kend);   // in flight during the MFMAs below
+    if (t + 1 < ntiles) ldr.issue(Kh, k0 + kKeyTile, n, ktile[(t + 1) & 1], wave);   // in flight during the MFMAs below
     const unsigned char* kt = ktile[t & 1];
 #pragma unroll
     for (int kh = 0; kh < NU; ++kh) {
@@ -211,7 +235,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
       if (pend_key >= 0) softmax_unit(pend_key, acc[(kh & 1) ^ 1]);   // independent of the MFMAs above
       pend_key = act ? key0 : -1;
     }
-    if (t + 1 < ntiles) stg.commit(ktile[(t + 1) & 1]);
+    wait_lds_loads();
     __syncthreads();
   }
   if (pend_key >= 0) softmax_unit(pend_key, acc[(NU - 1) & 1]);
@@ -299,30 +323,36 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
     for (int kk = 0; kk < NK; ++kk) kop[kc][kk] = global_operand<T, D>(Kh + (size_t)kr * D, kk, lane);
   }
 
-  float cum_acc[2] = {0.f, 0.f}, band_acc[2] = {0.f, 0.f};
+  float cum_acc[2] = {0.f, 0.f}, band_acc[2] = {0.f, 0.f};   // per key; summed per query head first
   float cum_g[2] = {0.f, 0.f}, band_g[2] = {0.f, 0.f};
   const int i_begin = kb * kKeysPerWG + ch * rchunk;     // this chunk's query rows [i_begin, i_end)
   const int i_end = min(n, i_begin + rchunk);
   const int ntiles = (i_end - i_begin + kRowTile - 1) / kRowTile;   // query tiles per query head
   const int total = G * ntiles;
-  Stager<T, D, kRowTile> stg;
+  LdsLoader<T, D, kRowTile> ldr;
+  ldr.init(wave, lane);
   float lpre = 0.f;
-  auto issue = [&](int u) {                                      // tile u of the (g, tile) sequence
-    const int g = u / ntiles, i0 = i_begin + (u % ntiles) * kRowTile;
-    const size_t qh = (size_t)b * Hq + (size_t)h * G + g;
-    stg.prefetch(Q + qh * n * D, i0, i_end);
+  // tiles run over (query head g, row tile) with the row tile fastest; the
+  // next tile to issue is tracked incrementally (no integer division per tile)
+  int ig = 0, it = 0;
+  auto issue = [&](int u) {                                      // tile u = (ig, it) of the sequence
+    const int i0 = i_begin + it * kRowTile;
+    const size_t qh = (size_t)b * Hq + (size_t)h * G + ig;
+    ldr.issue(Q + qh * n * D, i0, n, qtile[u & 1], wave);
     if (threadIdx.x < kRowTile) lpre = (i0 + (int)threadIdx.x < i_end) ? lse2[qh * n + i0 + threadIdx.x] : INFINITY;
+    if (++it == ntiles) { it = 0; ++ig; }
   };
-  auto commit = [&](int buf) {
-    stg.commit(qtile[buf]);
-    if (threadIdx.x < kRowTile) lse_t[buf][threadIdx.x] = lpre;     // rows past n get P = 0
+  auto commit = [&](int u) {                                     // tile u's lse2 into its LDS slot
+    wait_lds_loads();
+    if (threadIdx.x < kRowTile) lse_t[u & 1][threadIdx.x] = lpre;   // rows past the chunk get P = 0
   };
   issue(0);
   commit(0);
   __syncthreads();
+  int t_cur = 0;                                                 // row tile of tile u
   for (int u = 0; u < total; ++u) {
     if (u + 1 < total) issue(u + 1);
-    const int i0 = i_begin + (u % ntiles) * kRowTile;
+    const int i0 = i_begin + t_cur * kRowTile;
     const unsigned char* qt = qtile[u & 1];
     const float* lt = lse_t[u & 1];
     if (i0 + kRowTile - 1 >= j0 && i0 < i_end) {                // wave-uniform: some pair is causal
@@ -361,7 +391,7 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
           const float ts = tree_sum16(p);
           cum_g[kc] += ts;
           if ((r0 + 31) - jc < w_l) {
-            band_g[kc] += ts;                                   // every pair of the half is in the band
+            band_g[kc] += ts;                                   // every pair of the slice is in the band
           } else if (r0 - (jc + 31) < w_l) {
             float tb = 0.f;
 #pragma unroll
@@ -372,7 +402,8 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
         }
       }
     }
-    if ((u + 1) % ntiles == 0) {                                // end of one query head's rows
+    if (++t_cur == ntiles) {                                    // end of one query head's rows
+      t_cur = 0;
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         cum_acc[kc] += cum_g[kc];
@@ -381,7 +412,7 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
         band_g[kc] = 0.f;
       }
     }
-    if (u + 1 < total) commit((u + 1) & 1);
+    if (u + 1 < total) commit(u + 1);
     __syncthreads();
   }
 #pragma unroll
