@@ -66,19 +66,22 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ c
   }
 }
 
-// Exclusive prefix sums over heads: rows and decode work items.  One workgroup.
+// Exclusive prefix sums over heads: rows and decode work items, and the largest
+// item count of a head.  One workgroup.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ capacity, int H, int chunk,
                                                     int64_t* __restrict__ row_offset, int64_t* __restrict__ work_offset,
                                                     int64_t* __restrict__ totals) {
   __shared__ long long sr[1024], sw[1024];
   __shared__ long long carry_r, carry_w;
-  if (threadIdx.x == 0) { carry_r = 0; carry_w = 0; }
+  __shared__ int max_w;
+  if (threadIdx.x == 0) { carry_r = 0; carry_w = 0; max_w = 1; }
   __syncthreads();
   for (int base = 0; base < H; base += blockDim.x) {
     const int i = base + threadIdx.x;
     const long long cap = i < H ? capacity[i] : 0;
     sr[threadIdx.x] = cap;
     sw[threadIdx.x] = i < H ? max(1LL, (cap + chunk - 1) / chunk) : 0;   // every head gets an item
+    atomicMax(&max_w, (int)sw[threadIdx.x]);
     __syncthreads();
     for (int o = 1; o < (int)blockDim.x; o <<= 1) {          // inclusive Hillis-Steele scan
       const long long ar = threadIdx.x >= (unsigned)o ? sr[threadIdx.x - o] : 0;
@@ -101,6 +104,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
     work_offset[0] = 0;
     totals[0] = carry_r;
     totals[1] = carry_w;
+    totals[2] = max_w;
   }
 }
 
@@ -179,14 +183,23 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, co
   }
 }
 
-__global__ __launch_bounds__(256) void worklist_kernel(const int64_t* __restrict__ work_offset, int chunk,
-                                                       int32_t* __restrict__ work, int32_t* __restrict__ arrive) {
+// Decode work items of one head: 128-row chunks of its capacity, each
+// (head, first row, first absolute row, rows in use).  The rows-in-use count of
+// an item is kept current by the decode step's appends.
+__global__ __launch_bounds__(256) void worklist_kernel(const int64_t* __restrict__ work_offset,
+                                                       const int64_t* __restrict__ row_offset,
+                                                       const int32_t* __restrict__ len, int chunk,
+                                                       int32_t* __restrict__ work) {
   const int hd = blockIdx.x;
-  if (threadIdx.x == 0) arrive[hd] = 0;
   const int64_t w0 = work_offset[hd], w1 = work_offset[hd + 1];
+  const int64_t base = row_offset[hd];
+  const int L = len[hd];
   for (int64_t w = w0 + threadIdx.x; w < w1; w += blockDim.x) {
-    work[2 * w] = hd;
-    work[2 * w + 1] = (int32_t)((w - w0) * chunk);
+    const int start = (int)((w - w0) * chunk);
+    work[4 * w] = hd;
+    work[4 * w + 1] = start;
+    work[4 * w + 2] = (int32_t)(base + start);
+    work[4 * w + 3] = min(chunk, max(0, L - start));
   }
 }
 
@@ -216,7 +229,7 @@ static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timed_begin(FG_K_WORKLIST, st);
-  worklist_kernel<<<dim3(H), dim3(256), 0, st>>>(a.work_offset, a.chunk_rows, a.work, a.arrive);
+  worklist_kernel<<<dim3(H), dim3(256), 0, st>>>(a.work_offset, a.row_offset, a.len, a.chunk_rows, a.work);
   timed_end(st);
   return hipGetLastError();
 }

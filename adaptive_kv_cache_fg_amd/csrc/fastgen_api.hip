@@ -253,14 +253,17 @@ fg_status fg_compact_plan(const fg_shape* shape, const fg_params* params, const 
   return FG_OK;
 }
 
-static fg_status check_cache_views(const fg_cache* c) {
+static fg_status check_cache_views(const fg_cache* c, const fg_shape* shape) {
   if (!c) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
   if (!c->k || !c->v || !c->pos || !c->row_offset || !c->len || !c->capacity || !c->ring || !c->policy ||
-      !c->work_offset || !c->arrive || !c->error_word || (c->n_work > 0 && !c->work))
+      !c->work_offset || !c->error_word || (c->n_work > 0 && !c->work))
     return fail(FG_ERR_INVALID_ARG, "a cache buffer is NULL");
   if (!aligned16(c->k) || !aligned16(c->v)) return fail(FG_ERR_INVALID_ARG, "cache k and v must be 16-byte aligned");
-  if (c->total_rows < 0 || c->n_work < 0 || c->n_work > 0x7fffffff)
-    return fail(FG_ERR_INVALID_ARG, "bad total_rows or n_work");
+  if (c->total_rows < 0 || c->total_rows > 0x7fffffff || c->n_work < 0 || c->n_work > 0x7fffffff / 4)
+    return fail(FG_ERR_INVALID_ARG, "bad total_rows or n_work (both must fit 32-bit row and item indices)");
+  if (c->items_per_head < 1 || c->items_per_head > 0x7fffffff ||
+      (int64_t)shape->batch * shape->n_kv_heads * c->items_per_head < c->n_work)
+    return fail(FG_ERR_INVALID_ARG, "items_per_head must be the largest work-item count of a head");
   return FG_OK;
 }
 
@@ -270,7 +273,7 @@ fg_status fg_compact(const fg_shape* shape, const fg_params* params, const void*
   fg_status s = check_shape(shape);
   if (s != FG_OK) return s;
   if ((s = check_params(params)) != FG_OK) return s;
-  if ((s = check_cache_views(cache)) != FG_OK) return s;
+  if ((s = check_cache_views(cache, shape)) != FG_OK) return s;
   if (!K || !V || !token_class || !policy || !freq_mask) return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(K) || !aligned16(V)) return fail(FG_ERR_INVALID_ARG, "K and V must be 16-byte aligned");
   fg::GatherArgs a{};
@@ -294,7 +297,6 @@ fg_status fg_compact(const fg_shape* shape, const fg_params* params, const void*
   a.pos = cache->pos;
   a.len = cache->len;
   a.work = cache->work;
-  a.arrive = cache->arrive;
   a.error_word = cache->error_word;
   a.chunk_rows = fg::kDecodeChunk;
   hipError_t e = fg::launch_gather(a, stream);
@@ -309,15 +311,17 @@ fg_status fg_compact(const fg_shape* shape, const fg_params* params, const void*
 size_t fg_decode_workspace_size(const fg_cache* c) {
   if (!c || check_shape(&c->shape) != FG_OK) return 0;
   const int G = c->shape.n_q_heads / c->shape.n_kv_heads;
-  return align256((size_t)(c->n_work > 0 ? c->n_work : 1) * G * (c->shape.head_dim + 2) * sizeof(float));
+  const int64_t slots = (int64_t)c->shape.batch * c->shape.n_kv_heads * (c->items_per_head > 0 ? c->items_per_head : 1);
+  return align256((size_t)slots * G * (c->shape.head_dim + 2) * sizeof(float));
 }
 
 fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
                          const uint8_t* new_class, float* out, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
-  fg_status s = check_cache_views(cache);
+  if (!cache) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
+  fg_status s = check_shape(&cache->shape);
   if (s != FG_OK) return s;
-  if ((s = check_shape(&cache->shape)) != FG_OK) return s;
+  if ((s = check_cache_views(cache, &cache->shape)) != FG_OK) return s;
   if (!q || !k_new || !v_new || !out) return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(q)) return fail(FG_ERR_INVALID_ARG, "q must be 16-byte aligned");
   if (cache->next_pos < cache->n_prompt || cache->next_pos >= 0x7fffffff)
@@ -349,9 +353,9 @@ fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, cons
   a.policy = cache->policy;
   a.work_offset = cache->work_offset;
   a.work = cache->work;
-  a.arrive = cache->arrive;
   a.error_word = cache->error_word;
   a.chunk_rows = fg::kDecodeChunk;
+  a.items_per_head = (int)cache->items_per_head;
   hipError_t e = fg::launch_decode(a, stream);
   if (e != hipSuccess) return hip_fail(e, "decode step");
   cache->next_pos += 1;

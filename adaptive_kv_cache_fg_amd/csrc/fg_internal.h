@@ -92,7 +92,6 @@ struct GatherArgs {
   int32_t* pos;
   int32_t* len;
   int32_t* work;
-  int32_t* arrive;
   uint32_t* error_word;
   int chunk_rows;
 };
@@ -116,10 +115,10 @@ struct DecodeArgs {
   const int32_t* ring;
   const uint8_t* policy;
   const int64_t* work_offset;
-  const int32_t* work;
-  int32_t* arrive;
+  int32_t* work;     // [n_work * 4] (head, first row, first absolute row, rows in use)
   uint32_t* error_word;
   int chunk_rows;
+  int items_per_head;   // partial-state slots per head
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 

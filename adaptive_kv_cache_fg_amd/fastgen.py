@@ -39,8 +39,8 @@ class FgCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
                 ("row_offset", ctypes.c_void_p), ("len", ctypes.c_void_p), ("capacity", ctypes.c_void_p),
                 ("ring", ctypes.c_void_p), ("policy", ctypes.c_void_p), ("work_offset", ctypes.c_void_p),
-                ("work", ctypes.c_void_p), ("arrive", ctypes.c_void_p), ("error_word", ctypes.c_void_p),
-                ("total_rows", ctypes.c_int64), ("n_work", ctypes.c_int64),
+                ("work", ctypes.c_void_p), ("error_word", ctypes.c_void_p),
+                ("total_rows", ctypes.c_int64), ("n_work", ctypes.c_int64), ("items_per_head", ctypes.c_int64),
                 ("n_prompt", ctypes.c_int32), ("w_l", ctypes.c_int32), ("next_pos", ctypes.c_int32),
                 ("shape", FgShape)]
 
@@ -258,16 +258,16 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
     else:
         kept_count, ring, capacity = torch.empty(H, **i32), torch.empty(H, **i32), torch.empty(H, **i32)
         row_offset, work_offset = torch.empty(H + 1, **i64), torch.empty(H + 1, **i64)
-        totals = torch.empty(2, **i64)
+        totals = torch.empty(3, **i64)
     L = lib()
     _check(L.fg_compact_plan(ctypes.byref(shape), ctypes.byref(params), _ptr(token_class), _ptr(prof.policy),
                              _ptr(prof.freq_mask), int(max_new_tokens), int(max_new_kept), _ptr(kept_count),
                              _ptr(ring), _ptr(capacity), _ptr(row_offset), _ptr(work_offset), _ptr(totals),
                              _stream()), "fg_compact_plan")
-    total_rows, n_work = (int(x) for x in totals.cpu().tolist())     # the one host synchronisation
+    total_rows, n_work, per_head = (int(x) for x in totals.cpu().tolist())   # the one host synchronisation
     if reuse is not None:
         c = reuse.c
-        if total_rows > c.total_rows or n_work != c.n_work:
+        if total_rows > c.total_rows or n_work != c.n_work or per_head != c.items_per_head:
             raise ValueError("reuse: the new plan does not fit the cache's buffers")
         reuse.t["policy"].copy_(prof.policy.reshape(-1))
         _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),
@@ -279,14 +279,14 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
         "pos": torch.empty(max(total_rows, 1), **i32),
         "row_offset": row_offset, "len": torch.empty(H, **i32), "capacity": capacity, "ring": ring,
         "policy": prof.policy.reshape(-1).clone(), "work_offset": work_offset, "totals": totals,
-        "work": torch.empty(max(2 * n_work, 2), **i32), "arrive": torch.empty(H, **i32),
+        "work": torch.empty(max(4 * n_work, 4), **i32),
         "error_word": torch.empty(1, **i32),
     }
     c = FgCache()
     for name in ("k", "v", "pos", "row_offset", "len", "capacity", "ring", "policy", "work_offset", "work",
-                 "arrive", "error_word"):
+                 "error_word"):
         setattr(c, name, t[name].data_ptr())
-    c.total_rows, c.n_work = total_rows, n_work
+    c.total_rows, c.n_work, c.items_per_head = total_rows, n_work, per_head
     _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),
                         _ptr(t["policy"]), _ptr(prof.freq_mask), ctypes.byref(c), _stream()), "fg_compact")
     return Cache(shape, t, c, kept_count)

@@ -131,12 +131,14 @@ typedef struct {
   const int32_t* ring;     /* [B*Hkv] ring slots */
   const uint8_t* policy;   /* [B*Hkv] */
   const int64_t* work_offset; /* [B*Hkv + 1] decode work items per head (prefix) */
-  int32_t* work;           /* [n_work * 2] decode work items: (head, first row) */
-  int32_t* arrive;         /* [B*Hkv] per-head arrival counters of fg_decode_step;
-                              zeroed by fg_compact, left at zero by every step */
+  int32_t* work;           /* [n_work * 4] decode work items: (head, first row of the head,
+                              first absolute row, rows in use); fg_compact fills it and every
+                              fg_decode_step append keeps the rows-in-use count current */
   uint32_t* error_word;    /* [1] sticky device error bits: 1 = capacity overflow */
   int64_t total_rows;      /* [host] rows allocated */
   int64_t n_work;          /* [host] work items */
+  int64_t items_per_head;  /* [host] largest work-item count of a head (partial-state slots
+                              per head in the decode workspace) */
   int32_t n_prompt;        /* [host] n */
   int32_t w_l;             /* [host] local window */
   int32_t next_pos;        /* [host] position of the next generated token (starts at n) */
@@ -159,8 +161,9 @@ int32_t fg_decode_chunk_rows(void);
  * = ring + permanent prompt rows + (policy 4 ? max_new_tokens : max_new_kept);
  * row_offset [B*Hkv+1] and work_offset [B*Hkv+1] (exclusive prefix sums; a
  * head has max(1, ceil(capacity / fg_decode_chunk_rows())) work items);
- * totals [2] = {total rows, total work items}.  The caller reads totals to the
- * host (the one synchronisation of the path) to allocate the cache.
+ * totals [3] = {total rows, total work items, largest item count of a head}.
+ * The caller reads totals to the host (the one synchronisation of the path) to
+ * allocate the cache and set total_rows, n_work and items_per_head.
  */
 fg_status fg_compact_plan(const fg_shape* shape, const fg_params* params,
                           const uint8_t* token_class, const uint8_t* policy,
@@ -184,7 +187,8 @@ fg_status fg_compact(const fg_shape* shape, const fg_params* params,
 
 /* ------------------------------------------------------------------ decode */
 
-/* Workspace bytes for fg_decode_step: n_work * G * (d + 2) fp32 partials. */
+/* Workspace bytes for fg_decode_step: B*Hkv * items_per_head * G * (d + 2)
+ * fp32 partial states (one slot per work item, at a fixed stride per head). */
 size_t fg_decode_workspace_size(const fg_cache* cache);
 
 /*
@@ -201,9 +205,9 @@ size_t fg_decode_workspace_size(const fg_cache* cache);
  *   of position p + 1 - w_l is freed.
  * q [B,Hq,d], k_new / v_new [B,Hkv,d] (cache dtype); new_class [B] u8 or NULL
  * (all normal); out [B,Hq,d] fp32.  An append beyond capacity is skipped and
- * sets bit 1 of error_word.  Increments cache->next_pos.  One kernel launch:
- * every work item writes a partial softmax state, and the last item of a head
- * to arrive (per-head counter) merges them and updates that head's cache.
+ * sets bit 1 of error_word.  Increments cache->next_pos.  Two kernel launches:
+ * every work item writes a partial softmax state to its slot, then one
+ * workgroup per head merges the head's slots and updates that head's cache.
  * Steps on one cache must be issued in order on one stream.
  */
 fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, const void* v_new,

@@ -111,7 +111,7 @@ def test_decode_rejects_uncompacted_cache():
     c = fgb.FgCache()
     assert L.fg_decode_step(ctypes.byref(c), None, None, None, None, None, None, 0, None) == 1
     for name in ("k", "v", "pos", "row_offset", "len", "capacity", "ring", "policy", "work_offset", "work",
-                 "arrive", "error_word"):
+                 "error_word"):
         setattr(c, name, 0x1000)
     c.shape = fgb.FgShape(1, 4, 4, 16, 128, 0)
     c.n_prompt, c.next_pos = 16, 3          # next_pos before the prompt end
@@ -119,6 +119,8 @@ def test_decode_rejects_uncompacted_cache():
     assert L.fg_decode_step(ctypes.byref(c), p, p, p, None, p, p, 1 << 20, None) == 1
     c.next_pos = 16
     c.n_work = 10
+    assert L.fg_decode_step(ctypes.byref(c), p, p, p, None, p, p, 1 << 20, None) == 1   # no items_per_head
+    c.items_per_head = 3
     assert L.fg_decode_step(ctypes.byref(c), p, p, p, None, p, p, 16, None) == 3
 
 
