@@ -50,7 +50,8 @@ template <> struct Vec16<float> {
 // by the head's item count afterwards, so they do not wait for it).
 constexpr int kCombineThreads = 1024;
 
-template <typename T, int D, int G>
+// HAS_CLASS = false: new_class is NULL and every generated token is normal.
+template <typename T, int D, int G, bool HAS_CLASS>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const uint8_t* __restrict__ new_class, float* __restrict__ out, const float* __restrict__ part,
@@ -60,94 +61,94 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, int S, float c) {
   constexpr int NT = kCombineThreads;
   constexpr int GD = G * D;
-  constexpr int NGRP = GD >= NT ? 1 : NT / GD;     // thread groups splitting the item list
+  static_assert(NT % GD == 0, "one output per thread");
+  constexpr int NGRP = NT / GD;                    // thread groups splitting the item list
   constexpr int kBatch = 8;                        // items per thread whose loads are in flight together
+  constexpr int kWavesPerHead = D / kWave;         // waves reducing one query head's q . k_new
   __shared__ float cm[NGRP][GD], cs[NGRP][GD], ca[NGRP][GD];
-  __shared__ float s_self[G];
+  __shared__ float s_wave[NT / kWave];
   const int hd = blockIdx.x;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int o = tid % GD, grp = tid / GD;          // this thread's output (query head g, dim dd)
+  const int g = o / D, dd = o % D;
   const float* hpart = part + (size_t)hd * S * G * (D + 2);   // this head's slots
 
-  // ---- per-head scalars
+  // ---- every load up front, unconditional (straight-line code, so none waits on another)
   const int64_t w0 = work_offset[hd];
   const int n_items = (int)(work_offset[hd + 1] - w0);
-  const int b = hd / Hkv;
   const int pol = policy[hd];
-  const uint8_t cls = new_class ? new_class[b] : kNormal;
+  const uint8_t cls = HAS_CLASS ? new_class[hd / Hkv] : kNormal;
   const int R = ring[hd];
   const int64_t base_h = row_offset[hd];
   const int cap = capacity[hd];
   const int L = len[hd];
-  const T* kn = k_new + (size_t)hd * D;
-  const T* vn = v_new + (size_t)hd * D;
-  const float kv_self = tid < D ? to_f32(kn[tid]) : 0.f;   // cache write of the new row
-  const float vv_self = tid < D ? to_f32(vn[tid]) : 0.f;
-
-  // ---- the new token's score per query head: wave w reduces heads w, w + NT/64, ...
-  for (int g = wave; g < G; g += NT / kWave) {
-    const T* qg = q + ((size_t)hd * G + g) * D;
-    float s = 0.f;
+  const float qv = to_f32(q[(size_t)hd * GD + o]);
+  const float kv_self = to_f32(k_new[(size_t)hd * D + dd]);   // thread (g, dd) holds k_new[dd], v_new[dd]
+  const float vv_self = to_f32(v_new[(size_t)hd * D + dd]);
+  float mv[kBatch], lv[kBatch], av[kBatch];
 #pragma unroll
-    for (int t = lane; t < D; t += kWave) s = fmaf(to_f32(qg[t]), to_f32(kn[t]), s);
-    s = group_sum<kWave>(s);
-    if (lane == 0) s_self[g] = s * c;
+  for (int k = 0; k < kBatch; ++k) {
+    const float* pp = hpart + ((size_t)min(grp + k * NGRP, S - 1) * G + g) * (D + 2);
+    mv[k] = pp[0];
+    lv[k] = pp[1];
+    av[k] = pp[2 + dd];
   }
 
+  // ---- the new token's score per query head: lane sums, then the head's waves in LDS
+  // (every wave reduces; only the first GD / 64 entries, those of group 0, are read)
+  const float sw = group_sum<kWave>(qv * kv_self);
+  if (lane == 0) s_wave[wave] = sw;
   // ---- thread (output o, group grp) merges items grp, grp + NGRP, ... online
-  {
-    const int grp = tid / GD;
-    if (grp < NGRP) {
-      for (int o = tid % GD; o < GD; o += NT) {
-        const int g = o / D, dd = o % D;
-        float M = kNegBig, Ls = 0.f, As = 0.f;
-        for (int wb = grp; wb < S; wb += NGRP * kBatch) {
-          float mv[kBatch], lv[kBatch], av[kBatch];
+  float M = kNegBig, Ls = 0.f, As = 0.f;
+  for (int wb = grp;;) {
 #pragma unroll
-          for (int k = 0; k < kBatch; ++k) {
-            const float* pp = hpart + ((size_t)min(wb + k * NGRP, S - 1) * G + g) * (D + 2);
-            mv[k] = pp[0];
-            lv[k] = pp[1];
-            av[k] = pp[2 + dd];
-          }
+    for (int k = 0; k < kBatch; ++k) {
+      // slots past the head's items hold stale data; an empty item stored only (max, sum)
+      const bool live = wb + k * NGRP < n_items && lv[k] > 0.f;
+      const float mn = live ? fmaxf(M, mv[k]) : M;
+      const float s1 = fast_exp2(M - mn);
+      const float s2 = live ? fast_exp2(mv[k] - mn) : 0.f;
+      Ls = fmaf(Ls, s1, live ? lv[k] * s2 : 0.f);
+      As = fmaf(As, s1, live ? av[k] * s2 : 0.f);
+      M = mn;
+    }
+    wb += NGRP * kBatch;
+    if (wb >= n_items) break;                       // long lists: the next batch
 #pragma unroll
-          for (int k = 0; k < kBatch; ++k) {
-            // slots past the head's items hold stale data; an empty item stored only (max, sum)
-            const bool live = wb + k * NGRP < n_items && lv[k] > 0.f;
-            const float mn = live ? fmaxf(M, mv[k]) : M;
-            const float s1 = fast_exp2(M - mn);
-            const float s2 = live ? fast_exp2(mv[k] - mn) : 0.f;
-            Ls = fmaf(Ls, s1, live ? lv[k] * s2 : 0.f);
-            As = fmaf(As, s1, live ? av[k] * s2 : 0.f);
-            M = mn;
-          }
-        }
-        cm[grp][o] = M;
-        cs[grp][o] = Ls;
-        ca[grp][o] = As;
-      }
+    for (int k = 0; k < kBatch; ++k) {
+      const float* pp = hpart + ((size_t)min(wb + k * NGRP, S - 1) * G + g) * (D + 2);
+      mv[k] = pp[0];
+      lv[k] = pp[1];
+      av[k] = pp[2 + dd];
     }
   }
+  cm[grp][o] = M;
+  cs[grp][o] = Ls;
+  ca[grp][o] = As;
   const int lvl_self = cls == kSpecial ? 0 : (cls == kPunct ? 1 : (w_l >= 1 ? 3 : 4));
   const bool att_self = lvl_self <= pol;
   __syncthreads();
-  for (int o = tid; o < GD; o += NT) {
-    const int g = o / D, dd = o % D;
-    float M = att_self ? s_self[g] : kNegBig;
+  if (grp == 0) {
+    float s_self = 0.f;
 #pragma unroll
-    for (int r = 0; r < NGRP; ++r) M = fmaxf(M, cm[r][o]);
-    float Ls = 0.f, As = 0.f;
+    for (int w = 0; w < kWavesPerHead; ++w) s_self += s_wave[g * kWavesPerHead + w];
+    s_self *= c;
+    float Mx = att_self ? s_self : kNegBig;
+#pragma unroll
+    for (int r = 0; r < NGRP; ++r) Mx = fmaxf(Mx, cm[r][o]);
+    float Lt = 0.f, At = 0.f;
 #pragma unroll
     for (int r = 0; r < NGRP; ++r) {
-      const float a = fast_exp2(cm[r][o] - M);
-      Ls = fmaf(cs[r][o], a, Ls);
-      As = fmaf(ca[r][o], a, As);
+      const float a = fast_exp2(cm[r][o] - Mx);
+      Lt = fmaf(cs[r][o], a, Lt);
+      At = fmaf(ca[r][o], a, At);
     }
     if (att_self) {
-      const float a = fast_exp2(s_self[g] - M);
-      Ls += a;
-      As = fmaf(a, to_f32(vn[dd]), As);
+      const float a = fast_exp2(s_self - Mx);
+      Lt += a;
+      At = fmaf(a, vv_self, At);
     }
-    out[((size_t)hd * G + g) * D + dd] = Ls > 0.f ? As / Ls : 0.f;
+    out[(size_t)hd * GD + o] = Lt > 0.f ? At / Lt : 0.f;
   }
 
   // ---- cache update: afterwards the cache holds {j <= p : level(p + 1, j) <= policy}
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
   int64_t dst = -1;
   if (to_ring) dst = base_h + slot;
   else if (to_perm && L < cap) dst = base_h + L;
-  if (dst >= 0 && tid < D) {
+  if (dst >= 0 && tid < D) {                       // threads 0..D-1 hold element tid of the new row
     Kc[dst * D + tid] = T(kv_self);
     Vc[dst * D + tid] = T(vv_self);
   }
@@ -196,12 +197,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   const int item = blockIdx.x;
   const int4 wk = reinterpret_cast<const int4*>(work)[item];   // (head, first row, first absolute row, rows in use)
   const int hd = wk.x, k_item = wk.y / kDecodeChunk, abs0 = wk.z, n_use = wk.w;
-  if (k_item >= S) return;                                     // slot stride smaller than the head's items
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int sub = lane / LPR, sl_ = lane % LPR;
-  float* mypart = part + ((size_t)hd * S + k_item) * G * (D + 2);
+  float* mypart = part + ((size_t)hd * S + min(k_item, S - 1)) * G * (D + 2);
 
-  if (n_use > 0) {
+  // No branch between the item and the loads (a branch on loaded data would
+  // wait for it): lanes past the item's rows in use read q's first row and the
+  // item itself instead of a cache row (both always exist) and are masked, so
+  // an item with no rows in use stores the empty state (max -big, sum 0).
+  {
     // ---- every load of the chunk in flight at once
     float qv[G][E];
 #pragma unroll
@@ -213,10 +217,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int i = 0; i < NP; ++i) {
       const int row = wave * RPW + i * RPP + sub;
       in[i] = row < n_use;
-      const int64_t gr = abs0 + (in[i] ? row : 0);
-      kr[i] = *reinterpret_cast<const raw_t*>(Kc + gr * D + sl_ * E);
-      vr[i] = *reinterpret_cast<const raw_t*>(Vc + gr * D + sl_ * E);
-      pr[i] = pos[gr];
+      const int64_t gr = (int64_t)abs0 + row;
+      kr[i] = *reinterpret_cast<const raw_t*>((in[i] ? Kc + gr * D : q) + sl_ * E);
+      vr[i] = *reinterpret_cast<const raw_t*>((in[i] ? Vc + gr * D : q) + sl_ * E);
+      pr[i] = in[i] ? pos[gr] : work[0];
     }
     // ---- partial softmax state of this chunk
     float m[G], l[G], acc[G][E];
@@ -294,9 +298,6 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         mypart[(size_t)g * (D + 2) + 1] = ls;
       }
     }
-  } else if (tid < G) {                                  // nothing in use here: an empty state
-    mypart[(size_t)tid * (D + 2)] = kNegBig;
-    mypart[(size_t)tid * (D + 2) + 1] = 0.f;
   }
 
 }
@@ -308,15 +309,18 @@ static hipError_t launch_decode_tg(const DecodeArgs& a, hipStream_t st) {
   timed_begin(FG_K_DECODE, st);
   decode_step_kernel<T, D, G><<<dim3((unsigned)a.n_work), dim3(256), 0, st>>>(
       (const T*)a.q, a.part, a.work, (const T*)a.Kc, (const T*)a.Vc, a.pos, a.items_per_head, c);
+  timed_end(st);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) {
-    decode_combine_kernel<T, D, G><<<dim3(H), dim3(kCombineThreads), 0, st>>>(
+    timed_begin(FG_K_DECODE_MERGE, st);
+    auto kern = a.new_class ? decode_combine_kernel<T, D, G, true> : decode_combine_kernel<T, D, G, false>;
+    kern<<<dim3(H), dim3(kCombineThreads), 0, st>>>(
         (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work_offset, a.work,
         (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.error_word, a.Hkv, a.w_l,
         a.p, a.items_per_head, c);
+    timed_end(st);
     e = hipGetLastError();
   }
-  timed_end(st);
   return e;
 }
 

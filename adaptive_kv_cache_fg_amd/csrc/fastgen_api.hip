@@ -126,7 +126,7 @@ const char* fg_last_error(void) { return g_last_error.c_str(); }
 const char* fg_kernel_name(int32_t id) {
   static const char* names[FG_K_COUNT] = {"profile_rowstats", "profile_colsums", "profile_select",
                                           "compact_plan",     "compact_scan",    "compact_gather",
-                                          "compact_worklist", "decode_step"};
+                                          "compact_worklist", "decode_partials", "decode_merge"};
   return (id >= 0 && id < FG_K_COUNT) ? names[id] : "unknown";
 }
 
@@ -142,7 +142,7 @@ int32_t fg_kernel_timing_read(int32_t* ids, float* ms, int32_t max) {
     recs.swap(g_recs);
   }
   int32_t k = 0;
-  for (const TimingRec& r : recs) {
+  auto emit = [&](const TimingRec& r) {
     float t = -1.f;
     if (hipEventSynchronize(r.stop) == hipSuccess) (void)hipEventElapsedTime(&t, r.start, r.stop);
     if (k < max && ids && ms) {
@@ -150,7 +150,8 @@ int32_t fg_kernel_timing_read(int32_t* ids, float* ms, int32_t max) {
       ms[k] = t;
       ++k;
     }
-  }
+  };
+  for (const TimingRec& r : recs) emit(r);
   std::lock_guard<std::mutex> lk(g_tmu);
   for (const TimingRec& r : recs) {
     g_pool.push_back(r.start);
@@ -356,6 +357,7 @@ fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, cons
   a.error_word = cache->error_word;
   a.chunk_rows = fg::kDecodeChunk;
   a.items_per_head = (int)cache->items_per_head;
+  a.total_rows = cache->total_rows;
   hipError_t e = fg::launch_decode(a, stream);
   if (e != hipSuccess) return hip_fail(e, "decode step");
   cache->next_pos += 1;

@@ -119,6 +119,7 @@ struct DecodeArgs {
   uint32_t* error_word;
   int chunk_rows;
   int items_per_head;   // partial-state slots per head
+  int64_t total_rows;   // cache rows allocated
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 

@@ -23,7 +23,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
           4: "cache capacity exceeded", 5: "HIP error"}
 DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 KERNEL_NAMES = ["profile_rowstats", "profile_colsums", "profile_select", "compact_plan", "compact_scan",
-                "compact_gather", "compact_worklist", "decode_step"]
+                "compact_gather", "compact_worklist", "decode_partials", "decode_merge"]
 
 
 class FgShape(ctypes.Structure):
@@ -293,6 +293,7 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
 
 
 def timing_enable(on: bool = True) -> None:
+    """Bracket every eager launch with HIP events on its stream (not usable inside graph capture)."""
     lib().fg_kernel_timing_enable(1 if on else 0)
 
 

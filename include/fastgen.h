@@ -224,11 +224,12 @@ const char* fg_status_string(fg_status status);
 const char* fg_last_error(void);
 
 /* Kernel timing: when enabled, every launch is bracketed by HIP events on its
- * stream.  fg_kernel_timing_read synchronises those events and returns up to
- * max records (kernel id, milliseconds) accumulated since the last read. */
+ * stream (not for launches recorded into a HIP graph).  fg_kernel_timing_read
+ * synchronises those events and returns up to max records (kernel id,
+ * milliseconds) accumulated since the last read. */
 enum {
   FG_K_ROWSTATS = 0, FG_K_COLSUMS = 1, FG_K_SELECT = 2, FG_K_PLAN = 3, FG_K_SCAN = 4,
-  FG_K_GATHER = 5, FG_K_WORKLIST = 6, FG_K_DECODE = 7, FG_K_COUNT = 8
+  FG_K_GATHER = 5, FG_K_WORKLIST = 6, FG_K_DECODE = 7, FG_K_DECODE_MERGE = 8, FG_K_COUNT = 9
 };
 void fg_kernel_timing_enable(int enable);
 int32_t fg_kernel_timing_read(int32_t* kernel_ids, float* ms, int32_t max);

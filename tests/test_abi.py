@@ -128,5 +128,5 @@ def test_status_strings_and_kernel_names():
     L = fgb.lib()
     assert L.fg_status_string(0) == b"ok"
     assert L.fg_status_string(4) == b"cache capacity exceeded"
-    assert [L.fg_kernel_name(i).decode() for i in range(8)] == fgb.KERNEL_NAMES
+    assert [L.fg_kernel_name(i).decode() for i in range(9)] == fgb.KERNEL_NAMES
     assert L.fg_decode_chunk_rows() == 128
