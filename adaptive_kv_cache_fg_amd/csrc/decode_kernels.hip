@@ -43,11 +43,13 @@ template <> struct Vec16<float> {
   }
 };
 
-// Merge launch: one workgroup per head merges the head's partial states, the
-// new token, writes the output and updates the cache.  Every load is issued
-// before its first use: the per-head scalars, the new token's q . k_new and
-// K/V row, and the partial slots in batches of kBatch items per thread (masked
-// by the head's item count afterwards, so they do not wait for it).
+// Merge launch: one workgroup per query head merges its KV head's partial
+// states for that query head, adds the new token, writes the output; the
+// workgroup of the group's first query head also updates the KV head's cache.
+// Every load is issued before its first use: the per-head scalars, the new
+// token's q . k_new and K/V row, and the partial slots in batches of kBatch
+// items per thread (masked by the head's item count afterwards, so they do not
+// wait for it).
 constexpr int kCombineThreads = 1024;
 
 // HAS_CLASS = false: new_class is NULL and every generated token is normal.
@@ -58,20 +60,18 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     const int64_t* __restrict__ work_offset, int32_t* __restrict__ work, T* __restrict__ Kc, T* __restrict__ Vc,
     int32_t* __restrict__ pos, const int64_t* __restrict__ row_offset, int32_t* __restrict__ len,
     const int32_t* __restrict__ capacity, const int32_t* __restrict__ ring, const uint8_t* __restrict__ policy,
-    uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, int S, float c) {
+    uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, int S, int CH, float c) {
   constexpr int NT = kCombineThreads;
-  constexpr int GD = G * D;
-  static_assert(NT % GD == 0, "one output per thread");
-  constexpr int NGRP = NT / GD;                    // thread groups splitting the item list
+  static_assert(NT % D == 0, "one output per thread");
+  constexpr int NGRP = NT / D;                     // thread groups splitting the item list
   constexpr int kBatch = 8;                        // items per thread whose loads are in flight together
-  constexpr int kWavesPerHead = D / kWave;         // waves reducing one query head's q . k_new
-  __shared__ float cm[NGRP][GD], cs[NGRP][GD], ca[NGRP][GD];
+  constexpr int kWavesPerHead = D / kWave;         // waves reducing the query head's q . k_new
+  __shared__ float cm[NGRP][D], cs[NGRP][D], ca[NGRP][D];
   __shared__ float s_wave[NT / kWave];
-  const int hd = blockIdx.x;
+  const int qh = blockIdx.x, hd = qh / G, g = qh % G;   // query head, its KV head, its index in the group
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
-  const int o = tid % GD, grp = tid / GD;          // this thread's output (query head g, dim dd)
-  const int g = o / D, dd = o % D;
-  const float* hpart = part + (size_t)hd * S * G * (D + 2);   // this head's slots
+  const int dd = tid % D, grp = tid / D;           // this thread's output dimension and item group
+  const float* hpart = part + (size_t)hd * S * G * (D + 2) + (size_t)g * (D + 2);   // slot k at k * G * (D + 2)
 
   // ---- every load up front, unconditional (straight-line code, so none waits on another)
   const int64_t w0 = work_offset[hd];
@@ -82,23 +82,23 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
   const int64_t base_h = row_offset[hd];
   const int cap = capacity[hd];
   const int L = len[hd];
-  const float qv = to_f32(q[(size_t)hd * GD + o]);
-  const float kv_self = to_f32(k_new[(size_t)hd * D + dd]);   // thread (g, dd) holds k_new[dd], v_new[dd]
+  const float qv = to_f32(q[(size_t)qh * D + dd]);
+  const float kv_self = to_f32(k_new[(size_t)hd * D + dd]);   // thread dd holds k_new[dd], v_new[dd]
   const float vv_self = to_f32(v_new[(size_t)hd * D + dd]);
   float mv[kBatch], lv[kBatch], av[kBatch];
 #pragma unroll
   for (int k = 0; k < kBatch; ++k) {
-    const float* pp = hpart + ((size_t)min(grp + k * NGRP, S - 1) * G + g) * (D + 2);
+    const float* pp = hpart + (size_t)min(grp + k * NGRP, S - 1) * G * (D + 2);
     mv[k] = pp[0];
     lv[k] = pp[1];
     av[k] = pp[2 + dd];
   }
 
-  // ---- the new token's score per query head: lane sums, then the head's waves in LDS
-  // (every wave reduces; only the first GD / 64 entries, those of group 0, are read)
+  // ---- the new token's score: lane sums, then the D / 64 waves of one item group in LDS
+  // (every wave reduces; only group 0's entries are read)
   const float sw = group_sum<kWave>(qv * kv_self);
   if (lane == 0) s_wave[wave] = sw;
-  // ---- thread (output o, group grp) merges items grp, grp + NGRP, ... online
+  // ---- thread (dd, grp) merges items grp, grp + NGRP, ... online
   float M = kNegBig, Ls = 0.f, As = 0.f;
   for (int wb = grp;;) {
 #pragma unroll
@@ -116,40 +116,41 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     if (wb >= n_items) break;                       // long lists: the next batch
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const float* pp = hpart + ((size_t)min(wb + k * NGRP, S - 1) * G + g) * (D + 2);
+      const float* pp = hpart + (size_t)min(wb + k * NGRP, S - 1) * G * (D + 2);
       mv[k] = pp[0];
       lv[k] = pp[1];
       av[k] = pp[2 + dd];
     }
   }
-  cm[grp][o] = M;
-  cs[grp][o] = Ls;
-  ca[grp][o] = As;
+  cm[grp][dd] = M;
+  cs[grp][dd] = Ls;
+  ca[grp][dd] = As;
   const int lvl_self = cls == kSpecial ? 0 : (cls == kPunct ? 1 : (w_l >= 1 ? 3 : 4));
   const bool att_self = lvl_self <= pol;
   __syncthreads();
   if (grp == 0) {
     float s_self = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWavesPerHead; ++w) s_self += s_wave[g * kWavesPerHead + w];
+    for (int w = 0; w < kWavesPerHead; ++w) s_self += s_wave[w];
     s_self *= c;
     float Mx = att_self ? s_self : kNegBig;
 #pragma unroll
-    for (int r = 0; r < NGRP; ++r) Mx = fmaxf(Mx, cm[r][o]);
+    for (int r = 0; r < NGRP; ++r) Mx = fmaxf(Mx, cm[r][dd]);
     float Lt = 0.f, At = 0.f;
 #pragma unroll
     for (int r = 0; r < NGRP; ++r) {
-      const float a = fast_exp2(cm[r][o] - Mx);
-      Lt = fmaf(cs[r][o], a, Lt);
-      At = fmaf(ca[r][o], a, At);
+      const float a = fast_exp2(cm[r][dd] - Mx);
+      Lt = fmaf(cs[r][dd], a, Lt);
+      At = fmaf(ca[r][dd], a, At);
     }
     if (att_self) {
       const float a = fast_exp2(s_self - Mx);
       Lt += a;
       At = fmaf(a, vv_self, At);
     }
-    out[(size_t)hd * GD + o] = Lt > 0.f ? At / Lt : 0.f;
+    out[(size_t)qh * D + dd] = Lt > 0.f ? At / Lt : 0.f;
   }
+  if (g != 0) return;                              // one cache update per KV head
 
   // ---- cache update: afterwards the cache holds {j <= p : level(p + 1, j) <= policy}
   const bool to_ring = (cls == kNormal) && pol == 3 && w_l >= 2 && R > 0;
@@ -168,8 +169,8 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     if (to_perm) {
       if (dst >= 0) {
         len[hd] = L + 1;
-        const int64_t wi = w0 + L / kDecodeChunk;                 // the item that holds row L
-        work[4 * wi + 3] = L % kDecodeChunk + 1;
+        const int64_t wi = w0 + L / CH;                           // the item that holds row L
+        work[4 * wi + 3] = L % CH + 1;
       } else {
         atomicOr(error_word, 1u);
       }
@@ -180,62 +181,65 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const T* __restrict__ q, float* __restrict__ part, const int32_t* __restrict__ work,
-    const T* __restrict__ Kc, const T* __restrict__ Vc, const int32_t* __restrict__ pos, int S, float c) {
+    const T* __restrict__ Kc, const T* __restrict__ Vc, const int32_t* __restrict__ pos, int S, int CH,
+    float c) {
   using V16 = Vec16<T>;
   using raw_t = typename V16::raw_t;
   constexpr int E = V16::N;                 // elements per lane per row
   constexpr int LPR = D / E;                // lanes per row
   constexpr int RPP = kWave / LPR;          // rows per wave pass
   constexpr int kWaves = 4;
-  constexpr int RPW = kDecodeChunk / kWaves;   // rows per wave
-  constexpr int NP = RPW / RPP;             // passes per wave
+  constexpr int RPW = kDecodeSubRows / kWaves;   // rows per wave per sub-batch
+  constexpr int NP = RPW / RPP;             // passes per wave per sub-batch
   constexpr int GD = G * D;
-  static_assert(RPW % RPP == 0, "chunk must split evenly over the waves");
+  static_assert(RPW % RPP == 0, "sub-batch must split evenly over the waves");
   __shared__ float sm[kWaves][G], sl[kWaves][G];
   __shared__ float sacc[kWaves][G][D];
 
   const int item = blockIdx.x;
   const int4 wk = reinterpret_cast<const int4*>(work)[item];   // (head, first row, first absolute row, rows in use)
-  const int hd = wk.x, k_item = wk.y / kDecodeChunk, abs0 = wk.z, n_use = wk.w;
+  const int hd = wk.x, k_item = wk.y / CH, abs0 = wk.z, n_use = wk.w;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int sub = lane / LPR, sl_ = lane % LPR;
   float* mypart = part + ((size_t)hd * S + min(k_item, S - 1)) * G * (D + 2);
 
-  // No branch between the item and the loads (a branch on loaded data would
-  // wait for it): lanes past the item's rows in use read q's first row and the
-  // item itself instead of a cache row (both always exist) and are masked, so
-  // an item with no rows in use stores the empty state (max -big, sum 0).
-  {
-    // ---- every load of the chunk in flight at once
-    float qv[G][E];
+  float qv[G][E];
 #pragma unroll
-    for (int g = 0; g < G; ++g) V16::cvt(*reinterpret_cast<const raw_t*>(q + ((size_t)hd * G + g) * D + sl_ * E), qv[g]);
+  for (int g = 0; g < G; ++g) V16::cvt(*reinterpret_cast<const raw_t*>(q + ((size_t)hd * G + g) * D + sl_ * E), qv[g]);
+  float m[G], l[G], acc[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegBig;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+  }
+  // Sub-batches of kDecodeSubRows rows, all loads of one in flight at once.  The
+  // first has no branch between the item and its loads (a branch on loaded data
+  // would wait for it): lanes past the item's rows in use read q's first row
+  // and the item itself instead of a cache row (both always exist) and are
+  // masked, so an item with no rows in use stores the empty state (max -big,
+  // sum 0).
+  for (int r0 = 0;;) {
     raw_t kr[NP], vr[NP];
     int pr[NP];
     bool in[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int row = wave * RPW + i * RPP + sub;
+      const int row = r0 + wave * RPW + i * RPP + sub;
       in[i] = row < n_use;
       const int64_t gr = (int64_t)abs0 + row;
       kr[i] = *reinterpret_cast<const raw_t*>((in[i] ? Kc + gr * D : q) + sl_ * E);
       vr[i] = *reinterpret_cast<const raw_t*>((in[i] ? Vc + gr * D : q) + sl_ * E);
       pr[i] = in[i] ? pos[gr] : work[0];
     }
-    // ---- partial softmax state of this chunk
-    float m[G], l[G], acc[G][E];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m[g] = kNegBig;
-      l[g] = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
-    }
+    // scores of the sub-batch's rows first, then one rescale of the running
+    // state per query head and a plain weighted sum over the rows
+    float x[NP][G];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      float kv[E], vv[E];
+      float kv[E];
       V16::cvt(kr[i], kv);
-      V16::cvt(vr[i], vv);
       const bool valid = in[i] && pr[i] >= 0;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -243,17 +247,36 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) s = fmaf(qv[g][e], kv[e], s);
         s = group_sum<LPR>(s);
-        if (valid) {
-          const float x = s * c;
-          const float mn = fmaxf(m[g], x);
-          const float al = fast_exp2(m[g] - mn), pw = fast_exp2(x - mn);
-          l[g] = fmaf(l[g], al, pw);
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(acc[g][e], al, pw * vv[e]);
-          m[g] = mn;
-        }
+        x[i][g] = valid ? s * c : -INFINITY;
       }
     }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = m[g];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) mx = fmaxf(mx, x[i][g]);
+      const float al = fast_exp2(m[g] - mx);
+      l[g] *= al;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[g][e] *= al;
+      m[g] = mx;
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      float vv[E];
+      V16::cvt(vr[i], vv);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float pw = fast_exp2(x[i][g] - m[g]);   // 0 for masked rows
+        l[g] += pw;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pw, vv[e], acc[g][e]);
+      }
+    }
+    r0 += kDecodeSubRows;
+    if (r0 >= n_use) break;
+  }
+  {
     // merge the RPP row groups of the wave (lanes with equal sl_)
 #pragma unroll
     for (int o = LPR; o < kWave; o <<= 1) {
@@ -308,16 +331,16 @@ static hipError_t launch_decode_tg(const DecodeArgs& a, hipStream_t st) {
   const int H = a.B * a.Hkv;
   timed_begin(FG_K_DECODE, st);
   decode_step_kernel<T, D, G><<<dim3((unsigned)a.n_work), dim3(256), 0, st>>>(
-      (const T*)a.q, a.part, a.work, (const T*)a.Kc, (const T*)a.Vc, a.pos, a.items_per_head, c);
+      (const T*)a.q, a.part, a.work, (const T*)a.Kc, (const T*)a.Vc, a.pos, a.items_per_head, a.chunk_rows, c);
   timed_end(st);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) {
     timed_begin(FG_K_DECODE_MERGE, st);
     auto kern = a.new_class ? decode_combine_kernel<T, D, G, true> : decode_combine_kernel<T, D, G, false>;
-    kern<<<dim3(H), dim3(kCombineThreads), 0, st>>>(
+    kern<<<dim3(H * G), dim3(kCombineThreads), 0, st>>>(
         (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work_offset, a.work,
         (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.error_word, a.Hkv, a.w_l,
-        a.p, a.items_per_head, c);
+        a.p, a.items_per_head, a.chunk_rows, c);
     timed_end(st);
     e = hipGetLastError();
   }

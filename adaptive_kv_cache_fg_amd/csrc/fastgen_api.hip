@@ -216,7 +216,10 @@ fg_status fg_profile(const fg_shape* shape, const fg_params* params, const void*
   return FG_OK;
 }
 
-int32_t fg_decode_chunk_rows(void) { return fg::kDecodeChunk; }
+int32_t fg_decode_chunk_rows(const fg_shape* shape) {
+  if (check_shape(shape) != FG_OK) return 0;
+  return fg::decode_chunk_rows(shape->seq_len);
+}
 
 fg_status fg_compact_plan(const fg_shape* shape, const fg_params* params, const uint8_t* token_class,
                           const uint8_t* policy, const uint32_t* freq_mask, int32_t max_new_tokens,
@@ -248,7 +251,7 @@ fg_status fg_compact_plan(const fg_shape* shape, const fg_params* params, const 
   a.row_offset = row_offset;
   a.work_offset = work_offset;
   a.totals = totals;
-  a.chunk_rows = fg::kDecodeChunk;
+  a.chunk_rows = fg::decode_chunk_rows(shape->seq_len);
   hipError_t e = fg::launch_plan(a, stream);
   if (e != hipSuccess) return hip_fail(e, "compact plan");
   return FG_OK;
@@ -299,13 +302,14 @@ fg_status fg_compact(const fg_shape* shape, const fg_params* params, const void*
   a.len = cache->len;
   a.work = cache->work;
   a.error_word = cache->error_word;
-  a.chunk_rows = fg::kDecodeChunk;
+  a.chunk_rows = fg::decode_chunk_rows(shape->seq_len);
   hipError_t e = fg::launch_gather(a, stream);
   if (e != hipSuccess) return hip_fail(e, "compact gather");
   cache->shape = *shape;
   cache->n_prompt = shape->seq_len;
   cache->w_l = a.w_l;
   cache->next_pos = shape->seq_len;
+  cache->chunk_rows = a.chunk_rows;
   return FG_OK;
 }
 
@@ -327,6 +331,8 @@ fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, cons
   if (!aligned16(q)) return fail(FG_ERR_INVALID_ARG, "q must be 16-byte aligned");
   if (cache->next_pos < cache->n_prompt || cache->next_pos >= 0x7fffffff)
     return fail(FG_ERR_INVALID_ARG, "cache position out of range (was fg_compact called?)");
+  if (cache->chunk_rows != fg::decode_chunk_rows(cache->shape.seq_len))
+    return fail(FG_ERR_INVALID_ARG, "cache chunk_rows does not match its shape (was fg_compact called?)");
   if (!workspace || workspace_bytes < fg_decode_workspace_size(cache))
     return fail(FG_ERR_WORKSPACE, "decode workspace too small");
   fg::DecodeArgs a{};
@@ -355,7 +361,7 @@ fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, cons
   a.work_offset = cache->work_offset;
   a.work = cache->work;
   a.error_word = cache->error_word;
-  a.chunk_rows = fg::kDecodeChunk;
+  a.chunk_rows = cache->chunk_rows;
   a.items_per_head = (int)cache->items_per_head;
   a.total_rows = cache->total_rows;
   hipError_t e = fg::launch_decode(a, stream);

@@ -123,7 +123,14 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
-constexpr int kDecodeChunk = 128;  // cache rows per decode work item
+constexpr int kDecodeSubRows = 128;   // rows of a decode work item whose loads are issued together
+// Rows per decode work item: kDecodeSubRows doubled up to 2048 until a head of
+// n rows has at most 64 items (long heads: fewer partial states to merge).
+inline int decode_chunk_rows(int n) {
+  int c = kDecodeSubRows;
+  while (c < 2048 && (n + c - 1) / c > 64) c *= 2;
+  return c;
+}
 constexpr int kMaxGroup = 8;       // query heads per KV head supported by decode
 
 }  // namespace fg

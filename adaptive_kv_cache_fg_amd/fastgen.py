@@ -42,7 +42,7 @@ class FgCache(ctypes.Structure):
                 ("work", ctypes.c_void_p), ("error_word", ctypes.c_void_p),
                 ("total_rows", ctypes.c_int64), ("n_work", ctypes.c_int64), ("items_per_head", ctypes.c_int64),
                 ("n_prompt", ctypes.c_int32), ("w_l", ctypes.c_int32), ("next_pos", ctypes.c_int32),
-                ("shape", FgShape)]
+                ("chunk_rows", ctypes.c_int32), ("shape", FgShape)]
 
 
 class FastGenError(RuntimeError):
@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
     L.fg_cache_error.restype = ctypes.c_int
     L.fg_status_string.argtypes, L.fg_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     L.fg_last_error.argtypes, L.fg_last_error.restype = [], ctypes.c_char_p
-    L.fg_decode_chunk_rows.argtypes, L.fg_decode_chunk_rows.restype = [], I32
+    L.fg_decode_chunk_rows.argtypes, L.fg_decode_chunk_rows.restype = [sh], I32
     L.fg_kernel_timing_enable.argtypes, L.fg_kernel_timing_enable.restype = [ctypes.c_int], None
     L.fg_kernel_timing_read.argtypes = [ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_float), I32]
     L.fg_kernel_timing_read.restype = I32

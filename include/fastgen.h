@@ -142,11 +142,14 @@ typedef struct {
   int32_t n_prompt;        /* [host] n */
   int32_t w_l;             /* [host] local window */
   int32_t next_pos;        /* [host] position of the next generated token (starts at n) */
+  int32_t chunk_rows;      /* [host] cache rows per decode work item (set by fg_compact) */
   fg_shape shape;          /* [host] */
 } fg_cache;
 
-/* Rows of decode work per item (the split-K chunk of fg_decode_step). */
-int32_t fg_decode_chunk_rows(void);
+/* Rows of decode work per item (the split-K chunk of fg_decode_step) for a
+ * prompt shape: 128 rows, doubled up to 2048 until a head of seq_len rows has
+ * at most 64 items.  0 for an invalid shape. */
+int32_t fg_decode_chunk_rows(const fg_shape* shape);
 
 /*
  * fg_compact_plan -- size the head-specific caches (Method, second paragraph:
@@ -160,7 +163,7 @@ int32_t fg_decode_chunk_rows(void);
  * Outputs: kept_count [B*Hkv] prompt keys kept; ring [B*Hkv]; capacity [B*Hkv]
  * = ring + permanent prompt rows + (policy 4 ? max_new_tokens : max_new_kept);
  * row_offset [B*Hkv+1] and work_offset [B*Hkv+1] (exclusive prefix sums; a
- * head has max(1, ceil(capacity / fg_decode_chunk_rows())) work items);
+ * head has max(1, ceil(capacity / fg_decode_chunk_rows(shape))) work items);
  * totals [3] = {total rows, total work items, largest item count of a head}.
  * The caller reads totals to the host (the one synchronisation of the path) to
  * allocate the cache and set total_rows, n_work and items_per_head.

@@ -121,6 +121,8 @@ def test_decode_rejects_uncompacted_cache():
     c.n_work = 10
     assert L.fg_decode_step(ctypes.byref(c), p, p, p, None, p, p, 1 << 20, None) == 1   # no items_per_head
     c.items_per_head = 3
+    assert L.fg_decode_step(ctypes.byref(c), p, p, p, None, p, p, 1 << 20, None) == 1   # no chunk_rows
+    c.chunk_rows = 128
     assert L.fg_decode_step(ctypes.byref(c), p, p, p, None, p, p, 16, None) == 3
 
 
@@ -129,4 +131,7 @@ def test_status_strings_and_kernel_names():
     assert L.fg_status_string(0) == b"ok"
     assert L.fg_status_string(4) == b"cache capacity exceeded"
     assert [L.fg_kernel_name(i).decode() for i in range(9)] == fgb.KERNEL_NAMES
-    assert L.fg_decode_chunk_rows() == 128
+    def chunk(n):
+        return L.fg_decode_chunk_rows(ctypes.byref(fgb.FgShape(1, 4, 4, n, 128, 0)))
+    assert [chunk(n) for n in (1, 128, 8192, 8193, 32768, 1 << 20)] == [128, 128, 128, 256, 512, 2048]
+    assert L.fg_decode_chunk_rows(ctypes.byref(fgb.FgShape(1, 4, 4, 16, 96, 0))) == 0
