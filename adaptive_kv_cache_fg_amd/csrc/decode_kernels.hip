@@ -49,22 +49,22 @@ template <> struct Vec16<float> {
 // Every load is issued before its first use: the per-head scalars, the new
 // token's q . k_new and K/V row, and the partial slots in batches of kBatch
 // items per thread (masked by the head's item count afterwards, so they do not
-// wait for it).
-constexpr int kCombineThreads = 1024;
+// wait for it).  NT threads: 512 when one batch covers a head's items (a
+// smaller workgroup starts and drains sooner), else 1024.
+constexpr int kMergeBatch = 8;                     // items per thread whose loads are in flight together
 
 // HAS_CLASS = false: new_class is NULL and every generated token is normal.
-template <typename T, int D, int G, bool HAS_CLASS>
-__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
+template <typename T, int D, int G, bool HAS_CLASS, int NT>
+__global__ __launch_bounds__(NT) void decode_merge_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const uint8_t* __restrict__ new_class, float* __restrict__ out, const float* __restrict__ part,
     const int64_t* __restrict__ work_offset, int32_t* __restrict__ work, T* __restrict__ Kc, T* __restrict__ Vc,
     int32_t* __restrict__ pos, const int64_t* __restrict__ row_offset, int32_t* __restrict__ len,
     const int32_t* __restrict__ capacity, const int32_t* __restrict__ ring, const uint8_t* __restrict__ policy,
     uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, int S, int CH, float c) {
-  constexpr int NT = kCombineThreads;
   static_assert(NT % D == 0, "one output per thread");
   constexpr int NGRP = NT / D;                     // thread groups splitting the item list
-  constexpr int kBatch = 8;                        // items per thread whose loads are in flight together
+  constexpr int kBatch = kMergeBatch;
   constexpr int kWavesPerHead = D / kWave;         // waves reducing the query head's q . k_new
   __shared__ float cm[NGRP][D], cs[NGRP][D], ca[NGRP][D];
   __shared__ float s_wave[NT / kWave];
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+__global__ __launch_bounds__(256) void decode_partials_kernel(
     const T* __restrict__ q, float* __restrict__ part, const int32_t* __restrict__ work,
     const T* __restrict__ Kc, const T* __restrict__ Vc, const int32_t* __restrict__ pos, int S, int CH,
     float c) {
@@ -330,14 +330,16 @@ static hipError_t launch_decode_tg(const DecodeArgs& a, hipStream_t st) {
   const float c = kLog2e / sqrtf((float)D);
   const int H = a.B * a.Hkv;
   timed_begin(FG_K_DECODE, st);
-  decode_step_kernel<T, D, G><<<dim3((unsigned)a.n_work), dim3(256), 0, st>>>(
+  decode_partials_kernel<T, D, G><<<dim3((unsigned)a.n_work), dim3(256), 0, st>>>(
       (const T*)a.q, a.part, a.work, (const T*)a.Kc, (const T*)a.Vc, a.pos, a.items_per_head, a.chunk_rows, c);
   timed_end(st);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess) {
+  if (e == hipSuccess && !a.partials_only) {
     timed_begin(FG_K_DECODE_MERGE, st);
-    auto kern = a.new_class ? decode_combine_kernel<T, D, G, true> : decode_combine_kernel<T, D, G, false>;
-    kern<<<dim3(H * G), dim3(kCombineThreads), 0, st>>>(
+    const bool small = a.items_per_head <= (512 / D) * kMergeBatch;
+    auto kern = a.new_class ? (small ? decode_merge_kernel<T, D, G, true, 512> : decode_merge_kernel<T, D, G, true, 1024>)
+                            : (small ? decode_merge_kernel<T, D, G, false, 512> : decode_merge_kernel<T, D, G, false, 1024>);
+    kern<<<dim3(H * G), dim3(small ? 512 : 1024), 0, st>>>(
         (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work_offset, a.work,
         (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.error_word, a.Hkv, a.w_l,
         a.p, a.items_per_head, a.chunk_rows, c);

@@ -79,7 +79,8 @@ hipEvent_t take_event() {
     return e;
   }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  // timing only: no system-scope fence (cache write-back) when the event is recorded
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -320,14 +321,16 @@ size_t fg_decode_workspace_size(const fg_cache* c) {
   return align256((size_t)slots * G * (c->shape.head_dim + 2) * sizeof(float));
 }
 
-fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
-                         const uint8_t* new_class, float* out, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+// Shared by fg_decode_step and fg_decode_partials (partials_only: no merge
+// launch, the cache and next_pos are left unchanged, k_new / v_new / out unused).
+static fg_status decode_launch(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
+                               const uint8_t* new_class, float* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, bool partials_only) {
   if (!cache) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
   fg_status s = check_shape(&cache->shape);
   if (s != FG_OK) return s;
   if ((s = check_cache_views(cache, &cache->shape)) != FG_OK) return s;
-  if (!q || !k_new || !v_new || !out) return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!q || (!partials_only && (!k_new || !v_new || !out))) return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(q)) return fail(FG_ERR_INVALID_ARG, "q must be 16-byte aligned");
   if (cache->next_pos < cache->n_prompt || cache->next_pos >= 0x7fffffff)
     return fail(FG_ERR_INVALID_ARG, "cache position out of range (was fg_compact called?)");
@@ -364,10 +367,24 @@ fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, cons
   a.chunk_rows = cache->chunk_rows;
   a.items_per_head = (int)cache->items_per_head;
   a.total_rows = cache->total_rows;
+  a.partials_only = partials_only;
   hipError_t e = fg::launch_decode(a, stream);
   if (e != hipSuccess) return hip_fail(e, "decode step");
-  cache->next_pos += 1;
+  if (!partials_only) cache->next_pos += 1;
   return FG_OK;
+}
+
+fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
+                         const uint8_t* new_class, float* out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  return decode_launch(cache, q, k_new, v_new, new_class, out, workspace, workspace_bytes, stream, false);
+}
+
+fg_status fg_decode_partials(const fg_cache* cache, const void* q, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (!cache) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
+  fg_cache c = *cache;                                  // next_pos is not advanced
+  return decode_launch(&c, q, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, true);
 }
 
 fg_status fg_cache_error(const fg_cache* cache, uint32_t* bits_out, hipStream_t stream) {

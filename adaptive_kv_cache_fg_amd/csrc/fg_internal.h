@@ -120,6 +120,7 @@ struct DecodeArgs {
   int chunk_rows;
   int items_per_head;   // partial-state slots per head
   int64_t total_rows;   // cache rows allocated
+  bool partials_only;   // skip the merge launch (the cache is left unchanged)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 

@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
     L.fg_decode_workspace_size.argtypes, L.fg_decode_workspace_size.restype = [ca], S
     L.fg_decode_step.argtypes = [ca, P, P, P, P, P, P, S, P]
     L.fg_decode_step.restype = ctypes.c_int
+    L.fg_decode_partials.argtypes, L.fg_decode_partials.restype = [ca, P, P, S, P], ctypes.c_int
     L.fg_cache_error.argtypes = [ca, ctypes.POINTER(ctypes.c_uint32), P]
     L.fg_cache_error.restype = ctypes.c_int
     L.fg_status_string.argtypes, L.fg_status_string.restype = [ctypes.c_int], ctypes.c_char_p
@@ -198,12 +199,25 @@ class Cache:
         if out is None:
             out = torch.empty((s.batch, s.n_q_heads, s.head_dim), dtype=torch.float32, device=q.device)
         L = lib()
-        if self._ws is None:
-            nb = L.fg_decode_workspace_size(ctypes.byref(self.c))
-            self._ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+        self._workspace(q.device)
         _check(L.fg_decode_step(ctypes.byref(self.c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(new_class),
                                 _ptr(out), _ptr(self._ws), self._ws.numel(), _stream()), "fg_decode_step")
         return out
+
+    def decode_partials(self, q: torch.Tensor) -> None:
+        """fg_decode_partials: only the split-K launch of the next step (cache and next_pos unchanged)."""
+        s = self.shape
+        _need(q, "q", self.t["k"].dtype)
+        if q.shape != (s.batch, s.n_q_heads, s.head_dim):
+            raise ValueError("decode input shapes do not match the cache")
+        self._workspace(q.device)
+        _check(lib().fg_decode_partials(ctypes.byref(self.c), _ptr(q), _ptr(self._ws), self._ws.numel(), _stream()),
+               "fg_decode_partials")
+
+    def _workspace(self, device) -> None:
+        if self._ws is None:
+            nb = lib().fg_decode_workspace_size(ctypes.byref(self.c))
+            self._ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
 
     def kept_positions(self) -> List[np.ndarray]:
         """Sorted kept-index list of every (b, KV head), from the device cache (synchronises)."""

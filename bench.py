@@ -222,11 +222,26 @@ def main() -> int:
     wall = time.perf_counter() - t0
     fg.timing_enable(False)
     recs = fg.timing_read()
+    partials_us = None
     if graph is not None:
-        # launches inside the graph carry no events: time the decode kernels on one eager pass of
-        # the same steps from the same cache state (these events bracket only the library launches)
+        # launches inside the graph carry no per-launch events.  The split-K launch alone
+        # (fg_decode_partials: read-only on the cache) for the same 256 steps from the same cache
+        # state, as a graph timed by events around its replay; the merge launch on one eager pass
+        # with the library's events around each launch.
         prompt_phase(reuse=cache)
         torch.cuda.synchronize()
+        pgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pgraph):
+            for t in range(steps_dec):
+                cache.decode_partials(qs[t])
+        pgraph.replay()
+        pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        pe[0].record()
+        pgraph.replay()
+        pe[1].record()
+        torch.cuda.synchronize()
+        partials_us = 1e3 * pe[0].elapsed_time(pe[1]) / steps_dec
+        del pgraph
         fg.timing_read()
         fg.timing_enable(True)
         decode_eager(cache)
@@ -249,7 +264,17 @@ def main() -> int:
     for k, v in per.items():
         reps = args.steps if not (graph is not None and k.startswith("decode")) else 1
         kstats[k] = {"launches_per_step": len(v) / reps, "avg_us": 1e3 * float(np.mean(v)),
-                     "total_us_per_step": 1e3 * float(np.sum(v)) / reps}
+                     "total_us_per_step": 1e3 * float(np.sum(v)) / reps, "timing": "events around each launch"}
+    if partials_us is not None:
+        kstats["decode_partials"].update(
+            avg_us=partials_us, total_us_per_step=partials_us * steps_dec,
+            timing=f"events around a graph of {steps_dec} fg_decode_partials launches (per-launch events "
+                   f"in an eager pass: {kstats['decode_partials']['avg_us']:.2f} us)")
+        merge_us = 1e3 * decode_ms / steps_dec - partials_us
+        kstats["decode_merge"].update(
+            avg_us=merge_us, total_us_per_step=merge_us * steps_dec,
+            timing=f"graph decode step minus the graph-timed partials launch (per-launch events in an "
+                   f"eager pass: {kstats['decode_merge']['avg_us']:.2f} us)")
 
     # algorithmic work per launch
     prof, cache = last

@@ -217,6 +217,14 @@ fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, cons
                          const uint8_t* new_class, float* out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* fg_decode_partials -- only the first (split-K) launch of fg_decode_step for
+ * the next position: reads the cache and q [B,Hq,d] and writes the partial
+ * states into workspace; the cache, its next_pos and any output are left
+ * unchanged, so calls may repeat (e.g. to time that launch alone).  Errors as
+ * fg_decode_step. */
+fg_status fg_decode_partials(const fg_cache* cache, const void* q, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* Synchronises the stream and reads error_word: FG_OK, or FG_ERR_CAPACITY
  * when an append was dropped.  *bits_out [host] receives the raw bits if not NULL. */
 fg_status fg_cache_error(const fg_cache* cache, uint32_t* bits_out, hipStream_t stream);

@@ -59,3 +59,31 @@ def test_decode_graph_replay_matches_eager(hq, hkv):
         assert torch.equal(outs, eager), rep
         kept = cache.kept_positions()
         assert all(np.array_equal(a, b) for a, b in zip(kept, eager_kept)), rep
+
+
+def test_decode_partials_leaves_the_cache_unchanged():
+    """fg_decode_partials (the split-K launch alone) neither changes the cache nor next_pos, and
+    the following steps give the same outputs as a cache that never ran it."""
+    spec = syn.custom_spec(syn.CONFIGS[1], seq_len=300, n_q_heads=4, n_kv_heads=2, mix="fixed",
+                           fixed_types=("punct", "local"), batch=1)
+    steps = 6
+    print(f"[partials] n={spec.seq_len} steps={steps}", flush=True)
+    li = syn.make_layer(spec, 0)
+    ds = syn.make_decode_stream(spec, 0, steps)
+    Q, K, V = (_upload(x, spec.dtype) for x in (li.Q, li.K, li.V))
+    cls = torch.from_numpy(li.token_class).cuda()
+    qs, ks, vs = (_upload(x, spec.dtype) for x in (ds.q, ds.k, ds.v))
+    ncs = torch.from_numpy(ds.new_class).cuda()
+    prof = fg.profile(Q, K, cls, spec.r_l, spec.r_f, spec.T[0])
+    ref = fg.compact(K, V, cls, prof, 4, max_new_tokens=steps)
+    ref_out = [ref.decode_step(qs[t], ks[t], vs[t], ncs[t]).clone() for t in range(steps)]
+    cache = fg.compact(K, V, cls, prof, 4, max_new_tokens=steps)
+    kept0, pos0 = cache.kept_positions(), cache.next_pos
+    for t in range(steps):
+        cache.decode_partials(qs[t])
+    torch.cuda.synchronize()
+    assert cache.next_pos == pos0
+    assert all(np.array_equal(a, b) for a, b in zip(cache.kept_positions(), kept0))
+    for t in range(steps):
+        cache.decode_partials(qs[t])                  # repeated: still no effect
+        assert torch.equal(cache.decode_step(qs[t], ks[t], vs[t], ncs[t]), ref_out[t]), t
