@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, co
                                                      const int64_t* __restrict__ row_offset, const int32_t* __restrict__ ring,
                                                      int Hkv, int n, int nch, T* __restrict__ Kc, T* __restrict__ Vc,
                                                      int32_t* __restrict__ pos, int32_t* __restrict__ len,
-                                                     uint32_t* __restrict__ error_word) {
+                                                     uint32_t* __restrict__ error_word, int64_t total_rows) {
   constexpr int kCPR = D * (int)sizeof(T) / 16;           // 16-byte chunks per row
   __shared__ int red[4];
   __shared__ int wcnt[4], wrows[4];
@@ -130,6 +130,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, co
   const int64_t off = row_offset[hd];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (blockIdx.x == 0 && tid == 0) *error_word = 0u;
+  if (row_offset[hd + 1] > total_rows) {                  // the plan does not fit the cache: head left empty
+    if (ch == nch - 1 && tid == 0) len[hd] = 0;           // (the work list records the error)
+    return;
+  }
 
   // permanent keys at positions before this chunk
   int before = 0;
@@ -183,23 +187,39 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, co
   }
 }
 
-// Decode work items of one head: 128-row chunks of its capacity, each
-// (head, first row, first absolute row, rows in use).  The rows-in-use count of
-// an item is kept current by the decode step's appends.
+// Decode work items of one head: chunks of its capacity, each (head, first
+// row, first absolute row, rows in use).  The rows-in-use count of an item is
+// kept current by the decode step's appends.  The cache's buffers are
+// capacities (n_work_cap items, S_cap items per head, total_rows rows): a plan
+// that exceeds them sets bit 2 of error_word, and what does not fit becomes
+// empty items (head -1), as do the items past the plan's total, so a decode
+// grid of n_work_cap items stays valid.
 __global__ __launch_bounds__(256) void worklist_kernel(const int64_t* __restrict__ work_offset,
                                                        const int64_t* __restrict__ row_offset,
                                                        const int32_t* __restrict__ len, int chunk,
-                                                       int32_t* __restrict__ work) {
-  const int hd = blockIdx.x;
+                                                       int32_t* __restrict__ work, int64_t n_work_cap, int S_cap,
+                                                       int64_t total_rows, uint32_t* __restrict__ error_word) {
+  const int hd = blockIdx.x, H = gridDim.x;
   const int64_t w0 = work_offset[hd], w1 = work_offset[hd + 1];
   const int64_t base = row_offset[hd];
+  const bool fits = row_offset[hd + 1] <= total_rows && w1 <= n_work_cap && w1 - w0 <= S_cap;
+  if (threadIdx.x == 0 && !fits) atomicOr(error_word, 2u);
   const int L = len[hd];
-  for (int64_t w = w0 + threadIdx.x; w < w1; w += blockDim.x) {
+  for (int64_t w = w0 + threadIdx.x; w < min(w1, n_work_cap); w += blockDim.x) {
     const int start = (int)((w - w0) * chunk);
-    work[4 * w] = hd;
-    work[4 * w + 1] = start;
-    work[4 * w + 2] = (int32_t)(base + start);
-    work[4 * w + 3] = min(chunk, max(0, L - start));
+    const bool real = fits;
+    work[4 * w] = real ? hd : -1;
+    work[4 * w + 1] = real ? start : 0;
+    work[4 * w + 2] = real ? (int32_t)(base + start) : 0;
+    work[4 * w + 3] = real ? min(chunk, max(0, L - start)) : 0;
+  }
+  if (hd == 0) {                                           // items past the plan's total
+    for (int64_t w = work_offset[H] + threadIdx.x; w < n_work_cap; w += blockDim.x) {
+      work[4 * w] = -1;
+      work[4 * w + 1] = 0;
+      work[4 * w + 2] = 0;
+      work[4 * w + 3] = 0;
+    }
   }
 }
 
@@ -224,12 +244,13 @@ static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st) {
   timed_begin(FG_K_GATHER, st);
   gather_kernel<T, D><<<dim3(H * nch), dim3(256), 0, st>>>(
       (const T*)a.K, (const T*)a.V, a.cls, a.policy, a.fmask, a.row_offset, a.ring, a.Hkv, a.n, nch, (T*)a.Kc,
-      (T*)a.Vc, a.pos, a.len, a.error_word);
+      (T*)a.Vc, a.pos, a.len, a.error_word, a.total_rows);
   timed_end(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timed_begin(FG_K_WORKLIST, st);
-  worklist_kernel<<<dim3(H), dim3(256), 0, st>>>(a.work_offset, a.row_offset, a.len, a.chunk_rows, a.work);
+  worklist_kernel<<<dim3(H), dim3(256), 0, st>>>(a.work_offset, a.row_offset, a.len, a.chunk_rows, a.work, a.n_work,
+                                                 a.items_per_head, a.total_rows, a.error_word);
   timed_end(st);
   return hipGetLastError();
 }

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     const int64_t* __restrict__ work_offset, int32_t* __restrict__ work, T* __restrict__ Kc, T* __restrict__ Vc,
     int32_t* __restrict__ pos, const int64_t* __restrict__ row_offset, int32_t* __restrict__ len,
     const int32_t* __restrict__ capacity, const int32_t* __restrict__ ring, const uint8_t* __restrict__ policy,
-    uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, int S, int CH, float c) {
+    uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, int S, int CH, int64_t total_rows, float c) {
   static_assert(NT % D == 0, "one output per thread");
   constexpr int NGRP = NT / D;                     // thread groups splitting the item list
   constexpr int kBatch = kMergeBatch;
@@ -75,11 +75,12 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
 
   // ---- every load up front, unconditional (straight-line code, so none waits on another)
   const int64_t w0 = work_offset[hd];
-  const int n_items = (int)(work_offset[hd + 1] - w0);
+  const int n_items = (int)min<int64_t>(work_offset[hd + 1] - w0, S);   // more only if the plan did not fit
   const int pol = policy[hd];
   const uint8_t cls = HAS_CLASS ? new_class[hd / Hkv] : kNormal;
   const int R = ring[hd];
   const int64_t base_h = row_offset[hd];
+  const bool fits = row_offset[hd + 1] <= total_rows;   // else the plan did not fit: no update
   const int cap = capacity[hd];
   const int L = len[hd];
   const float qv = to_f32(q[(size_t)qh * D + dd]);
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     }
     out[(size_t)qh * D + dd] = Lt > 0.f ? At / Lt : 0.f;
   }
-  if (g != 0) return;                              // one cache update per KV head
+  if (g != 0 || !fits) return;                    // one cache update per KV head
 
   // ---- cache update: afterwards the cache holds {j <= p : level(p + 1, j) <= policy}
   const bool to_ring = (cls == kNormal) && pol == 3 && w_l >= 2 && R > 0;
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(
 
   const int item = blockIdx.x;
   const int4 wk = reinterpret_cast<const int4*>(work)[item];   // (head, first row, first absolute row, rows in use)
-  const int hd = wk.x, k_item = wk.y / CH, abs0 = wk.z, n_use = wk.w;
+  const int hd = max(wk.x, 0), k_item = wk.y / CH, abs0 = wk.z, n_use = wk.w;   // head -1: an empty item
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int sub = lane / LPR, sl_ = lane % LPR;
   float* mypart = part + ((size_t)hd * S + min(k_item, S - 1)) * G * (D + 2);
@@ -303,6 +304,7 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(
       }
     }
     __syncthreads();
+    if (wk.x < 0) return;                              // an empty item (past the plan's total): no slot
     for (int t = tid; t < GD; t += blockDim.x) {        // merge the 4 waves
       const int g = t / D, dd = t % D;
       float mx = sm[0][g];
@@ -342,7 +344,7 @@ static hipError_t launch_decode_tg(const DecodeArgs& a, hipStream_t st) {
     kern<<<dim3(H * G), dim3(small ? 512 : 1024), 0, st>>>(
         (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work_offset, a.work,
         (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.error_word, a.Hkv, a.w_l,
-        a.p, a.items_per_head, a.chunk_rows, c);
+        a.p, a.items_per_head, a.chunk_rows, a.total_rows, c);
     timed_end(st);
     e = hipGetLastError();
   }

@@ -304,6 +304,9 @@ fg_status fg_compact(const fg_shape* shape, const fg_params* params, const void*
   a.work = cache->work;
   a.error_word = cache->error_word;
   a.chunk_rows = fg::decode_chunk_rows(shape->seq_len);
+  a.total_rows = cache->total_rows;
+  a.n_work = cache->n_work;
+  a.items_per_head = (int)cache->items_per_head;
   hipError_t e = fg::launch_gather(a, stream);
   if (e != hipSuccess) return hip_fail(e, "compact gather");
   cache->shape = *shape;

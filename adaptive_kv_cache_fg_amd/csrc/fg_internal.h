@@ -94,6 +94,8 @@ struct GatherArgs {
   int32_t* work;
   uint32_t* error_word;
   int chunk_rows;
+  int64_t total_rows, n_work;   // the cache's capacities
+  int items_per_head;
 };
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
 

@@ -245,11 +245,14 @@ class Cache:
 
 
 def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: Profile, n_q_heads: int,
-            max_new_tokens: int, max_new_kept: Optional[int] = None, reuse: Optional[Cache] = None) -> Cache:
+            max_new_tokens: int, max_new_kept: Optional[int] = None, reuse: Optional[Cache] = None,
+            check: bool = True) -> Cache:
     """fg_compact_plan + one read of the totals + fg_compact: the ragged cache of one layer.
 
-    With ``reuse``, the plan must fit that cache's buffers, which are refilled in place
-    (same device addresses, so a captured decode graph stays valid).
+    With ``reuse``, that cache's buffers are refilled in place (same device addresses, so a
+    captured decode graph stays valid).  ``check=False`` (reuse only) skips the read of the new
+    totals, so nothing synchronises the host and the call can be captured in a graph; a plan
+    that does not fit the buffers then shows up as bit 2 of ``error_bits()``.
     """
     _need(K, "K")
     _need(V, "V", K.dtype)
@@ -278,10 +281,16 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
                              _ptr(prof.freq_mask), int(max_new_tokens), int(max_new_kept), _ptr(kept_count),
                              _ptr(ring), _ptr(capacity), _ptr(row_offset), _ptr(work_offset), _ptr(totals),
                              _stream()), "fg_compact_plan")
+    if reuse is not None and not check:
+        reuse.t["policy"].copy_(prof.policy.reshape(-1))
+        _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),
+                            _ptr(reuse.t["policy"]), _ptr(prof.freq_mask), ctypes.byref(reuse.c), _stream()),
+               "fg_compact")
+        return reuse
     total_rows, n_work, per_head = (int(x) for x in totals.cpu().tolist())   # the one host synchronisation
     if reuse is not None:
         c = reuse.c
-        if total_rows > c.total_rows or n_work != c.n_work or per_head != c.items_per_head:
+        if total_rows > c.total_rows or n_work > c.n_work or per_head > c.items_per_head:
             raise ValueError("reuse: the new plan does not fit the cache's buffers")
         reuse.t["policy"].copy_(prof.policy.reshape(-1))
         _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),

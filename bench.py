@@ -8,12 +8,18 @@ One step = the whole path over one synthetic Llama-1-7B attention layer
   256 x fg_decode_step over that cache (split-K partials + combine/append/evict).
 Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 
+The prompt phase (profile, then a compaction that refills the cache's buffers
+without a host read of the totals) and the 256-step decode loop are each
+captured once as a HIP graph and replayed (``--mode eager`` launches every call
+from Python instead).
+
 Prints ONE JSON line.  ``value`` is profile+compact prompt tokens/s; decode
-tokens/s, per-kernel durations (the library's HIP events on the launch stream:
-prompt kernels over the timed steps; the decode loop is timed as a graph
-replay, and its two kernels on one eager pass of the same steps right after),
-the roofline of the dominant kernel and the CPU oracle timed on the host cores
-are reported beside it.
+tokens/s, per-kernel durations, the roofline of the dominant kernel and the CPU
+oracle timed on the host cores are reported beside it.  Per-kernel durations
+are HIP events on the launch stream: the prompt kernels and the decode merge
+launch on one eager pass each (events around every launch), the decode
+split-K launch as a graph of 256 fg_decode_partials launches (events around the
+replay).
 """
 from __future__ import annotations
 
@@ -132,8 +138,9 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=1, help="workload id (1 = Llama-1-7B layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=16)
-    ap.add_argument("--decode-mode", choices=["graph", "eager"], default="graph",
-                    help="graph: the decode loop captured once as a HIP graph and replayed")
+    ap.add_argument("--mode", "--decode-mode", dest="mode", choices=["graph", "eager"], default="graph",
+                    help="graph: the prompt phase and the decode loop each captured once as a HIP graph "
+                         "and replayed; eager: every call launched from Python")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -163,10 +170,10 @@ def main() -> int:
     T = spec.T[0]
     B, Hq, n, d = li.Q.shape
 
-    def prompt_phase(reuse=None):
+    def prompt_phase(reuse=None, check=True):
         prof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T)
         cache = fg.compact(Kd, Vd, cls, prof, Hq, max_new_tokens=steps_dec, max_new_kept=max_new_kept,
-                           reuse=reuse)
+                           reuse=reuse, check=check)
         return prof, cache
 
     def decode_eager(cache):
@@ -176,10 +183,16 @@ def main() -> int:
     # one eager pass allocates the cache and the decode workspace
     prof, cache = prompt_phase()
     decode_eager(cache)
-    graph = None
-    if args.decode_mode == "graph":
-        # the whole 256-token decode loop as one HIP graph over the (reused) cache buffers
-        prof, cache = prompt_phase(reuse=cache)
+    graph = pgraph_prompt = None
+    prof_g = None
+    if args.mode == "graph":
+        # the prompt phase (profile, then the compaction refilling the cache's buffers without a
+        # host read of the totals) and the whole 256-token decode loop, each as one HIP graph
+        torch.cuda.synchronize()
+        pgraph_prompt = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pgraph_prompt):
+            prof_g, _ = prompt_phase(reuse=cache, check=False)
+        prompt_phase(reuse=cache)                            # eager: resets the host-side position
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
@@ -189,7 +202,11 @@ def main() -> int:
     def one_step(ev=None):
         if ev is not None:
             ev[0].record()
-        res = prompt_phase(reuse=cache)
+        if pgraph_prompt is not None:
+            pgraph_prompt.replay()
+            res = (prof_g, cache)
+        else:
+            res = prompt_phase(reuse=cache)
         if ev is not None:
             ev[1].record()
         if graph is not None:
@@ -203,13 +220,20 @@ def main() -> int:
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    # correctness guard on the timed configuration: the last decode output equals an eager rerun
+    # correctness guard on the timed configuration: the replayed prompt phase and decode loop
+    # equal an eager rerun
     ref_out = outs.clone()
-    prompt_phase(reuse=cache)
+    ref_prof = [x.clone() for x in (prof_g.policy, prof_g.cum, prof_g.recovery)] if prof_g is not None else None
+    eprof, _ = prompt_phase(reuse=cache)
     decode_eager(cache)
     torch.cuda.synchronize()
     if not torch.equal(ref_out, outs):
         raise RuntimeError("graph replay and eager decode disagree")
+    if ref_prof is not None and not all(torch.equal(a, b) for a, b in
+                                        zip(ref_prof, (eprof.policy, eprof.cum, eprof.recovery))):
+        raise RuntimeError("graph replay and eager prompt phase disagree")
+    if cache.error_bits() != 0:
+        raise RuntimeError("cache error bits set")
     fg.timing_read()                                         # drop anything pending
     fg.timing_enable(True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -222,6 +246,14 @@ def main() -> int:
     wall = time.perf_counter() - t0
     fg.timing_enable(False)
     recs = fg.timing_read()
+    if pgraph_prompt is not None:
+        # the prompt kernels on one eager pass with the library's events around each launch
+        torch.cuda.synchronize()
+        fg.timing_enable(True)
+        prompt_phase(reuse=cache)
+        torch.cuda.synchronize()
+        fg.timing_enable(False)
+        recs += fg.timing_read()
     partials_us = None
     if graph is not None:
         # launches inside the graph carry no per-launch events.  The split-K launch alone
@@ -262,7 +294,8 @@ def main() -> int:
         per.setdefault(name, []).append(ms)
     kstats = {}
     for k, v in per.items():
-        reps = args.steps if not (graph is not None and k.startswith("decode")) else 1
+        reps = 1 if (graph is not None and k.startswith("decode")) or (pgraph_prompt is not None and
+                                                                       not k.startswith("decode")) else args.steps
         kstats[k] = {"launches_per_step": len(v) / reps, "avg_us": 1e3 * float(np.mean(v)),
                      "total_us_per_step": 1e3 * float(np.sum(v)) / reps, "timing": "events around each launch"}
     if partials_us is not None:
@@ -358,7 +391,7 @@ def main() -> int:
                                f"n={n}, d={d}, {spec.dtype}, T={T}, r_l={spec.r_l}, r_f={spec.r_f}, "
                                f"{steps_dec} decode steps",
                    "batch": B, "seq_len": n, "decode_steps": steps_dec},
-        "decode_tok_s": decode_tok_s, "decode_mode": args.decode_mode,
+        "decode_tok_s": decode_tok_s, "mode": args.mode,
         "prompt_ms": prompt_ms, "decode_ms": decode_ms,
         "policy_histogram": np.bincount(pol, minlength=5).tolist(),
         "kept_fraction": float(kept.sum() / (B * spec.n_kv_heads * n)),

@@ -134,7 +134,9 @@ typedef struct {
   int32_t* work;           /* [n_work * 4] decode work items: (head, first row of the head,
                               first absolute row, rows in use); fg_compact fills it and every
                               fg_decode_step append keeps the rows-in-use count current */
-  uint32_t* error_word;    /* [1] sticky device error bits: 1 = capacity overflow */
+  uint32_t* error_word;    /* [1] sticky device error bits: 1 = an append found its head full,
+                              2 = the compaction plan did not fit total_rows / n_work /
+                              items_per_head (the heads that do not fit are left empty) */
   int64_t total_rows;      /* [host] rows allocated */
   int64_t n_work;          /* [host] work items */
   int64_t items_per_head;  /* [host] largest work-item count of a head (partial-state slots
@@ -181,7 +183,12 @@ fg_status fg_compact_plan(const fg_shape* shape, const fg_params* params,
  * and clear error_word.  cache must hold the buffers sized from
  * fg_compact_plan (k, v, pos with total_rows rows; work with n_work items)
  * and its row_offset, capacity, ring, policy, work_offset arrays; n_prompt,
- * w_l and next_pos are set by this call.  Rows are byte copies.
+ * w_l, next_pos and chunk_rows are set by this call.  Rows are byte copies.
+ * total_rows, n_work and items_per_head are capacities: a cache allocated for
+ * an earlier plan can be refilled without reading the new totals (no host
+ * synchronisation), and a plan that exceeds them sets bit 2 of error_word
+ * (read with fg_cache_error) and leaves the heads that do not fit empty,
+ * with every write kept inside the buffers.
  */
 fg_status fg_compact(const fg_shape* shape, const fg_params* params,
                      const void* K, const void* V, const uint8_t* token_class,

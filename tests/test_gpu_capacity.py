@@ -1,0 +1,67 @@
+"""Refilling a cache allocated for another plan, without reading the new totals.
+
+fg_compact treats the cache's total_rows / n_work / items_per_head as capacities:
+a smaller plan refills the buffers exactly like a fresh cache, and a plan that
+does not fit sets bit 2 of error_word and leaves those heads empty, with every
+write inside the buffers (the kernels bound-check against the capacities)."""
+import numpy as np
+import pytest
+import torch
+
+from adaptive_kv_cache_fg_amd import fastgen as fg
+from synth import inputs as syn
+
+pytestmark = pytest.mark.gpu
+
+
+def _upload(x, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(syn.bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _setup(steps):
+    spec = syn.custom_spec(syn.CONFIGS[1], seq_len=520, n_q_heads=8, n_kv_heads=4, mix="fixed",
+                           fixed_types=("special", "punct", "local", "none"), batch=2)
+    li = syn.make_layer(spec, 0)
+    ds = syn.make_decode_stream(spec, 0, steps)
+    Q, K, V = (_upload(x, spec.dtype) for x in (li.Q, li.K, li.V))
+    cls = torch.from_numpy(li.token_class).cuda()
+    qs, ks, vs = (_upload(x, spec.dtype) for x in (ds.q, ds.k, ds.v))
+    ncs = torch.from_numpy(ds.new_class).cuda()
+    small = fg.profile(Q, K, cls, spec.r_l, spec.r_f, 0.6)       # low threshold: cheap policies
+    big = fg.profile(Q, K, cls, spec.r_l, spec.r_f, 1.0)         # every head keeps everything
+    return spec, K, V, cls, qs, ks, vs, ncs, small, big
+
+
+def test_smaller_plan_refills_like_a_fresh_cache():
+    steps = 10
+    spec, K, V, cls, qs, ks, vs, ncs, small, big = _setup(steps)
+    print(f"[capacity] smaller plan, n={spec.seq_len}", flush=True)
+    fresh = fg.compact(K, V, cls, small, 8, max_new_tokens=steps)
+    want = [fresh.decode_step(qs[t], ks[t], vs[t], ncs[t]).clone() for t in range(steps)]
+    want_kept = fresh.kept_positions()
+    cache = fg.compact(K, V, cls, big, 8, max_new_tokens=steps)    # buffers sized for the bigger plan
+    assert cache.c.total_rows > fresh.c.total_rows
+    fg.compact(K, V, cls, small, 8, max_new_tokens=steps, reuse=cache, check=False)
+    got = [cache.decode_step(qs[t], ks[t], vs[t], ncs[t]).clone() for t in range(steps)]
+    assert cache.error_bits() == 0
+    for t in range(steps):
+        assert torch.equal(got[t], want[t]), t
+    assert all(np.array_equal(a, b) for a, b in zip(cache.kept_positions(), want_kept))
+
+
+def test_plan_that_does_not_fit_is_reported():
+    steps = 4
+    spec, K, V, cls, qs, ks, vs, ncs, small, big = _setup(steps)
+    print(f"[capacity] plan beyond the buffers, n={spec.seq_len}", flush=True)
+    cache = fg.compact(K, V, cls, small, 8, max_new_tokens=steps)  # buffers sized for the smaller plan
+    fg.compact(K, V, cls, big, 8, max_new_tokens=steps, reuse=cache, check=False)
+    for t in range(steps):
+        out = cache.decode_step(qs[t], ks[t], vs[t], ncs[t])
+        assert torch.isfinite(out).all()
+    assert cache.error_bits() & 2
+    # the same buffers take the fitting plan again afterwards
+    fg.compact(K, V, cls, small, 8, max_new_tokens=steps, reuse=cache, check=False)
+    cache.decode_step(qs[0], ks[0], vs[0], ncs[0])
+    assert cache.error_bits() == 0
