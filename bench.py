@@ -46,10 +46,10 @@ def _oracle_head(args):
     """Profile + compact (and optionally decode) one KV head with the oracle, 1 BLAS thread."""
     from threadpoolctl import threadpool_limits
     from oracle import fastgen_ref as ref
-    spec_id, h, do_decode = args
+    spec_id, layer, h, do_decode = args
     spec = syn.CONFIGS[spec_id]
     with threadpool_limits(1):
-        li = syn.make_layer(spec, 0, heads=[h])
+        li = syn.make_layer(spec, layer, heads=[h])
         G = spec.group
         t0 = time.perf_counter()
         pr = ref.profile_head(li.Q[0, :G], li.K[0, 0], li.token_class[0], spec.r_l, spec.r_f, spec.T[0])
@@ -57,7 +57,7 @@ def _oracle_head(args):
         t1 = time.perf_counter()
         td = 0.0
         if do_decode:
-            ds = syn.make_decode_stream(spec, 0, heads=[h])
+            ds = syn.make_decode_stream(spec, layer, heads=[h])
             t2 = time.perf_counter()
             ref.decode_incremental(li.K[0, 0], li.V[0, 0], li.token_class[0], pr.F, pr.w_l, pr.policy,
                                    ds.q[:, 0, :G], ds.k[:, 0, 0], ds.v[:, 0, 0], ds.new_class[:, 0])
@@ -65,7 +65,7 @@ def _oracle_head(args):
     return t1 - t0, td
 
 
-def cpu_baseline(spec: syn.ConfigSpec, sample_heads: int) -> dict:
+def cpu_baseline(spec: syn.ConfigSpec, sample_heads: int, layer: int = 0) -> dict:
     """Time the oracle on a sample of KV heads over a fork pool (run before the GPU is touched)."""
     import concurrent.futures as cf
     import multiprocessing as mp
@@ -74,10 +74,10 @@ def cpu_baseline(spec: syn.ConfigSpec, sample_heads: int) -> dict:
     ctx = mp.get_context("fork")
     with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
         t0 = time.perf_counter()
-        res = list(ex.map(_oracle_head, [(spec.cfg_id, h, False) for h in heads]))
+        res = list(ex.map(_oracle_head, [(spec.cfg_id, layer, h, False) for h in heads]))
         w_prompt = time.perf_counter() - t0
         t0 = time.perf_counter()
-        res_d = list(ex.map(_oracle_head, [(spec.cfg_id, h, True) for h in heads]))
+        res_d = list(ex.map(_oracle_head, [(spec.cfg_id, layer, h, True) for h in heads]))
         w_both = time.perf_counter() - t0
     scale = spec.batch * spec.n_kv_heads / len(heads)
     prompt_tok_s = spec.batch * spec.seq_len / (w_prompt * scale)
@@ -136,8 +136,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=1, help="workload id (1 = Llama-1-7B layer)")
+    ap.add_argument("--layer", type=int, default=0, help="layer of a multi-layer workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=16)
+    ap.add_argument("--no-full-baseline", action="store_true",
+                    help="skip the full-cache decode baseline (every head keeps every key)")
     ap.add_argument("--mode", "--decode-mode", dest="mode", choices=["graph", "eager"], default="graph",
                     help="graph: the prompt phase and the decode loop each captured once as a HIP graph "
                          "and replayed; eager: every call launched from Python")
@@ -146,18 +149,19 @@ def main() -> int:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         return 2
     spec = syn.CONFIGS[args.config]
-    if spec.layers != 1:
-        spec = syn.custom_spec(spec, layers=1)
+    if not 0 <= args.layer < spec.layers:
+        print(json.dumps({"error": f"--layer must be in [0, {spec.layers})"}))
+        return 2
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, args.cpu_sample_heads)     # before any GPU call (fork pool)
+        cpu = cpu_baseline(spec, args.cpu_sample_heads, args.layer)   # before any GPU call (fork pool)
 
     import torch
     from adaptive_kv_cache_fg_amd import fastgen as fg
 
-    li = syn.make_layer(spec, 0)
-    ds = syn.make_decode_stream(spec, 0)
+    li = syn.make_layer(spec, args.layer)
+    ds = syn.make_decode_stream(spec, args.layer)
     steps_dec = spec.decode_steps
     Qd, Kd, Vd = upload(torch, li.Q, spec.dtype), upload(torch, li.K, spec.dtype), upload(torch, li.V, spec.dtype)
     cls = torch.from_numpy(li.token_class).cuda()
@@ -372,6 +376,48 @@ def main() -> int:
     roofline = {"bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"], "unit": dk["unit"],
                 "frac": dk["frac"], "traffic": measured_traffic(dominant), "kernel": dominant}
 
+    # full-cache baseline (outside the timed region): the same decode loop over caches that keep
+    # every key (T = 1: every head takes the full policy), against the adaptive caches above
+    full = None
+    if not args.no_full_baseline:
+        fprof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, 1.0)
+        fcache = fg.compact(Kd, Vd, cls, fprof, Hq, max_new_tokens=steps_dec, max_new_kept=max_new_kept)
+        fouts = torch.empty_like(outs)
+
+        def full_decode():
+            for t in range(steps_dec):
+                fcache.decode_step(qs[t], ks[t], vs[t], ncs[t], out=fouts[t])
+
+        full_decode()
+        fg.compact(Kd, Vd, cls, fprof, Hq, max_new_tokens=steps_dec, max_new_kept=max_new_kept, reuse=fcache)
+        torch.cuda.synchronize()
+        fgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(fgraph):
+            full_decode()
+        fts = []
+        for _ in range(max(3, min(args.steps, 10))):
+            fg.compact(Kd, Vd, cls, fprof, Hq, max_new_tokens=steps_dec, max_new_kept=max_new_kept,
+                       reuse=fcache, check=False)
+            fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            fe[0].record()
+            fgraph.replay()
+            fe[1].record()
+            torch.cuda.synchronize()
+            fts.append(fe[0].elapsed_time(fe[1]))
+        del fgraph
+        full_ms = float(np.median(fts))
+        full_rows = float(B * spec.n_kv_heads * n + B * spec.n_kv_heads * (steps_dec - 1) / 2.0)
+        kept_rows = mean_rows
+        full = {
+            "decode_tok_s": B * steps_dec / (full_ms * 1e-3),
+            "decode_speedup": (full_ms / steps_dec) / (decode_ms / steps_dec),
+            "kv_bytes_full": full_rows * 2 * d * e,
+            "kv_bytes_adaptive": kept_rows * 2 * d * e,
+            "kv_pruned_fraction": 1.0 - kept_rows / full_rows,
+            "note": "same decode loop over caches keeping every key (T = 1), graph-replayed; KV bytes are "
+                    "mean rows in use over the steps x 2*d*e",
+        }
+
     # a plain copy of known size, outside the timed region: the reference that scales the
     # FETCH_SIZE / WRITE_SIZE counters of the kernels above when this script runs under rocprofv3
     calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -387,15 +433,17 @@ def main() -> int:
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
         "data": "synthetic (seeded Llama-shaped post-RoPE Q/K/V with planted head types)",
-        "config": {"workload": f"{spec.name}: 1 attention layer, B={B}, Hq={Hq}, Hkv={spec.n_kv_heads}, "
-                               f"n={n}, d={d}, {spec.dtype}, T={T}, r_l={spec.r_l}, r_f={spec.r_f}, "
-                               f"{steps_dec} decode steps",
-                   "batch": B, "seq_len": n, "decode_steps": steps_dec},
+        "config": {"workload": f"{spec.name}: 1 attention layer"
+                               f"{f' (layer {args.layer} of {spec.layers})' if spec.layers > 1 else ''}, "
+                               f"B={B}, Hq={Hq}, Hkv={spec.n_kv_heads}, n={n}, d={d}, {spec.dtype}, T={T}, "
+                               f"r_l={spec.r_l}, r_f={spec.r_f}, {steps_dec} decode steps",
+                   "batch": B, "seq_len": n, "decode_steps": steps_dec, "layer": args.layer},
         "decode_tok_s": decode_tok_s, "mode": args.mode,
         "prompt_ms": prompt_ms, "decode_ms": decode_ms,
         "policy_histogram": np.bincount(pol, minlength=5).tolist(),
         "kept_fraction": float(kept.sum() / (B * spec.n_kv_heads * n)),
         "roofline": roofline,
+        "full_cache_baseline": full,
         "kernels": kstats,
         "cpu_baseline": cpu,
     }
