@@ -28,6 +28,25 @@ __device__ __forceinline__ bool perm_keep(uint8_t c, bool f, int pol) {
 
 __device__ __forceinline__ int ring_slots(int pol, int w_l) { return (pol == 3 && w_l >= 2) ? w_l - 1 : 0; }
 
+// Permanent-key mask of the 32 positions [32w, 32w + 32) of one head, bit i =
+// position 32w + i, from 8 aligned 4-byte words of class bytes (each byte 0, 1
+// or 2: bit 0 = special, bit 1 = punct) and the frequent-set word.  The caller
+// guarantees that the 32 positions exist and that cl32 is 4-byte aligned.
+__device__ __forceinline__ uint32_t perm_mask_word(const uint32_t* cl32, const uint32_t* fm, int w, int pol) {
+  if (pol == 4) return 0xffffffffu;
+  const uint32_t f = pol >= 2 ? fm[w] : 0u;
+  uint32_t m = 0u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t x = cl32[8 * w + k];
+    uint32_t keep = x & 0x01010101u;                             // special
+    if (pol >= 1) keep |= (x >> 1) & 0x01010101u;                // punct
+    keep |= (((f >> (4 * k)) & 0xFu) * 0x00204081u) & 0x01010101u;   // frequent: 4 bits spread to bytes
+    m |= ((keep * 0x10204080u) >> 28) << (4 * k);                // byte bits gathered back in order
+  }
+  return m;
+}
+
 __device__ __forceinline__ int block_sum_i(int v, int* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -52,7 +71,20 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ c
   const int pol = policy[hd];
   const int R = ring_slots(pol, w_l);
   int np = 0, nr = 0;
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+  int j0 = 0;                                              // positions below j0 are counted by words
+  if ((reinterpret_cast<uintptr_t>(cl) & 3u) == 0) {       // class row 4-byte aligned: 32 positions a step
+    const uint32_t* cl32 = reinterpret_cast<const uint32_t*>(cl);
+    for (int w = threadIdx.x; w < n / 32; w += blockDim.x) {
+      const uint32_t m = perm_mask_word(cl32, fm, w, pol);
+      np += __popc(m);
+      if (R > 0) {                                         // normal keys of the window [n - R, n)
+        const int lo = max(n - R - 32 * w, 0);
+        if (lo < 32) nr += __popc(~m & (0xffffffffu << lo));
+      }
+    }
+    j0 = (n / 32) * 32;
+  }
+  for (int j = j0 + threadIdx.x; j < n; j += blockDim.x) {
     const bool p = perm_keep(cl[j], fbit(fm, j), pol);
     np += p;
     nr += (!p && R > 0 && j >= n - R);
@@ -137,7 +169,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, co
 
   // permanent keys at positions before this chunk
   int before = 0;
-  for (int j = tid; j < ch * kPosChunk; j += blockDim.x) before += perm_keep(cl[j], fbit(fm, j), pol);
+  if ((reinterpret_cast<uintptr_t>(cl) & 3u) == 0) {       // 32 positions a step (all before this chunk exist)
+    const uint32_t* cl32 = reinterpret_cast<const uint32_t*>(cl);
+    for (int w = tid; w < ch * (kPosChunk / 32); w += blockDim.x) before += __popc(perm_mask_word(cl32, fm, w, pol));
+  } else {
+    for (int j = tid; j < ch * kPosChunk; j += blockDim.x) before += perm_keep(cl[j], fbit(fm, j), pol);
+  }
   before = block_sum_i(before, red);
 
   const int j = ch * kPosChunk + tid;
