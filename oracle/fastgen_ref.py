@@ -138,6 +138,29 @@ def column_scores(Qg: np.ndarray, K: np.ndarray, w_l: int, executor=None) -> Dic
     return {"cum": cum, "band": band, "lse": lse}
 
 
+def attention_output(Qg: np.ndarray, K: np.ndarray, V: np.ndarray, executor=None) -> np.ndarray:
+    """Prompt-phase attention output O^g = A^g V of one KV head's G query heads.
+
+    This is the ordinary causal attention the model computes while it encodes
+    the prompt, the pass the profiling rides on (Method, first paragraph: the
+    heads are profiled during prompt encoding).  Qg: [G, n, d], K: [n, d],
+    V: [n, d_v].  Returns [G, n, d_v] fp64; row blocks are independent.
+    """
+    Qg = np.asarray(Qg, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    G, n, _ = Qg.shape
+
+    def block(item):
+        g, r0, r1 = item
+        return causal_attention_rows(Qg[g, r0:r1], K, r0) @ V
+
+    items = _blocks(G, n)
+    out = np.zeros((G, n, V.shape[1]), dtype=np.float64)
+    for (g, r0, r1), o in zip(items, _map(block, items, executor)):
+        out[g, r0:r1] = o
+    return out
+
+
 def frequent_set(cum: np.ndarray, k_f: int) -> np.ndarray:
     """F: the k_f keys with the largest cumulative score, ties to the lower index."""
     n = cum.shape[0]
@@ -370,7 +393,7 @@ def pairs_causal(n: int) -> int:
 
 
 __all__: Sequence[str] = [
-    "budgets", "causal_attention_rows", "column_scores", "frequent_set", "key_levels", "row_bins",
+    "budgets", "causal_attention_rows", "attention_output", "column_scores", "frequent_set", "key_levels", "row_bins",
     "recovery_from_bins", "select_policy", "kept_positions", "compact_head", "profile_head",
     "profile_layer", "decode_incremental", "decode_masked", "HeadProfile",
 ]

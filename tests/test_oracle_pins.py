@@ -238,6 +238,43 @@ def test_attention_rows_match_torch_sdpa():
         np.testing.assert_allclose(A, out[0, 0].numpy(), atol=1e-13)
 
 
+def test_attention_output_matches_torch_sdpa():
+    rng = np.random.default_rng(25)
+    for G, n, d, dv in [(1, 1, 8, 8), (2, 9, 16, 5), (3, 600, 32, 32)]:
+        Qg = rng.standard_normal((G, n, d)) * 2
+        K = rng.standard_normal((n, d)) * 2
+        V = rng.standard_normal((n, dv))
+        O = ref.attention_output(Qg, K, V)
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Qg)[None], torch.from_numpy(K)[None, None].expand(1, G, -1, -1),
+            torch.from_numpy(V)[None, None].expand(1, G, -1, -1), is_causal=True)[0]
+        np.testing.assert_allclose(O, want.numpy(), atol=1e-12)
+
+
+def test_attention_output_closed_forms():
+    rng = np.random.default_rng(26)
+    G, n, d = 2, 700, 16
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, 4))
+    # zero queries attend uniformly: row i is the mean of V[0..i]
+    O = ref.attention_output(np.zeros((G, n, d)), K, V)
+    prefix_mean = np.cumsum(V, axis=0) / np.arange(1, n + 1)[:, None]
+    np.testing.assert_allclose(O[0], prefix_mean, atol=1e-12)
+    np.testing.assert_allclose(O[1], prefix_mean, atol=1e-12)
+    # row 0 sees only key 0; a constant value column passes through unchanged
+    Qg = rng.standard_normal((G, n, d)) * 3
+    V[:, 2] = 1.75
+    O = ref.attention_output(Qg, K, V)
+    np.testing.assert_allclose(O[:, 0], np.broadcast_to(V[0], (G, 4)), atol=1e-12)
+    np.testing.assert_allclose(O[:, :, 2], 1.75, atol=1e-12)
+    # a query far along k_j picks out v_j when k_j is the unique maximiser
+    K2 = np.eye(n, d) if n <= d else np.vstack([np.eye(d), np.zeros((n - d, d))])
+    q = np.zeros((1, n, d))
+    q[0, d - 1:, d - 1] = 200.0
+    O2 = ref.attention_output(q, K2, V)
+    np.testing.assert_allclose(O2[0, n - 1], V[d - 1], atol=1e-12)
+
+
 def test_lse_matches_scipy():
     from scipy.special import logsumexp
     rng = np.random.default_rng(22)
