@@ -127,7 +127,8 @@ const char* fg_last_error(void) { return g_last_error.c_str(); }
 const char* fg_kernel_name(int32_t id) {
   static const char* names[FG_K_COUNT] = {"profile_rowstats", "profile_colsums", "profile_select",
                                           "compact_plan",     "compact_scan",    "compact_gather",
-                                          "compact_worklist", "decode_partials", "decode_merge"};
+                                          "compact_worklist", "decode_partials", "decode_merge",
+                                          "attention"};
   return (id >= 0 && id < FG_K_COUNT) ? names[id] : "unknown";
 }
 
@@ -170,16 +171,50 @@ size_t fg_profile_workspace_size(const fg_shape* s) {
          align256(sp.cs_bytes);
 }
 
-fg_status fg_profile(const fg_shape* shape, const fg_params* params, const void* Q, const void* K,
-                     const uint8_t* token_class, uint8_t* policy, float* cum_score, float* recovery,
-                     uint32_t* freq_mask, float* lse_out, float* band_out, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
+namespace {
+
+fg_status check_attention(const fg_shape* shape, const void* Q, const void* K, const void* V, const void* O) {
+  if (shape->dtype != FG_DTYPE_BF16) return fail(FG_ERR_UNSUPPORTED, "attention output needs bf16 inputs");
+  if (!V || !O) return fail(FG_ERR_INVALID_ARG, "V and O must not be NULL");
+  if (!aligned16(V) || !aligned16(O)) return fail(FG_ERR_INVALID_ARG, "V and O must be 16-byte aligned");
+  const size_t o_bytes = (size_t)shape->batch * shape->n_q_heads * shape->seq_len * shape->head_dim * 2;
+  const size_t kv_bytes = (size_t)shape->batch * shape->n_kv_heads * shape->seq_len * shape->head_dim * 2;
+  auto overlaps = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+  };
+  if (overlaps(O, o_bytes, Q, o_bytes) || overlaps(O, o_bytes, K, kv_bytes) || overlaps(O, o_bytes, V, kv_bytes))
+    return fail(FG_ERR_INVALID_ARG, "O must not overlap Q, K or V");
+  return FG_OK;
+}
+
+fg::AttentionArgs attention_args(const fg_shape* shape, const void* Q, const void* K, const void* V, void* O) {
+  fg::AttentionArgs a{};
+  a.D = shape->head_dim;
+  a.B = shape->batch;
+  a.Hq = shape->n_q_heads;
+  a.Hkv = shape->n_kv_heads;
+  a.n = shape->seq_len;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  return a;
+}
+
+// fg_profile and fg_profile_attention: V and O are NULL for the former
+fg_status profile_impl(const fg_shape* shape, const fg_params* params, const void* Q, const void* K, const void* V,
+                       const uint8_t* token_class, void* O, uint8_t* policy, float* cum_score, float* recovery,
+                       uint32_t* freq_mask, float* lse_out, float* band_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
   fg_status s = check_shape(shape);
   if (s != FG_OK) return s;
   if ((s = check_params(params)) != FG_OK) return s;
   if (!Q || !K || !token_class || !policy || !cum_score || !recovery || !freq_mask)
     return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(Q) || !aligned16(K)) return fail(FG_ERR_INVALID_ARG, "Q and K must be 16-byte aligned");
+  const bool with_output = V || O;
+  if (with_output && (s = check_attention(shape, Q, K, V, O)) != FG_OK) return s;
   const size_t need = fg_profile_workspace_size(shape);
   if (!workspace || workspace_bytes < need) return fail(FG_ERR_WORKSPACE, "profile workspace too small");
   fg::ProfileArgs a{};
@@ -210,10 +245,52 @@ fg_status fg_profile(const fg_shape* shape, const fg_params* params, const void*
   a.fmask = freq_mask;
   a.recovery = recovery;
   a.policy = policy;
+  if (with_output) {                               // the attention kernel writes the row statistics
+    fg::AttentionArgs at = attention_args(shape, Q, K, V, O);
+    at.lse2 = a.lse2;
+    at.lse_out = lse_out;
+    const hipError_t e = fg::launch_attention(at, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention");
+    a.lse_ready = true;
+    a.rs_part = nullptr;
+  }
   hipError_t e = fg::launch_profile_sweeps(a, stream);
   if (e != hipSuccess) return hip_fail(e, "profile sweeps");
   e = fg::launch_select(a, stream);
   if (e != hipSuccess) return hip_fail(e, "profile select");
+  return FG_OK;
+}
+
+}  // namespace
+
+fg_status fg_profile(const fg_shape* shape, const fg_params* params, const void* Q, const void* K,
+                     const uint8_t* token_class, uint8_t* policy, float* cum_score, float* recovery,
+                     uint32_t* freq_mask, float* lse_out, float* band_out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  return profile_impl(shape, params, Q, K, nullptr, token_class, nullptr, policy, cum_score, recovery, freq_mask,
+                      lse_out, band_out, workspace, workspace_bytes, stream);
+}
+
+fg_status fg_profile_attention(const fg_shape* shape, const fg_params* params, const void* Q, const void* K,
+                               const void* V, const uint8_t* token_class, void* O, uint8_t* policy, float* cum_score,
+                               float* recovery, uint32_t* freq_mask, float* lse_out, float* band_out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!V || !O) return fail(FG_ERR_INVALID_ARG, "V and O must not be NULL");
+  return profile_impl(shape, params, Q, K, V, token_class, O, policy, cum_score, recovery, freq_mask, lse_out,
+                      band_out, workspace, workspace_bytes, stream);
+}
+
+fg_status fg_attention(const fg_shape* shape, const void* Q, const void* K, const void* V, void* O, float* lse_out,
+                       hipStream_t stream) {
+  fg_status s = check_shape(shape);
+  if (s != FG_OK) return s;
+  if (!Q || !K) return fail(FG_ERR_INVALID_ARG, "Q and K must not be NULL");
+  if (!aligned16(Q) || !aligned16(K)) return fail(FG_ERR_INVALID_ARG, "Q and K must be 16-byte aligned");
+  if ((s = check_attention(shape, Q, K, V, O)) != FG_OK) return s;
+  fg::AttentionArgs a = attention_args(shape, Q, K, V, O);
+  a.lse_out = lse_out;
+  const hipError_t e = fg::launch_attention(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention");
   return FG_OK;
 }
 

@@ -32,6 +32,7 @@ struct ProfileArgs {
   int kchunk, rchunk;
   float2* rs_part;   // [ceil(n/kchunk), B*Hq, n]
   float2* cs_part;   // [ceil(n/rchunk), B*Hkv, n]
+  bool lse_ready;    // lse2 already written (by the attention kernel): skip sweep 1
 };
 
 // Sweep tiling shared by the launcher and the workspace query.
@@ -59,6 +60,18 @@ inline SweepSplit sweep_split(int B, int Hq, int Hkv, int n) {
 }
 
 hipError_t launch_profile_sweeps(const ProfileArgs& a, hipStream_t st);
+
+// Causal attention output of the prompt (bf16), with the row log-sum-exp.
+struct AttentionArgs {
+  int D, B, Hq, Hkv, n;
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;           // [B*Hq*n, D] bf16
+  float* lse2;       // [B*Hq*n] log2-domain row log-sum-exp, or nullptr
+  float* lse_out;    // [B*Hq*n] natural-log copy, or nullptr
+};
+hipError_t launch_attention(const AttentionArgs& a, hipStream_t st);
 hipError_t launch_select(const ProfileArgs& a, hipStream_t st);
 
 struct PlanArgs {

@@ -23,7 +23,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
           4: "cache capacity exceeded", 5: "HIP error"}
 DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 KERNEL_NAMES = ["profile_rowstats", "profile_colsums", "profile_select", "compact_plan", "compact_scan",
-                "compact_gather", "compact_worklist", "decode_partials", "decode_merge"]
+                "compact_gather", "compact_worklist", "decode_partials", "decode_merge", "attention"]
 
 
 class FgShape(ctypes.Structure):
@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
     L.fg_profile_workspace_size.argtypes, L.fg_profile_workspace_size.restype = [sh], S
     L.fg_profile.argtypes = [sh, pa, P, P, P, P, P, P, P, P, P, P, S, P]
     L.fg_profile.restype = ctypes.c_int
+    L.fg_profile_attention.argtypes = [sh, pa, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    L.fg_profile_attention.restype = ctypes.c_int
+    L.fg_attention.argtypes, L.fg_attention.restype = [sh, P, P, P, P, P, P], ctypes.c_int
     L.fg_compact_plan.argtypes = [sh, pa, P, P, P, I32, I32, P, P, P, P, P, P, P]
     L.fg_compact_plan.restype = ctypes.c_int
     L.fg_compact.argtypes = [sh, pa, P, P, P, P, P, ca, P]
@@ -132,6 +135,7 @@ class Profile:
     r_l: float
     r_f: float
     T: float
+    out: Optional[torch.Tensor] = None   # [B, Hq, n, d] attention output (profile with V only)
 
     def frequent(self) -> np.ndarray:
         """Host bool array [B, Hkv, n] of the frequent set (synchronises)."""
@@ -142,8 +146,12 @@ class Profile:
 
 
 def profile(Q: torch.Tensor, K: torch.Tensor, token_class: torch.Tensor, r_l: float, r_f: float, T: float,
-            want_lse: bool = False, want_band: bool = False) -> Profile:
-    """fg_profile: per (b, KV head) cumulative scores, frequent set, recovery R_0..R_4 and policy."""
+            want_lse: bool = False, want_band: bool = False, V: Optional[torch.Tensor] = None) -> Profile:
+    """fg_profile: per (b, KV head) cumulative scores, frequent set, recovery R_0..R_4 and policy.
+
+    With V (bf16 only) this is fg_profile_attention: the prompt's attention
+    output is computed in the same pass and returned as ``Profile.out``.
+    """
     _need(Q, "Q")
     _need(K, "K")
     _need(token_class, "token_class", torch.uint8)
@@ -161,10 +169,43 @@ def profile(Q: torch.Tensor, K: torch.Tensor, token_class: torch.Tensor, r_l: fl
     ws_bytes = L.fg_profile_workspace_size(ctypes.byref(shape))
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     params = FgParams(r_l, r_f, T)
-    _check(L.fg_profile(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), _ptr(K), _ptr(token_class),
-                        _ptr(policy), _ptr(cum), _ptr(rec), _ptr(fmask), _ptr(lse), _ptr(band),
-                        _ptr(ws), ws_bytes, _stream()), "fg_profile")
-    return Profile(policy, cum, rec, fmask, lse, band, r_l, r_f, T)
+    if V is None:
+        out = None
+        _check(L.fg_profile(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), _ptr(K), _ptr(token_class),
+                            _ptr(policy), _ptr(cum), _ptr(rec), _ptr(fmask), _ptr(lse), _ptr(band),
+                            _ptr(ws), ws_bytes, _stream()), "fg_profile")
+    else:
+        _need(V, "V", Q.dtype)
+        if V.shape != K.shape:
+            raise ValueError(f"V shape {tuple(V.shape)} does not match K {tuple(K.shape)}")
+        out = torch.empty_like(Q)
+        _check(L.fg_profile_attention(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), _ptr(K), _ptr(V),
+                                      _ptr(token_class), _ptr(out), _ptr(policy), _ptr(cum), _ptr(rec),
+                                      _ptr(fmask), _ptr(lse), _ptr(band), _ptr(ws), ws_bytes, _stream()),
+               "fg_profile_attention")
+    return Profile(policy, cum, rec, fmask, lse, band, r_l, r_f, T, out)
+
+
+def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, want_lse: bool = False,
+              out: Optional[torch.Tensor] = None):
+    """fg_attention: causal softmax(Q K^T / sqrt(d)) V per query head (bf16) -> (O, lse or None)."""
+    _need(Q, "Q")
+    _need(K, "K")
+    _need(V, "V", Q.dtype)
+    shape = make_shape(Q, K)
+    if V.shape != K.shape:
+        raise ValueError(f"V shape {tuple(V.shape)} does not match K {tuple(K.shape)}")
+    if out is None:
+        out = torch.empty_like(Q)
+    else:
+        _need(out, "out", Q.dtype)
+        if out.shape != Q.shape:
+            raise ValueError("out must have Q's shape")
+    B, Hq, n, _ = Q.shape
+    lse = torch.empty((B, Hq, n), dtype=torch.float32, device=Q.device) if want_lse else None
+    _check(lib().fg_attention(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse), _stream()),
+           "fg_attention")
+    return out, lse
 
 
 class Cache:

@@ -110,6 +110,32 @@ fg_status fg_profile(const fg_shape* shape, const fg_params* params,
                      float* lse_out, float* band_out,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fg_attention -- the prompt's causal attention output, the pass the profiling
+ * rides on (Method, first paragraph: heads are profiled while the prompt is
+ * encoded).  Per batch entry b and query head hq with KV head h = hq / G:
+ *   O[b,hq,i,:] = sum_{j <= i} A_ij V[b,h,j,:],  A_ij = softmax_j(q_i . k_j / sqrt(d)).
+ * bf16 only (FG_ERR_UNSUPPORTED for fp32): Q [B,Hq,n,d], K, V [B,Hkv,n,d],
+ * O [B,Hq,n,d] bf16 (caller-allocated, may not alias the inputs), all 16-byte
+ * aligned.  lse_out [B*Hq*n] fp32 (optional, NULL to skip): natural-log
+ * log-sum-exp of each row's scaled scores.  No workspace.
+ */
+fg_status fg_attention(const fg_shape* shape, const void* Q, const void* K, const void* V, void* O,
+                       float* lse_out, hipStream_t stream);
+
+/*
+ * fg_profile_attention -- fg_profile fused with fg_attention: the attention
+ * output O is computed together with the row statistics the profiling needs,
+ * so the profiling adds only its column sweep and the policy selection.
+ * Arguments and outputs as fg_profile plus V (input) and O (output) as
+ * fg_attention; bf16 only.  workspace: fg_profile_workspace_size(shape) bytes.
+ */
+fg_status fg_profile_attention(const fg_shape* shape, const fg_params* params,
+                               const void* Q, const void* K, const void* V, const uint8_t* token_class,
+                               void* O, uint8_t* policy, float* cum_score, float* recovery,
+                               uint32_t* freq_mask, float* lse_out, float* band_out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ compaction */
 
 /*
@@ -247,7 +273,8 @@ const char* fg_last_error(void);
  * milliseconds) accumulated since the last read. */
 enum {
   FG_K_ROWSTATS = 0, FG_K_COLSUMS = 1, FG_K_SELECT = 2, FG_K_PLAN = 3, FG_K_SCAN = 4,
-  FG_K_GATHER = 5, FG_K_WORKLIST = 6, FG_K_DECODE = 7, FG_K_DECODE_MERGE = 8, FG_K_COUNT = 9
+  FG_K_GATHER = 5, FG_K_WORKLIST = 6, FG_K_DECODE = 7, FG_K_DECODE_MERGE = 8, FG_K_ATTENTION = 9,
+  FG_K_COUNT = 10
 };
 void fg_kernel_timing_enable(int enable);
 int32_t fg_kernel_timing_read(int32_t* kernel_ids, float* ms, int32_t max);

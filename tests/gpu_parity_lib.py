@@ -10,7 +10,12 @@ Tolerances (fixed by the parity contract, written once here):
 * recovery: 1e-4 absolute;
 * decode outputs: max |gpu - oracle| <= 2e-3 * max |oracle| per output vector for
   bf16 inputs, 1e-5 for fp32;
-* the cache after every decode step: the exact set of kept positions.
+* the cache after every decode step: the exact set of kept positions;
+* prompt attention output O (bf16): per element
+  |gpu - oracle| <= (2^-8 + 5e-4) * (A|V|)_i + 2^-8 * |O_i|, from the bf16
+  rounding of the softmax numerators fed to the P V product (unit roundoff
+  2^-8 on each term), the bf16 rounding of the output, and fp32 slack for the
+  score and sum accumulation; plus an RMS of the normalised error <= 2^-9.
 """
 from __future__ import annotations
 
@@ -86,8 +91,37 @@ def eps_topk_ok(cum_ref: np.ndarray, F_gpu: np.ndarray, k_f: int, tau: float) ->
     return bool(np.all(cum_ref[F_gpu] >= sk - w) and np.all(cum_ref[~F_gpu] <= sk1 + w))
 
 
+def download(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_attention_head(O_g: np.ndarray, Qg: np.ndarray, K: np.ndarray, V: np.ndarray,
+                         rows: Optional[np.ndarray] = None) -> float:
+    """O_g [G, n, d] (or [G, len(rows), d]) of one KV head against the oracle; returns the
+    largest error relative to the bound."""
+    if rows is None:
+        want = ref.attention_output(Qg, K, V)
+        scale = ref.attention_output(Qg, K, np.abs(V))
+    else:
+        G = Qg.shape[0]
+        want = np.empty((G, len(rows), V.shape[1]))
+        scale = np.empty_like(want)
+        for g in range(G):
+            for k, r in enumerate(rows):
+                a = ref.causal_attention_rows(Qg[g, r:r + 1], K[: r + 1], int(r))
+                want[g, k] = (a @ V[: r + 1])[0]
+                scale[g, k] = (a @ np.abs(V[: r + 1]))[0]
+    err = np.abs(O_g - want)
+    bound = (2.0 ** -8 + 5e-4) * scale + 2.0 ** -8 * np.abs(want)
+    worst = float(np.max(err / bound))
+    assert worst <= 1.0, ("attention output outside the rounding bound", worst)
+    rms = float(np.sqrt(np.mean((err / (scale + np.abs(want))) ** 2)))
+    assert rms <= 2.0 ** -9, ("attention output error not rounding-sized", rms)
+    return worst
+
+
 def run_case(spec: syn.ConfigSpec, layer: int = 0, T: Optional[float] = None, steps: Optional[int] = None,
-             batch=None, seed=None, check_decode: bool = True) -> CaseReport:
+             batch=None, seed=None, check_decode: bool = True, fused: bool = False) -> CaseReport:
     T = spec.T[0] if T is None else T
     steps = spec.decode_steps if steps is None else steps
     log(f"[case] cfg={spec.cfg_id} {spec.name} B={spec.batch} Hq={spec.n_q_heads} Hkv={spec.n_kv_heads} "
@@ -98,8 +132,15 @@ def run_case(spec: syn.ConfigSpec, layer: int = 0, T: Optional[float] = None, st
     G = Hq // Hkv
     Qd, Kd, Vd = upload(li.Q, spec.dtype), upload(li.K, spec.dtype), upload(li.V, spec.dtype)
     cls_d = torch.from_numpy(li.token_class).cuda()
-    prof = fg.profile(Qd, Kd, cls_d, spec.r_l, spec.r_f, T, want_lse=True, want_band=True)
+    prof = fg.profile(Qd, Kd, cls_d, spec.r_l, spec.r_f, T, want_lse=True, want_band=True,
+                      V=Vd if fused else None)
     torch.cuda.synchronize()
+    if fused:                                  # the attention output the profiling rode on
+        O_g = download(prof.out)
+        for b in range(B):
+            for h in range(Hkv):
+                check_attention_head(O_g[b, h * G:(h + 1) * G], li.Q[b, h * G:(h + 1) * G].astype(np.float64),
+                                     li.K[b, h].astype(np.float64), li.V[b, h].astype(np.float64))
     pol_g = prof.policy.cpu().numpy()
     cum_g = prof.cum.cpu().numpy().astype(np.float64)
     band_g = prof.band.cpu().numpy().astype(np.float64)

@@ -95,6 +95,31 @@ def test_profile_rejects_null_and_small_workspace():
     assert _call_profile(shape, params, ptr=0x1004) == 1
 
 
+def test_attention_rejects_bad_arguments():
+    L = fgb.lib()
+    p = ctypes.c_void_p(0x1000)
+    o = ctypes.c_void_p(1 << 40)
+    bf16 = fgb.FgShape(1, 4, 4, 16, 128, 0)
+    assert L.fg_attention(ctypes.byref(fgb.FgShape(1, 4, 4, 16, 128, 1)), p, p, p, o, None, None) == 2   # fp32
+    assert L.fg_attention(ctypes.byref(fgb.FgShape(1, 4, 4, 16, 96, 0)), p, p, p, o, None, None) == 2    # head_dim
+    assert L.fg_attention(ctypes.byref(bf16), p, p, None, o, None, None) == 1                            # no V
+    assert L.fg_attention(ctypes.byref(bf16), p, p, p, None, None, None) == 1                            # no O
+    assert L.fg_attention(ctypes.byref(bf16), p, p, p, ctypes.c_void_p(0x1008 + (1 << 40)), None, None) == 1
+    # O overlapping an input
+    q = ctypes.c_void_p(1 << 30)
+    assert L.fg_attention(ctypes.byref(bf16), q, p, p, ctypes.c_void_p((1 << 30) + 4096), None, None) == 1
+    params = fgb.FgParams(0.3, 0.3, 0.95)
+    ws = 1 << 30
+    args = (ctypes.byref(bf16), ctypes.byref(params), p, p)
+    assert L.fg_profile_attention(*args, None, p, o, p, p, p, p, None, None, p, ws, None) == 1     # no V
+    assert L.fg_profile_attention(*args, p, p, None, p, p, p, p, None, None, p, ws, None) == 1     # no O
+    fp32 = fgb.FgShape(1, 4, 4, 16, 128, 1)
+    assert L.fg_profile_attention(ctypes.byref(fp32), ctypes.byref(params), p, p, p, p, o, p, p, p, p, None, None,
+                                  p, ws, None) == 2
+    need = L.fg_profile_workspace_size(ctypes.byref(bf16))
+    assert L.fg_profile_attention(*args, p, p, o, p, p, p, p, None, None, p, need - 1, None) == 3
+
+
 def test_compact_plan_rejects_bad_budgets():
     L = fgb.lib()
     shape = fgb.FgShape(1, 4, 4, 16, 128, 0)
@@ -130,7 +155,7 @@ def test_status_strings_and_kernel_names():
     L = fgb.lib()
     assert L.fg_status_string(0) == b"ok"
     assert L.fg_status_string(4) == b"cache capacity exceeded"
-    assert [L.fg_kernel_name(i).decode() for i in range(9)] == fgb.KERNEL_NAMES
+    assert [L.fg_kernel_name(i).decode() for i in range(10)] == fgb.KERNEL_NAMES
     def chunk(n):
         return L.fg_decode_chunk_rows(ctypes.byref(fgb.FgShape(1, 4, 4, n, 128, 0)))
     assert [chunk(n) for n in (1, 128, 8192, 8193, 32768, 1 << 20)] == [128, 128, 128, 256, 512, 2048]
