@@ -130,6 +130,84 @@ def upload(torch, x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
 
 
+def prompt_attention(torch, fg, Qd, Kd, Vd, cls, spec, T, sweep_flops, reps=20) -> dict:
+    """Profiling's marginal cost over the prompt attention it rides on (graph-replayed calls)."""
+    B, Hq, n, d = Qd.shape
+    O = torch.empty_like(Qd)
+
+    def time_graph(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(reps):
+            g.replay()
+        e[1].record()
+        torch.cuda.synchronize()
+        del g
+        return 1e3 * e[0].elapsed_time(e[1]) / reps
+
+    attn_us = time_graph(lambda: fg.attention(Qd, Kd, Vd, out=O))
+    fused_us = time_graph(lambda: fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T, V=Vd))
+    prof_us = time_graph(lambda: fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T))
+    # the fused call gives the same attention output and the same decisions as the two separate calls
+    fused = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T, V=Vd)
+    plain = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T)
+    fg.attention(Qd, Kd, Vd, out=O)
+    torch.cuda.synchronize()
+    if not (torch.equal(fused.out, O) and torch.equal(fused.policy, plain.policy)):
+        raise RuntimeError("fused profiling disagrees with attention + profiling")
+    # per-kernel times of one eager fused call
+    fg.timing_read()
+    fg.timing_enable(True)
+    fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T, V=Vd)
+    torch.cuda.synchronize()
+    fg.timing_enable(False)
+    kern = {k: 1e3 * ms for k, ms in fg.timing_read()}
+    attn_flops = 2 * sweep_flops                          # S = Q K^T and O = P V over the causal pairs
+    sdpa_us = None
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        G = Hq // Kd.shape[1]
+        Ke = Kd.repeat_interleave(G, dim=1) if G > 1 else Kd
+        Ve = Vd.repeat_interleave(G, dim=1) if G > 1 else Vd
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            sdpa = lambda: torch.nn.functional.scaled_dot_product_attention(Qd, Ke, Ve, is_causal=True)  # noqa: E731
+            sdpa()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            e[0].record()
+            for _ in range(reps):
+                sdpa()
+            e[1].record()
+            torch.cuda.synchronize()
+            sdpa_us = 1e3 * e[0].elapsed_time(e[1]) / reps
+        del Ke, Ve
+    except Exception:                                    # no fused torch attention for this shape
+        sdpa_us = None
+    ach = attn_flops / (kern["attention"] * 1e-6) / 1e12
+    return {
+        "attention_us": attn_us, "profile_attention_us": fused_us, "profile_alone_us": prof_us,
+        "profiling_marginal_us": fused_us - attn_us,
+        "profiling_marginal_frac": (fused_us - attn_us) / attn_us,
+        "fusion_saving_us": attn_us + prof_us - fused_us,
+        "attention_kernel": {"avg_us": kern["attention"], "algorithmic_flops": attn_flops, "achieved": ach,
+                             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_MFMA_PEAK_TFLOPS},
+        "fused_kernels_us": kern,
+        "torch_sdpa_us": sdpa_us,
+        "prompt_tok_s_attention_only": B * n / (attn_us * 1e-6),
+        "prompt_tok_s_attention_with_profiling": B * n / (fused_us * 1e-6),
+        "note": "graph-replayed calls; marginal = fg_profile_attention - fg_attention; torch_sdpa_us is "
+                "torch's fused causal attention on the same tensors (K, V repeated per query head), "
+                "launched eagerly",
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +219,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample-heads", type=int, default=16)
     ap.add_argument("--no-full-baseline", action="store_true",
                     help="skip the full-cache decode baseline (every head keeps every key)")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the prompt-attention measurement (profiling's marginal cost over attention)")
     ap.add_argument("--mode", "--decode-mode", dest="mode", choices=["graph", "eager"], default="graph",
                     help="graph: the prompt phase and the decode loop each captured once as a HIP graph "
                          "and replayed; eager: every call launched from Python")
@@ -418,6 +498,18 @@ def main() -> int:
                     "mean rows in use over the steps x 2*d*e",
         }
 
+    # the prompt's attention output with the profiling riding on it (outside the timed region):
+    # attention alone, attention fused with the profiling, the profiling alone, each captured as
+    # a HIP graph and timed over replays; torch's own causal attention on the same tensors as
+    # context.  Profiling's marginal cost is fused minus attention alone.
+    attn = None
+    if spec.dtype == "bf16" and not args.no_attention:
+        attn = prompt_attention(torch, fg, Qd, Kd, Vd, cls, spec, T, sweep_flops)
+        # one layer's generation: fused prompt pass, compaction, every decode step
+        gen_us = attn["profile_attention_us"] + max(0.0, 1e3 * prompt_ms - attn["profile_alone_us"]) + 1e3 * decode_ms
+        attn["generation_us"] = gen_us
+        attn["profiling_share_of_generation"] = attn["profiling_marginal_us"] / gen_us
+
     # a plain copy of known size, outside the timed region: the reference that scales the
     # FETCH_SIZE / WRITE_SIZE counters of the kernels above when this script runs under rocprofv3
     calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -444,6 +536,7 @@ def main() -> int:
         "kept_fraction": float(kept.sum() / (B * spec.n_kv_heads * n)),
         "roofline": roofline,
         "full_cache_baseline": full,
+        "prompt_attention": attn,
         "kernels": kstats,
         "cpu_baseline": cpu,
     }
