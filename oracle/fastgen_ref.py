@@ -234,6 +234,30 @@ def select_policy(R: np.ndarray, T: float) -> int:
     return LEVEL_FULL
 
 
+def head_type_map(R: np.ndarray, policies: np.ndarray, T: float) -> Dict[str, np.ndarray]:
+    """Offline multi-prompt head map: one policy per KV head from many sample prompts.
+
+    The jisaku.com glossary entry "FastGen" (section Profiling phase) profiles
+    a set of representative prompts once, assigns every head a type from its
+    attention over them, saves that map and applies it at inference.  Read
+    here as: R [P, H, 5] holds each prompt's recovery per KV head; the map
+    takes the recovery averaged over the P prompts and picks the first
+    shortlist entry whose mean reaches T (the per-prompt rule applied to the
+    mean); ``count`` [H, 5] tallies the per-prompt policies ``policies``
+    [P, H] as the spread of that choice.
+    """
+    R = np.asarray(R, dtype=np.float64)
+    policies = np.asarray(policies, dtype=np.int64)
+    P, H, _ = R.shape
+    mean = R.sum(axis=0) / float(P)
+    policy = np.array([select_policy(mean[h], T) for h in range(H)], dtype=np.int64)
+    count = np.zeros((H, N_LEVELS), dtype=np.int64)
+    for p in range(P):
+        for h in range(H):
+            count[h, policies[p, h]] += 1
+    return {"mean": mean, "policy": policy, "count": count}
+
+
 def kept_positions(cls: np.ndarray, F: np.ndarray, w_l: int, policy: int) -> np.ndarray:
     """Prompt keys kept in the compressed cache: {j < n : level(n, j) <= policy}.
 
@@ -395,5 +419,5 @@ def pairs_causal(n: int) -> int:
 __all__: Sequence[str] = [
     "budgets", "causal_attention_rows", "attention_output", "column_scores", "frequent_set", "key_levels", "row_bins",
     "recovery_from_bins", "select_policy", "kept_positions", "compact_head", "profile_head",
-    "profile_layer", "decode_incremental", "decode_masked", "HeadProfile",
+    "profile_layer", "decode_incremental", "decode_masked", "HeadProfile", "head_type_map",
 ]

@@ -224,6 +224,54 @@ def test_band_special_cases():
     assert np.all(zero["band"] == 0)
 
 
+# ---------------------------------------------------------------- multi-prompt head map
+
+def test_head_map_of_identical_prompts_is_the_single_prompt_policy():
+    rng = np.random.default_rng(31)
+    for _ in range(20):
+        H = 6
+        R1 = np.sort(rng.random((H, 5)), axis=1)
+        R1[:, 4] = 1.0
+        T = float(rng.choice([0.5, 0.9, 0.95]))
+        pol1 = np.array([ref.select_policy(R1[h], T) for h in range(H)])
+        P = int(rng.integers(1, 9))
+        m = ref.head_type_map(np.broadcast_to(R1, (P, H, 5)), np.broadcast_to(pol1, (P, H)), T)
+        assert np.array_equal(m["policy"], pol1)
+        np.testing.assert_allclose(m["mean"], R1, rtol=0, atol=1e-15)
+        assert np.array_equal(m["count"][np.arange(H), pol1], np.full(H, P))
+        assert np.all(m["count"].sum(axis=1) == P)
+
+
+def test_head_map_decides_on_the_mean_not_the_majority():
+    # two prompts: R_0 = 0.96 and 0.90 at T = 0.92 -> mean 0.93 keeps the special-only
+    # policy although one prompt alone needed more; three prompts with R_0 = 0.95, 0.95, 0.80
+    # at T = 0.92 -> mean 0.90 falls to the next entry although most prompts chose policy 0
+    R = np.array([[[0.96, 0.97, 0.98, 0.99, 1.0]], [[0.90, 0.97, 0.98, 0.99, 1.0]]])
+    m = ref.head_type_map(R, [[0], [1]], 0.92)
+    assert m["policy"].tolist() == [0] and m["count"].tolist() == [[1, 1, 0, 0, 0]]
+    np.testing.assert_allclose(m["mean"][0, 0], 0.93, atol=1e-15)
+    R = np.array([[[0.95, 0.96, 0.97, 0.98, 1.0]], [[0.95, 0.96, 0.97, 0.98, 1.0]], [[0.80, 0.90, 0.95, 0.97, 1.0]]])
+    m = ref.head_type_map(R, [[0], [0], [2]], 0.92)
+    assert m["policy"].tolist() == [1] and m["count"].tolist() == [[2, 0, 1, 0, 0]]
+
+
+def test_head_map_recovers_planted_types_over_prompts():
+    # eight independent tiny prompts of one planted layer: the map lands on the planted policy
+    spec = syn.CONFIGS[0]
+    li = syn.make_layer(spec, batch=[0], seed=101)
+    types = li.types
+    Rs, pols = [], []
+    for seed in range(101, 109):
+        li = syn.make_layer(spec, batch=[0], seed=seed)
+        assert li.types == types
+        prof = ref.profile_layer(li.Q, li.K, li.token_class, spec.r_l, spec.r_f, spec.T[0])[0]
+        Rs.append([p.R for p in prof])
+        pols.append([p.policy for p in prof])
+    m = ref.head_type_map(np.array(Rs), np.array(pols), spec.T[0])
+    want = {"special": 0, "punct": 1, "local": 3, "none": 4}
+    assert [int(x) for x in m["policy"]] == [want[t] for t in types]
+
+
 # ---------------------------------------------------------------- library routines
 
 def test_attention_rows_match_torch_sdpa():
