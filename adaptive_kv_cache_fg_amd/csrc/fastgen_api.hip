@@ -294,6 +294,29 @@ fg_status fg_attention(const fg_shape* shape, const void* Q, const void* K, cons
   return FG_OK;
 }
 
+fg_status fg_head_map_accumulate(int32_t n_prompts, int32_t n_kv_heads, const float* recovery, const uint8_t* policy,
+                                 double* rec_sum, int32_t* policy_count, hipStream_t stream) {
+  if (n_prompts < 1 || n_kv_heads < 1) return fail(FG_ERR_INVALID_ARG, "n_prompts and n_kv_heads must be >= 1");
+  if ((double)n_prompts * n_kv_heads * 5 > 2.0e9) return fail(FG_ERR_UNSUPPORTED, "too many prompts x heads");
+  if (!recovery || !policy || !rec_sum || !policy_count) return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
+  const hipError_t e = fg::launch_head_map_accumulate(recovery, policy, rec_sum, policy_count, n_prompts, n_kv_heads,
+                                                      stream);
+  if (e != hipSuccess) return hip_fail(e, "head map accumulate");
+  return FG_OK;
+}
+
+fg_status fg_head_map_finish(int32_t n_kv_heads, int64_t n_prompts, const fg_params* params, const double* rec_sum,
+                             float* mean_recovery, uint8_t* policy, hipStream_t stream) {
+  fg_status s = check_params(params);
+  if (s != FG_OK) return s;
+  if (n_kv_heads < 1 || n_prompts < 1) return fail(FG_ERR_INVALID_ARG, "n_prompts and n_kv_heads must be >= 1");
+  if (!rec_sum || !mean_recovery || !policy) return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
+  const hipError_t e = fg::launch_head_map_finish(rec_sum, (double)n_prompts, params->T, mean_recovery, policy,
+                                                  n_kv_heads, stream);
+  if (e != hipSuccess) return hip_fail(e, "head map finish");
+  return FG_OK;
+}
+
 int32_t fg_decode_chunk_rows(const fg_shape* shape) {
   if (check_shape(shape) != FG_OK) return 0;
   return fg::decode_chunk_rows(shape->seq_len);

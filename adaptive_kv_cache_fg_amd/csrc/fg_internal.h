@@ -73,6 +73,10 @@ struct AttentionArgs {
 };
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t st);
 hipError_t launch_select(const ProfileArgs& a, hipStream_t st);
+hipError_t launch_head_map_accumulate(const float* recovery, const uint8_t* policy, double* rec_sum, int32_t* count,
+                                      int P, int H, hipStream_t st);
+hipError_t launch_head_map_finish(const double* rec_sum, double n_prompts, double T, float* mean, uint8_t* policy,
+                                  int H, hipStream_t st);
 
 struct PlanArgs {
   int B, Hkv, n, w_l;

@@ -186,4 +186,66 @@ hipError_t launch_select(const ProfileArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- multi-prompt head map
+// jisaku.com glossary entry "FastGen", section Profiling phase: heads are typed
+// once from a set of sample prompts and the resulting map is applied at
+// inference.  Each KV head's recovery is summed over the prompts in fp64 (a
+// fixed order: prompt by prompt) with a count of the per-prompt policies; the
+// map's policy is the first shortlist entry whose mean recovery reaches T.
+__global__ __launch_bounds__(256) void head_map_accumulate_kernel(const float* __restrict__ recovery,
+                                                                  const uint8_t* __restrict__ policy,
+                                                                  double* __restrict__ rec_sum,
+                                                                  int32_t* __restrict__ count, int P, int H) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  double s[5];
+  int c[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    s[k] = rec_sum[h * 5 + k];
+    c[k] = count[h * 5 + k];
+  }
+  for (int p = 0; p < P; ++p) {
+    const size_t hd = (size_t)p * H + h;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) s[k] += (double)recovery[hd * 5 + k];
+    const int pol = min((int)policy[hd], 4);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) c[k] += (k == pol);
+  }
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    rec_sum[h * 5 + k] = s[k];
+    count[h * 5 + k] = c[k];
+  }
+}
+
+__global__ __launch_bounds__(256) void head_map_finish_kernel(const double* __restrict__ rec_sum, double n_prompts,
+                                                              double T, float* __restrict__ mean,
+                                                              uint8_t* __restrict__ policy, int H) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  int pol = 4;
+  for (int k = 4; k >= 0; --k) {
+    const double m = rec_sum[h * 5 + k] / n_prompts;
+    mean[h * 5 + k] = (float)m;
+    if (k < 4 && m >= T) pol = k;
+  }
+  policy[h] = (uint8_t)pol;
+}
+
+hipError_t launch_head_map_accumulate(const float* recovery, const uint8_t* policy, double* rec_sum, int32_t* count,
+                                      int P, int H, hipStream_t st) {
+  head_map_accumulate_kernel<<<dim3((unsigned)((H + 255) / 256)), dim3(256), 0, st>>>(recovery, policy, rec_sum,
+                                                                                      count, P, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_map_finish(const double* rec_sum, double n_prompts, double T, float* mean, uint8_t* policy,
+                                  int H, hipStream_t st) {
+  head_map_finish_kernel<<<dim3((unsigned)((H + 255) / 256)), dim3(256), 0, st>>>(rec_sum, n_prompts, T, mean,
+                                                                                  policy, H);
+  return hipGetLastError();
+}
+
 }  // namespace fg

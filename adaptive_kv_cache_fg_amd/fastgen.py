@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
     L.fg_profile_attention.argtypes = [sh, pa, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     L.fg_profile_attention.restype = ctypes.c_int
     L.fg_attention.argtypes, L.fg_attention.restype = [sh, P, P, P, P, P, P], ctypes.c_int
+    L.fg_head_map_accumulate.argtypes = [I32, I32, P, P, P, P, P]
+    L.fg_head_map_accumulate.restype = ctypes.c_int
+    L.fg_head_map_finish.argtypes, L.fg_head_map_finish.restype = [I32, I64, pa, P, P, P, P], ctypes.c_int
     L.fg_compact_plan.argtypes = [sh, pa, P, P, P, I32, I32, P, P, P, P, P, P, P]
     L.fg_compact_plan.restype = ctypes.c_int
     L.fg_compact.argtypes = [sh, pa, P, P, P, P, P, ca, P]
@@ -206,6 +209,41 @@ def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, want_lse: bool 
     _check(lib().fg_attention(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse), _stream()),
            "fg_attention")
     return out, lse
+
+
+class HeadMap:
+    """Multi-prompt head map of one layer (fg_head_map_accumulate / fg_head_map_finish)."""
+
+    def __init__(self, n_kv_heads: int, device="cuda"):
+        self.n_kv_heads = n_kv_heads
+        self.rec_sum = torch.zeros((n_kv_heads, 5), dtype=torch.float64, device=device)
+        self.policy_count = torch.zeros((n_kv_heads, 5), dtype=torch.int32, device=device)
+        self.n_prompts = 0
+
+    def add(self, prof: Profile) -> None:
+        """Add the batch entries of one fg_profile call as prompts."""
+        B, Hkv = prof.policy.shape
+        if Hkv != self.n_kv_heads:
+            raise ValueError(f"profile has {Hkv} KV heads, the map {self.n_kv_heads}")
+        _check(lib().fg_head_map_accumulate(B, Hkv, _ptr(prof.recovery), _ptr(prof.policy), _ptr(self.rec_sum),
+                                            _ptr(self.policy_count), _stream()), "fg_head_map_accumulate")
+        self.n_prompts += B
+
+    def finish(self, T: float, r_l: float = 0.0, r_f: float = 0.0):
+        """(mean recovery [Hkv, 5] fp32, policy [Hkv] u8) over the prompts added so far."""
+        mean = torch.empty((self.n_kv_heads, 5), dtype=torch.float32, device=self.rec_sum.device)
+        policy = torch.empty((self.n_kv_heads,), dtype=torch.uint8, device=self.rec_sum.device)
+        params = FgParams(r_l, r_f, T)
+        _check(lib().fg_head_map_finish(self.n_kv_heads, self.n_prompts, ctypes.byref(params), _ptr(self.rec_sum),
+                                        _ptr(mean), _ptr(policy), _stream()), "fg_head_map_finish")
+        return mean, policy
+
+
+def apply_head_map(prof: Profile, policy: torch.Tensor) -> Profile:
+    """The profile with its policies replaced by a head map's (repeated over the batch), for fg_compact."""
+    from dataclasses import replace
+    B, Hkv = prof.policy.shape
+    return replace(prof, policy=policy.reshape(1, Hkv).expand(B, Hkv).contiguous())
 
 
 class Cache:

@@ -136,6 +136,30 @@ fg_status fg_profile_attention(const fg_shape* shape, const fg_params* params,
                                uint32_t* freq_mask, float* lse_out, float* band_out,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Multi-prompt head map (jisaku.com glossary entry "FastGen", section
+ * Profiling phase: heads are typed once from sample prompts, the map is saved
+ * and applied at inference).  Profile P prompts (one fg_profile call with
+ * batch = prompts, or several calls), add each call's outputs with
+ * fg_head_map_accumulate, then fg_head_map_finish gives each KV head the first
+ * shortlist entry whose recovery averaged over the prompts reaches T.  Apply
+ * the map by passing its policy (repeated over the batch) to fg_compact_plan /
+ * fg_compact together with the prompt's own freq_mask.
+ *
+ * fg_head_map_accumulate: recovery [n_prompts * n_kv_heads * 5] fp32 and
+ *   policy [n_prompts * n_kv_heads] u8 as fg_profile wrote them; rec_sum
+ *   [n_kv_heads * 5] fp64 and policy_count [n_kv_heads * 5] int32 are running
+ *   sums (in/out), zeroed by the caller before the first call; the sums run
+ *   prompt by prompt in a fixed order.
+ * fg_head_map_finish: n_prompts = the total added; mean_recovery
+ *   [n_kv_heads * 5] fp32 = rec_sum / n_prompts; policy [n_kv_heads] u8 = the
+ *   first k < 4 with rec_sum[k] / n_prompts >= T (fp64 compare), else 4.
+ */
+fg_status fg_head_map_accumulate(int32_t n_prompts, int32_t n_kv_heads, const float* recovery, const uint8_t* policy,
+                                 double* rec_sum, int32_t* policy_count, hipStream_t stream);
+fg_status fg_head_map_finish(int32_t n_kv_heads, int64_t n_prompts, const fg_params* params, const double* rec_sum,
+                             float* mean_recovery, uint8_t* policy, hipStream_t stream);
+
 /* ------------------------------------------------------------------ compaction */
 
 /*

@@ -120,6 +120,18 @@ def test_attention_rejects_bad_arguments():
     assert L.fg_profile_attention(*args, p, p, o, p, p, p, p, None, None, p, need - 1, None) == 3
 
 
+def test_head_map_rejects_bad_arguments():
+    L = fgb.lib()
+    p = ctypes.c_void_p(0x1000)
+    assert L.fg_head_map_accumulate(0, 4, p, p, p, p, None) == 1
+    assert L.fg_head_map_accumulate(4, 0, p, p, p, p, None) == 1
+    assert L.fg_head_map_accumulate(4, 4, p, None, p, p, None) == 1
+    params = fgb.FgParams(0.3, 0.3, 0.95)
+    assert L.fg_head_map_finish(4, 0, ctypes.byref(params), p, p, p, None) == 1
+    assert L.fg_head_map_finish(4, 8, ctypes.byref(fgb.FgParams(0.3, 0.3, 1.5)), p, p, p, None) == 1
+    assert L.fg_head_map_finish(4, 8, ctypes.byref(params), p, None, p, None) == 1
+
+
 def test_compact_plan_rejects_bad_budgets():
     L = fgb.lib()
     shape = fgb.FgShape(1, 4, 4, 16, 128, 0)
