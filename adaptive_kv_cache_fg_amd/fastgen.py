@@ -394,6 +394,23 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
     return Cache(shape, t, c, kept_count)
 
 
+def kept_counts(K: torch.Tensor, token_class: torch.Tensor, prof: Profile, n_q_heads: int) -> torch.Tensor:
+    """Prompt keys each (b, KV head) keeps under the profile's policies (fg_compact_plan only) -> [B*Hkv] int32."""
+    _need(K, "K")
+    B, Hkv, n, d = K.shape
+    shape = FgShape(B, n_q_heads, Hkv, n, d, DTYPE[K.dtype])
+    params = FgParams(prof.r_l, prof.r_f, prof.T)
+    H = B * Hkv
+    i32 = dict(dtype=torch.int32, device=K.device)
+    i64 = dict(dtype=torch.int64, device=K.device)
+    kept, ring, cap = torch.empty(H, **i32), torch.empty(H, **i32), torch.empty(H, **i32)
+    row_offset, work_offset, totals = torch.empty(H + 1, **i64), torch.empty(H + 1, **i64), torch.empty(3, **i64)
+    _check(lib().fg_compact_plan(ctypes.byref(shape), ctypes.byref(params), _ptr(token_class), _ptr(prof.policy),
+                                 _ptr(prof.freq_mask), 0, 0, _ptr(kept), _ptr(ring), _ptr(cap), _ptr(row_offset),
+                                 _ptr(work_offset), _ptr(totals), _stream()), "fg_compact_plan")
+    return kept
+
+
 def timing_enable(on: bool = True) -> None:
     """Bracket every eager launch with HIP events on its stream (not usable inside graph capture)."""
     lib().fg_kernel_timing_enable(1 if on else 0)

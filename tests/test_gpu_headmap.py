@@ -101,3 +101,21 @@ def test_head_map_accumulates_over_calls(gpl):
     assert torch.equal(one.policy_count, split.policy_count)
     assert torch.equal(one.rec_sum, split.rec_sum)      # prompt-by-prompt order in both
     assert torch.equal(m1, m2) and torch.equal(p1, p2)
+
+
+def test_headmap_cli_and_sensitivity(gpl, capsys):
+    from adaptive_kv_cache_fg_amd import headmap
+    import json
+    assert headmap.main(["--config", "0", "--prompts", "6", "--r", "0.2", "0.3", "--T", "0.9", "0.95", "0.99"]) == 0
+    out = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    m = out["layers"]["0"]
+    assert m["n_prompts"] == 6 and sum(m["policy_histogram"]) == 4
+    assert 0.0 < m["agreement"] <= 1.0
+    assert 0.0 < m["kept_share_map_policies"] <= 1.0
+    rows = out["sensitivity"]
+    assert len(rows) == 6
+    for row in rows:
+        assert row["retained_min"] >= row["T"] - 1e-6          # the chosen policy meets T (or is full)
+    for r in (0.2, 0.3):                                        # a higher T never keeps fewer keys
+        shares = [row["kept_share"] for row in rows if row["r"] == r]
+        assert shares == sorted(shares)
