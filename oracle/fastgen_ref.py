@@ -375,6 +375,50 @@ def decode_incremental(K: np.ndarray, V: np.ndarray, cls: np.ndarray, F: np.ndar
     return outs, caches
 
 
+def decode_tracking(K_all: np.ndarray, cls_all: np.ndarray, F: np.ndarray, w_l: int, n: int,
+                    caches: Sequence[np.ndarray], q: np.ndarray, cum0: np.ndarray):
+    """Attention of each generated token over its head's cache, split by level, and
+    the cumulative attention score of every cached key carried through generation.
+
+    The method reuses the prompt's policy because the accumulated attention of a
+    head keeps its shape from prompt encoding into decoding (hyper.ai summary,
+    Method, last paragraph, which checks accumulated scores at the prompt step and
+    later decode steps).  Step t (position p = n + t) takes the cache after that
+    step (``caches[t]``: kept positions, e.g. from ``decode_incremental``; with the
+    full policy these are 0..p) and the step's queries q[t] [G, d]:
+
+      a_gj    = softmax_j(q_g . k_j / sqrt(d)) over the cached positions j;
+      bins[t] = (1/G) sum_g sum_{j : level(p, j) = k} a_gj    for k = 0..4;
+      score_j += sum_g a_gj, where a position entering the cache starts at 0 and
+              the prompt positions start at cum0 (the prompt's cumulative score).
+
+    Returns (bins [steps, 5], score: {position: score} of the final cache).
+    """
+    K_all = np.asarray(K_all, dtype=np.float64)
+    steps, G, d = q.shape
+    score: Dict[int, float] = {}
+    for j in (caches[0] if steps else []):
+        if j < n:
+            score[int(j)] = float(cum0[j])
+    bins = np.zeros((steps, N_LEVELS), dtype=np.float64)
+    for t in range(steps):
+        p = n + t
+        rows = np.asarray(caches[t], dtype=np.int64)
+        score = {int(j): (score.get(int(j), 0.0) if j != p else 0.0) for j in rows}
+        if len(rows) == 0:
+            continue
+        s = (np.asarray(q[t], dtype=np.float64) @ K_all[rows].T) / math.sqrt(d)
+        a = np.exp(s - s.max(axis=1, keepdims=True))
+        a /= a.sum(axis=1, keepdims=True)
+        lev = key_levels(cls_all[: p + 1], F, np.array([p]), w_l)[0][rows]
+        for k in range(N_LEVELS):
+            bins[t, k] = a[:, lev == k].sum() / G
+        col = a.sum(axis=0)
+        for idx, j in enumerate(rows):
+            score[int(j)] += col[idx]
+    return bins, score
+
+
 def decode_masked(K: np.ndarray, V: np.ndarray, cls: np.ndarray, F: np.ndarray, w_l: int, policy: int,
                   q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, new_cls: np.ndarray,
                   steps_subset: Optional[Sequence[int]] = None):
@@ -420,4 +464,5 @@ __all__: Sequence[str] = [
     "budgets", "causal_attention_rows", "attention_output", "column_scores", "frequent_set", "key_levels", "row_bins",
     "recovery_from_bins", "select_policy", "kept_positions", "compact_head", "profile_head",
     "profile_layer", "decode_incremental", "decode_masked", "HeadProfile", "head_type_map",
+    "decode_tracking",
 ]

@@ -224,6 +224,79 @@ def test_band_special_cases():
     assert np.all(zero["band"] == 0)
 
 
+# ---------------------------------------------------------------- decode-time tracking
+
+def _tracking_case(rng, n, d, G, steps, policy, zero_q=False):
+    Qg, K, V, cls = _random_head(rng, n, d, G)
+    cls = cls.copy()
+    cls[0] = ref.TOKEN_SPECIAL
+    cls[rng.random(n) < 0.1] = ref.TOKEN_PUNCT
+    w_l, k_f = 5, 6
+    prof = ref.profile_head(Qg, K, cls, 0.1, 0.1, 0.9)
+    F = ref.frequent_set(prof.cum, k_f)
+    q = np.zeros((steps, G, d)) if zero_q else rng.standard_normal((steps, G, d))
+    kn = rng.standard_normal((steps, d))
+    vn = rng.standard_normal((steps, d))
+    nc = np.where(rng.random(steps) < 0.3, ref.TOKEN_PUNCT, ref.TOKEN_NORMAL).astype(np.uint8)
+    _, caches = ref.decode_incremental(K, V, cls, F, w_l, policy, q, kn, vn, nc)
+    K_all = np.concatenate([K, kn])
+    cls_all = np.concatenate([cls, nc])
+    return dict(Qg=Qg, K_all=K_all, cls_all=cls_all, F=F, w_l=w_l, n=n, caches=caches, q=q, cum0=prof.cum, G=G)
+
+
+def test_tracking_uniform_attention_closed_form():
+    rng = np.random.default_rng(41)
+    n, G, steps = 40, 2, 9
+    c = _tracking_case(rng, n, 8, G, steps, ref.LEVEL_FULL, zero_q=True)
+    bins, score = ref.decode_tracking(c["K_all"], c["cls_all"], c["F"], c["w_l"], n, c["caches"], c["q"], c["cum0"])
+    cls_all, F, w_l = c["cls_all"], c["F"], c["w_l"]
+    for t in range(steps):
+        p = n + t
+        js = np.arange(p + 1)
+        sp = cls_all[js] == ref.TOKEN_SPECIAL
+        pu = cls_all[js] == ref.TOKEN_PUNCT
+        fr = np.zeros(p + 1, dtype=bool)
+        fr[:n] = F
+        fr &= ~sp & ~pu
+        lo = (p - js < w_l) & ~sp & ~pu & ~fr
+        counts = [sp.sum(), pu.sum(), fr.sum(), lo.sum()]
+        counts.append(p + 1 - sum(counts))
+        np.testing.assert_allclose(bins[t], np.array(counts) / (p + 1), atol=1e-13)
+    harm = [G * sum(1.0 / (n + u + 1) for u in range(t0, steps)) for t0 in range(steps)]
+    for j, v in score.items():
+        want = c["cum0"][j] + harm[0] if j < n else harm[j - n]
+        assert abs(v - want) < 1e-12, (j, v, want)
+
+
+def test_tracking_full_cache_equals_row_bins_and_conserves_mass():
+    rng = np.random.default_rng(42)
+    n, d, G, steps = 30, 8, 3, 7
+    c = _tracking_case(rng, n, d, G, steps, ref.LEVEL_FULL)
+    bins, score = ref.decode_tracking(c["K_all"], c["cls_all"], c["F"], c["w_l"], n, c["caches"], c["q"], c["cum0"])
+    for t in range(steps):
+        p = n + t
+        Qx = rng.standard_normal((G, p + 1, d))
+        Qx[:, p] = c["q"][t]
+        rb = ref.row_bins(Qx, c["K_all"][: p + 1], c["cls_all"][: p + 1], c["F"], c["w_l"])
+        np.testing.assert_allclose(bins[t], rb[:, p].mean(axis=0), atol=1e-13)
+        assert abs(bins[t].sum() - 1.0) < 1e-13
+    assert sorted(score) == list(range(n + steps))
+    assert abs(sum(score.values()) - (c["cum0"].sum() + G * steps)) < 1e-10
+
+
+@pytest.mark.parametrize("policy", [0, 1, 2, 3])
+def test_tracking_compressed_cache_has_no_mass_above_its_policy(policy):
+    rng = np.random.default_rng(43 + policy)
+    n, G, steps = 35, 2, 8
+    c = _tracking_case(rng, n, 8, G, steps, policy)
+    bins, score = ref.decode_tracking(c["K_all"], c["cls_all"], c["F"], c["w_l"], n, c["caches"], c["q"], c["cum0"])
+    for t in range(steps):
+        if len(c["caches"][t]):
+            assert abs(bins[t].sum() - 1.0) < 1e-13
+            assert np.all(bins[t, policy + 1:] == 0.0)
+    assert sorted(score) == sorted(int(j) for j in c["caches"][-1])
+
+
 # ---------------------------------------------------------------- multi-prompt head map
 
 def test_head_map_of_identical_prompts_is_the_single_prompt_policy():
