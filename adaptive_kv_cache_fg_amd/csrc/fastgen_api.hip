@@ -128,7 +128,7 @@ const char* fg_kernel_name(int32_t id) {
   static const char* names[FG_K_COUNT] = {"profile_rowstats", "profile_colsums", "profile_select",
                                           "compact_plan",     "compact_scan",    "compact_gather",
                                           "compact_worklist", "decode_partials", "decode_merge",
-                                          "attention"};
+                                          "attention",        "decode_track"};
   return (id >= 0 && id < FG_K_COUNT) ? names[id] : "unknown";
 }
 
@@ -488,6 +488,71 @@ fg_status fg_decode_partials(const fg_cache* cache, const void* q, void* workspa
   if (!cache) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
   fg_cache c = *cache;                                  // next_pos is not advanced
   return decode_launch(&c, q, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, true);
+}
+
+fg_status fg_decode_track_init(const fg_cache* cache, const float* cum_score, float* row_score, hipStream_t stream) {
+  if (!cache) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
+  fg_status s = check_shape(&cache->shape);
+  if (s != FG_OK) return s;
+  if ((s = check_cache_views(cache, &cache->shape)) != FG_OK) return s;
+  if (!cum_score || !row_score) return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (cache->n_prompt != cache->shape.seq_len) return fail(FG_ERR_INVALID_ARG, "cache not compacted");
+  const hipError_t e = fg::launch_track_init(cache->row_offset, cache->pos, cum_score, row_score,
+                                             cache->shape.batch * cache->shape.n_kv_heads, cache->n_prompt, stream);
+  if (e != hipSuccess) return hip_fail(e, "track init");
+  return FG_OK;
+}
+
+size_t fg_decode_track_workspace_size(const fg_cache* c) {
+  if (!c || check_shape(&c->shape) != FG_OK || c->items_per_head < 1) return 0;
+  return fg::track_workspace_bytes((int64_t)c->shape.batch * c->shape.n_kv_heads, c->items_per_head,
+                                   c->shape.n_q_heads / c->shape.n_kv_heads);
+}
+
+fg_status fg_decode_track(const fg_cache* cache, const void* q, const uint8_t* token_class, int32_t n_total,
+                          const uint32_t* freq_mask, float* row_score, float* level_bins, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (!cache) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
+  fg_status s = check_shape(&cache->shape);
+  if (s != FG_OK) return s;
+  if ((s = check_cache_views(cache, &cache->shape)) != FG_OK) return s;
+  if (!q || !token_class || !freq_mask || !row_score || !level_bins)
+    return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(q)) return fail(FG_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  if (cache->n_prompt != cache->shape.seq_len || cache->next_pos <= cache->n_prompt || cache->next_pos >= 0x7fffffff)
+    return fail(FG_ERR_INVALID_ARG, "no decode step to track (call after fg_decode_step)");
+  if (n_total < cache->next_pos) return fail(FG_ERR_INVALID_ARG, "token_class must cover every position so far");
+  if (cache->chunk_rows != fg::decode_chunk_rows(cache->shape.seq_len))
+    return fail(FG_ERR_INVALID_ARG, "cache chunk_rows does not match its shape (was fg_compact called?)");
+  const size_t need = fg_decode_track_workspace_size(cache);
+  if (!workspace || workspace_bytes < need) return fail(FG_ERR_WORKSPACE, "track workspace too small");
+  fg::TrackArgs a{};
+  a.dtype = cache->shape.dtype;
+  a.D = cache->shape.head_dim;
+  a.B = cache->shape.batch;
+  a.Hq = cache->shape.n_q_heads;
+  a.Hkv = cache->shape.n_kv_heads;
+  a.w_l = cache->w_l;
+  a.p = cache->next_pos - 1;
+  a.n_prompt = cache->n_prompt;
+  a.n_total = n_total;
+  a.n_work = cache->n_work;
+  a.q = q;
+  a.Kc = cache->k;
+  a.pos = cache->pos;
+  a.work = cache->work;
+  a.work_offset = cache->work_offset;
+  a.cls = token_class;
+  a.fmask = freq_mask;
+  a.score = row_score;
+  a.level_bins = level_bins;
+  a.workspace = workspace;
+  a.chunk_rows = cache->chunk_rows;
+  a.items_per_head = (int)cache->items_per_head;
+  if (a.n_work == 0) return FG_OK;
+  const hipError_t e = fg::launch_track(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode track");
+  return FG_OK;
 }
 
 fg_status fg_cache_error(const fg_cache* cache, uint32_t* bits_out, hipStream_t stream) {

@@ -153,4 +153,31 @@ inline int decode_chunk_rows(int n) {
 }
 constexpr int kMaxGroup = 8;       // query heads per KV head supported by decode
 
+// Decode-time tracking (level shares of a step's attention, cumulative key scores).
+struct TrackArgs {
+  int dtype, D, B, Hq, Hkv, w_l, p, n_prompt, n_total;
+  int64_t n_work;
+  const void* q;
+  const void* Kc;
+  const int32_t* pos;
+  const int32_t* work;
+  const int64_t* work_offset;
+  const uint8_t* cls;        // [B, n_total] class of every position
+  const uint32_t* fmask;     // [B*Hkv, ceil(n_prompt/32)]
+  float* score;              // [total_rows] in/out
+  float* level_bins;         // [B*Hkv, 5]
+  void* workspace;
+  int chunk_rows, items_per_head;
+};
+// workspace: per (head, item slot, query head) a (max, sum) pair, then per (head, item slot) 5 bins
+inline size_t track_stats_bytes(int64_t heads, int64_t slots, int G) {
+  return (((size_t)heads * slots * G * 8) + 255) & ~(size_t)255;
+}
+inline size_t track_workspace_bytes(int64_t heads, int64_t slots, int G) {
+  return track_stats_bytes(heads, slots, G) + (size_t)heads * slots * 5 * 4;
+}
+hipError_t launch_track(const TrackArgs& a, hipStream_t st);
+hipError_t launch_track_init(const int64_t* row_offset, const int32_t* pos, const float* cum, float* score, int H,
+                             int n_prompt, hipStream_t st);
+
 }  // namespace fg

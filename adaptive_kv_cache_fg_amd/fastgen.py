@@ -23,7 +23,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
           4: "cache capacity exceeded", 5: "HIP error"}
 DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 KERNEL_NAMES = ["profile_rowstats", "profile_colsums", "profile_select", "compact_plan", "compact_scan",
-                "compact_gather", "compact_worklist", "decode_partials", "decode_merge", "attention"]
+                "compact_gather", "compact_worklist", "decode_partials", "decode_merge", "attention", "decode_track"]
 
 
 class FgShape(ctypes.Structure):
@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
     L.fg_profile_attention.argtypes = [sh, pa, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     L.fg_profile_attention.restype = ctypes.c_int
     L.fg_attention.argtypes, L.fg_attention.restype = [sh, P, P, P, P, P, P], ctypes.c_int
+    L.fg_decode_track_init.argtypes, L.fg_decode_track_init.restype = [ca, P, P, P], ctypes.c_int
+    L.fg_decode_track_workspace_size.argtypes, L.fg_decode_track_workspace_size.restype = [ca], S
+    L.fg_decode_track.argtypes = [ca, P, P, I32, P, P, P, P, S, P]
+    L.fg_decode_track.restype = ctypes.c_int
     L.fg_head_map_accumulate.argtypes = [I32, I32, P, P, P, P, P]
     L.fg_head_map_accumulate.restype = ctypes.c_int
     L.fg_head_map_finish.argtypes, L.fg_head_map_finish.restype = [I32, I64, pa, P, P, P, P], ctypes.c_int
@@ -255,6 +259,7 @@ class Cache:
         self.c = struct
         self.kept_count = kept_count
         self._ws = None
+        self._tws = None
 
     @property
     def next_pos(self) -> int:
@@ -292,6 +297,32 @@ class Cache:
         self._workspace(q.device)
         _check(lib().fg_decode_partials(ctypes.byref(self.c), _ptr(q), _ptr(self._ws), self._ws.numel(), _stream()),
                "fg_decode_partials")
+
+    def track_init(self, prof: Profile) -> torch.Tensor:
+        """fg_decode_track_init: per-row cumulative scores [total_rows] starting from the prompt's."""
+        score = torch.empty(max(int(self.c.total_rows), 1), dtype=torch.float32, device=self.t["k"].device)
+        _check(lib().fg_decode_track_init(ctypes.byref(self.c), _ptr(prof.cum), _ptr(score), _stream()),
+               "fg_decode_track_init")
+        return score
+
+    def track(self, q: torch.Tensor, token_class: torch.Tensor, freq_mask: torch.Tensor, row_score: torch.Tensor,
+              level_bins: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """fg_decode_track after a decode step with that step's q: level bins [B, Hkv, 5] of its attention;
+        row_score updated in place.  token_class [B, n_total] u8 covers every position so far."""
+        s = self.shape
+        _need(q, "q", self.t["k"].dtype)
+        _need(token_class, "token_class", torch.uint8)
+        if q.shape != (s.batch, s.n_q_heads, s.head_dim) or token_class.dim() != 2 or token_class.shape[0] != s.batch:
+            raise ValueError("track input shapes do not match the cache")
+        if level_bins is None:
+            level_bins = torch.empty((s.batch, s.n_kv_heads, 5), dtype=torch.float32, device=q.device)
+        if self._tws is None:
+            nb = lib().fg_decode_track_workspace_size(ctypes.byref(self.c))
+            self._tws = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+        _check(lib().fg_decode_track(ctypes.byref(self.c), _ptr(q), _ptr(token_class), token_class.shape[1],
+                                     _ptr(freq_mask), _ptr(row_score), _ptr(level_bins), _ptr(self._tws),
+                                     self._tws.numel(), _stream()), "fg_decode_track")
+        return level_bins
 
     def _workspace(self, device) -> None:
         if self._ws is None:

@@ -457,10 +457,11 @@ def main() -> int:
                 "frac": dk["frac"], "traffic": measured_traffic(dominant), "kernel": dominant}
 
     # full-cache baseline (outside the timed region): the same decode loop over caches that keep
-    # every key (T = 1: every head takes the full policy), against the adaptive caches above
+    # every key (the full policy forced for every head), against the adaptive caches above
     full = None
     if not args.no_full_baseline:
-        fprof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, 1.0)
+        fprof = fg.apply_head_map(fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T),
+                                  torch.full((spec.n_kv_heads,), 4, dtype=torch.uint8, device="cuda"))
         fcache = fg.compact(Kd, Vd, cls, fprof, Hq, max_new_tokens=steps_dec, max_new_kept=max_new_kept)
         fouts = torch.empty_like(outs)
 
@@ -494,7 +495,8 @@ def main() -> int:
             "kv_bytes_full": full_rows * 2 * d * e,
             "kv_bytes_adaptive": kept_rows * 2 * d * e,
             "kv_pruned_fraction": 1.0 - kept_rows / full_rows,
-            "note": "same decode loop over caches keeping every key (T = 1), graph-replayed; KV bytes are "
+            "note": "same decode loop over caches keeping every key (the full policy forced for every head), "
+                    "graph-replayed; KV bytes are "
                     "mean rows in use over the steps x 2*d*e",
         }
 

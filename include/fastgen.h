@@ -286,6 +286,37 @@ fg_status fg_decode_partials(const fg_cache* cache, const void* q, void* workspa
  * when an append was dropped.  *bits_out [host] receives the raw bits if not NULL. */
 fg_status fg_cache_error(const fg_cache* cache, uint32_t* bits_out, hipStream_t stream);
 
+/* ------------------------------------------------------------------ decode-time tracking */
+
+/*
+ * Accumulated attention during generation (Method, last paragraph: the policy
+ * is reused because a head's accumulated attention keeps its shape from the
+ * prompt step into later decode steps).  Call fg_decode_track after an
+ * fg_decode_step with that step's queries q; with p = cache->next_pos - 1 (the
+ * position the step generated), per (b, KV head) hd over the rows the cache
+ * holds after the step:
+ *   a_gj = softmax_j(q_g . k_j / sqrt(d)) over the cached positions j;
+ *   level_bins[hd][k] = (1/G) sum_g sum_{j : level(p, j) = k} a_gj, k = 0..4
+ *     (level as fg_profile: 0 special, 1 punct, 2 frequent, 3 p - j < w_l, 4 other);
+ *   row_score[row] += sum_g a_gj  (a row holding position p starts from 0).
+ * Over a full cache (every head with policy 4) the bins are the level shares
+ * of the generated token's whole attention row, the figure to set beside the
+ * prompt's recovery.
+ *
+ * fg_decode_track_init: row_score [total_rows] fp32 := cum_score [B*Hkv*n_prompt]
+ *   (fg_profile's output) at rows holding prompt positions, 0 elsewhere.
+ * fg_decode_track: token_class [B, n_total] u8 classes of positions
+ *   0 .. n_total - 1 (prompt and generated; n_total >= next_pos); freq_mask as
+ *   fg_profile wrote it; row_score in/out; level_bins [B*Hkv*5] fp32 out;
+ *   workspace fg_decode_track_workspace_size(cache) bytes.  Errors: no step
+ *   decoded yet (next_pos == n_prompt) or n_total < next_pos -> FG_ERR_INVALID_ARG.
+ */
+fg_status fg_decode_track_init(const fg_cache* cache, const float* cum_score, float* row_score, hipStream_t stream);
+size_t fg_decode_track_workspace_size(const fg_cache* cache);
+fg_status fg_decode_track(const fg_cache* cache, const void* q, const uint8_t* token_class, int32_t n_total,
+                          const uint32_t* freq_mask, float* row_score, float* level_bins, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ diagnostics */
 
 const char* fg_status_string(fg_status status);
@@ -298,7 +329,7 @@ const char* fg_last_error(void);
 enum {
   FG_K_ROWSTATS = 0, FG_K_COLSUMS = 1, FG_K_SELECT = 2, FG_K_PLAN = 3, FG_K_SCAN = 4,
   FG_K_GATHER = 5, FG_K_WORKLIST = 6, FG_K_DECODE = 7, FG_K_DECODE_MERGE = 8, FG_K_ATTENTION = 9,
-  FG_K_COUNT = 10
+  FG_K_TRACK = 10, FG_K_COUNT = 11
 };
 void fg_kernel_timing_enable(int enable);
 int32_t fg_kernel_timing_read(int32_t* kernel_ids, float* ms, int32_t max);

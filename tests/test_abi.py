@@ -132,6 +132,26 @@ def test_head_map_rejects_bad_arguments():
     assert L.fg_head_map_finish(4, 8, ctypes.byref(params), p, None, p, None) == 1
 
 
+def test_decode_track_rejects_bad_arguments():
+    L = fgb.lib()
+    c = fgb.FgCache()
+    p = ctypes.c_void_p(0x1000)
+    assert L.fg_decode_track(ctypes.byref(c), p, p, 16, p, p, p, p, 1 << 20, None) == 1   # no buffers
+    for name in ("k", "v", "pos", "row_offset", "len", "capacity", "ring", "policy", "work_offset", "work",
+                 "error_word"):
+        setattr(c, name, 0x1000)
+    c.shape = fgb.FgShape(1, 4, 4, 16, 128, 0)
+    c.n_prompt, c.next_pos, c.n_work, c.items_per_head, c.chunk_rows = 16, 16, 4, 1, 128
+    assert L.fg_decode_track(ctypes.byref(c), p, p, 16, p, p, p, p, 1 << 20, None) == 1   # no step decoded yet
+    c.next_pos = 18
+    assert L.fg_decode_track(ctypes.byref(c), p, p, 17, p, p, p, p, 1 << 20, None) == 1   # classes too short
+    assert L.fg_decode_track(ctypes.byref(c), p, None, 18, p, p, p, p, 1 << 20, None) == 1
+    need = L.fg_decode_track_workspace_size(ctypes.byref(c))
+    assert need >= 4 * 1 * 5 * 4
+    assert L.fg_decode_track(ctypes.byref(c), p, p, 18, p, p, p, p, need - 1, None) == 3
+    assert L.fg_decode_track_init(ctypes.byref(c), None, p, None) == 1
+
+
 def test_compact_plan_rejects_bad_budgets():
     L = fgb.lib()
     shape = fgb.FgShape(1, 4, 4, 16, 128, 0)
@@ -167,7 +187,7 @@ def test_status_strings_and_kernel_names():
     L = fgb.lib()
     assert L.fg_status_string(0) == b"ok"
     assert L.fg_status_string(4) == b"cache capacity exceeded"
-    assert [L.fg_kernel_name(i).decode() for i in range(10)] == fgb.KERNEL_NAMES
+    assert [L.fg_kernel_name(i).decode() for i in range(11)] == fgb.KERNEL_NAMES
     def chunk(n):
         return L.fg_decode_chunk_rows(ctypes.byref(fgb.FgShape(1, 4, 4, n, 128, 0)))
     assert [chunk(n) for n in (1, 128, 8192, 8193, 32768, 1 << 20)] == [128, 128, 128, 256, 512, 2048]
