@@ -208,6 +208,67 @@ def prompt_attention(torch, fg, Qd, Kd, Vd, cls, spec, T, sweep_flops, reps=20) 
     }
 
 
+def decode_stability(torch, fg, Kd, Vd, cls, prof, qs, ks, vs, ncs, spec, T) -> dict:
+    """Accumulated attention at the prompt step against the generated tokens' attention, over full
+    caches (every head keeps every key), tracked on the device step by step with fg_decode_track."""
+    B, Hkv, n, d = Kd.shape
+    Hq = qs.shape[2]
+    steps = qs.shape[0]
+    e = Kd.element_size()
+    full = fg.apply_head_map(prof, torch.full((Hkv,), 4, dtype=torch.uint8, device="cuda"))
+    cache = fg.compact(Kd, Vd, cls, full, Hq, max_new_tokens=steps, max_new_kept=steps)
+    score = cache.track_init(prof)
+    cls_all = torch.cat([cls, ncs.t()], dim=1).contiguous()             # classes of positions 0 .. n+steps-1
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    bins = torch.empty((steps, B, Hkv, 5), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    fg.timing_read()
+    fg.timing_enable(True)
+    for t in range(steps):
+        cache.decode_step(qs[t], ks[t], vs[t], ncs[t], out=out)
+        cache.track(qs[t], cls_all, prof.freq_mask, score, level_bins=bins[t])
+    torch.cuda.synchronize()
+    fg.timing_enable(False)
+    track_ms = [ms for k, ms in fg.timing_read() if k == "decode_track"]
+    b = bins.cpu().numpy().astype(np.float64)                           # [steps, B, Hkv, 5]
+    R = prof.recovery.cpu().numpy().astype(np.float64)
+    share_prompt = np.diff(np.concatenate([np.zeros((B, Hkv, 1)), R], axis=-1), axis=-1)
+    tv_mean_share = 0.5 * np.abs(b.mean(axis=0) - share_prompt).sum(axis=-1)   # [B, Hkv]
+    tv_step = 0.5 * np.abs(b - share_prompt[None]).sum(axis=-1)                  # [steps, B, Hkv]
+    pol = prof.policy.cpu().numpy().astype(np.int64)
+    retained = np.take_along_axis(np.cumsum(b, axis=-1), pol[None, :, :, None], axis=-1)[..., 0]
+    # frequent set re-ranked by the scores accumulated through generation (full caches: row j holds
+    # position j of its head), against the prompt's
+    k_f = int(np.floor(spec.r_f * n))
+    sc = score.cpu().numpy()
+    ro = cache.t["row_offset"].cpu().numpy()
+    F0 = prof.frequent()
+    overlap = []
+    for hd in range(B * Hkv):
+        s_h = sc[ro[hd]: ro[hd] + n + steps]
+        top = np.lexsort((np.arange(len(s_h)), -s_h))[:k_f]              # largest first, ties to the lower index
+        overlap.append(len(set(top.tolist()) & set(np.flatnonzero(F0[hd // Hkv, hd % Hkv]).tolist())) / max(k_f, 1))
+    rows = float(B * Hkv * n + B * Hkv * (steps + 1) / 2.0)
+    track_bytes = rows * (2 * d * e + 12)
+    avg_us = 1e3 * float(np.mean(track_ms))
+    return {
+        "steps": steps,
+        "tv_distance_mean_share": {"mean": float(tv_mean_share.mean()), "max": float(tv_mean_share.max())},
+        "tv_distance_per_step": {"mean": float(tv_step.mean()), "p95": float(np.percentile(tv_step, 95))},
+        "prompt_policy_retained_ge_T": float(np.mean(retained >= T - 1e-6)),
+        "prompt_policy_retained_min": float(retained.min()),
+        "frequent_set_overlap_after_generation": {"mean": float(np.mean(overlap)), "min": float(np.min(overlap))},
+        "track_kernel": {"avg_us": avg_us, "algorithmic_bytes": track_bytes,
+                         "achieved": track_bytes / (avg_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": track_bytes / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "note": "three launches per step (events around the whole call); K of every cached row "
+                                 "read twice, position and score read, score written"},
+        "note": "full caches (every head keeps every key); level shares of each generated token's attention vs "
+                "the prompt's per-level recovery increments; total-variation distance; retained = attention "
+                "the prompt-chosen policy's levels get at each decode step",
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +282,8 @@ def main() -> int:
                     help="skip the full-cache decode baseline (every head keeps every key)")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the prompt-attention measurement (profiling's marginal cost over attention)")
+    ap.add_argument("--no-stability", action="store_true",
+                    help="skip the decode-time stability measurement over full caches")
     ap.add_argument("--mode", "--decode-mode", dest="mode", choices=["graph", "eager"], default="graph",
                     help="graph: the prompt phase and the decode loop each captured once as a HIP graph "
                          "and replayed; eager: every call launched from Python")
@@ -512,6 +575,11 @@ def main() -> int:
         attn["generation_us"] = gen_us
         attn["profiling_share_of_generation"] = attn["profiling_marginal_us"] / gen_us
 
+    # stability of accumulated attention from the prompt into generation (outside the timed region)
+    stab = None
+    if not args.no_stability:
+        stab = decode_stability(torch, fg, Kd, Vd, cls, prof, qs, ks, vs, ncs, spec, T)
+
     # a plain copy of known size, outside the timed region: the reference that scales the
     # FETCH_SIZE / WRITE_SIZE counters of the kernels above when this script runs under rocprofv3
     calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -539,6 +607,7 @@ def main() -> int:
         "roofline": roofline,
         "full_cache_baseline": full,
         "prompt_attention": attn,
+        "decode_stability": stab,
         "kernels": kstats,
         "cpu_baseline": cpu,
     }
