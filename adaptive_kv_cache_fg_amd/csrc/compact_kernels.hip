@@ -100,43 +100,73 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ c
 
 // Exclusive prefix sums over heads: rows and decode work items, and the largest
 // item count of a head.  One workgroup.
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ capacity, int H, int chunk,
-                                                    int64_t* __restrict__ row_offset, int64_t* __restrict__ work_offset,
-                                                    int64_t* __restrict__ totals) {
-  __shared__ long long sr[1024], sw[1024];
-  __shared__ long long carry_r, carry_w;
-  __shared__ int max_w;
-  if (threadIdx.x == 0) { carry_r = 0; carry_w = 0; max_w = 1; }
-  __syncthreads();
-  for (int base = 0; base < H; base += blockDim.x) {
-    const int i = base + threadIdx.x;
-    const long long cap = i < H ? capacity[i] : 0;
-    sr[threadIdx.x] = cap;
-    sw[threadIdx.x] = i < H ? max(1LL, (cap + chunk - 1) / chunk) : 0;   // every head gets an item
-    atomicMax(&max_w, (int)sw[threadIdx.x]);
-    __syncthreads();
-    for (int o = 1; o < (int)blockDim.x; o <<= 1) {          // inclusive Hillis-Steele scan
-      const long long ar = threadIdx.x >= (unsigned)o ? sr[threadIdx.x - o] : 0;
-      const long long aw = threadIdx.x >= (unsigned)o ? sw[threadIdx.x - o] : 0;
-      __syncthreads();
-      sr[threadIdx.x] += ar;
-      sw[threadIdx.x] += aw;
-      __syncthreads();
-    }
-    if (i < H) {
-      row_offset[i + 1] = carry_r + sr[threadIdx.x];
-      work_offset[i + 1] = carry_w + sw[threadIdx.x];
-    }
-    __syncthreads();
-    if (threadIdx.x == blockDim.x - 1) { carry_r += sr[threadIdx.x]; carry_w += sw[threadIdx.x]; }
-    __syncthreads();
+// Exclusive prefix sums of the heads' rows and decode work items, one
+// workgroup: each thread sums a contiguous segment of heads, the segment totals
+// are scanned with wave shuffles and one LDS exchange between the waves, then
+// every thread writes its segment's offsets.
+constexpr int kScanThreads = 256;
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ capacity, int H, int chunk,
+                                                            int64_t* __restrict__ row_offset,
+                                                            int64_t* __restrict__ work_offset,
+                                                            int64_t* __restrict__ totals) {
+  constexpr int kWaves = kScanThreads / kWave;
+  __shared__ long long wr[kWaves], ww[kWaves];
+  __shared__ int wm[kWaves];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int seg = (H + kScanThreads - 1) / kScanThreads;
+  const int i0 = min(H, t * seg), i1 = min(H, i0 + seg);
+  long long sr = 0, sw = 0;
+  int mw = 1;
+  for (int i = i0; i < i1; ++i) {
+    const long long cap = capacity[i];
+    const long long w = max(1LL, (cap + chunk - 1) / chunk);   // every head gets an item
+    sr += cap;
+    sw += w;
+    mw = max(mw, (int)w);
   }
-  if (threadIdx.x == 0) {
+  // inclusive scans of the segment totals within the wave
+  long long ir = sr, iw = sw;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const long long ar = __shfl_up(ir, o), aw = __shfl_up(iw, o);
+    if (lane >= o) {
+      ir += ar;
+      iw += aw;
+    }
+  }
+  int m = mw;
+  for (int o = 1; o < kWave; o <<= 1) m = max(m, __shfl_xor(m, o));
+  if (lane == kWave - 1) {
+    wr[wave] = ir;
+    ww[wave] = iw;
+  }
+  if (lane == 0) wm[wave] = m;
+  __syncthreads();
+  long long cr = 0, cw = 0, tr = 0, tw = 0;
+  int mx = 1;
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) {
+      cr += wr[w];
+      cw += ww[w];
+    }
+    tr += wr[w];
+    tw += ww[w];
+    mx = max(mx, wm[w]);
+  }
+  // this segment's exclusive start, then its heads in order
+  long long r = cr + ir - sr, w = cw + iw - sw;
+  for (int i = i0; i < i1; ++i) {
+    const long long cap = capacity[i];
+    r += cap;
+    w += max(1LL, (cap + chunk - 1) / chunk);
+    row_offset[i + 1] = r;
+    work_offset[i + 1] = w;
+  }
+  if (t == 0) {
     row_offset[0] = 0;
     work_offset[0] = 0;
-    totals[0] = carry_r;
-    totals[1] = carry_w;
-    totals[2] = max_w;
+    totals[0] = tr;
+    totals[1] = tw;
+    totals[2] = mx;
   }
 }
 
@@ -269,7 +299,8 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timed_begin(FG_K_SCAN, st);
-  scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(a.capacity, H, a.chunk_rows, a.row_offset, a.work_offset, a.totals);
+  scan_kernel<<<dim3(1), dim3(kScanThreads), 0, st>>>(a.capacity, H, a.chunk_rows, a.row_offset, a.work_offset,
+                                                       a.totals);
   timed_end(st);
   return hipGetLastError();
 }
