@@ -170,8 +170,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
   }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, const T* __restrict__ V,
+template <typename T, int D, int CHUNK>
+__global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, const T* __restrict__ V,
                                                      const uint8_t* __restrict__ cls, const uint8_t* __restrict__ policy,
                                                      const uint32_t* __restrict__ fmask,
                                                      const int64_t* __restrict__ row_offset, const int32_t* __restrict__ ring,
@@ -179,9 +179,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, co
                                                      int32_t* __restrict__ pos, int32_t* __restrict__ len,
                                                      uint32_t* __restrict__ error_word, int64_t total_rows) {
   constexpr int kCPR = D * (int)sizeof(T) / 16;           // 16-byte chunks per row
-  __shared__ int red[4];
-  __shared__ int wcnt[4], wrows[4];
-  __shared__ int src_j[kPosChunk], dst_r[kPosChunk];
+  constexpr int kWaves = CHUNK / kWave;
+  static_assert(CHUNK % kWave == 0 && CHUNK <= 1024, "one position per thread, whole waves");
+  __shared__ int red[kWaves];
+  __shared__ int wcnt[kWaves], wrows[kWaves];
+  __shared__ int src_j[CHUNK], dst_r[CHUNK];
 
   const int hd = blockIdx.x / nch, ch = blockIdx.x % nch, b = hd / Hkv;
   const int nw = (n + 31) / 32;
@@ -201,13 +203,13 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, co
   int before = 0;
   if ((reinterpret_cast<uintptr_t>(cl) & 3u) == 0) {       // 32 positions a step (all before this chunk exist)
     const uint32_t* cl32 = reinterpret_cast<const uint32_t*>(cl);
-    for (int w = tid; w < ch * (kPosChunk / 32); w += blockDim.x) before += __popc(perm_mask_word(cl32, fm, w, pol));
+    for (int w = tid; w < ch * (CHUNK / 32); w += blockDim.x) before += __popc(perm_mask_word(cl32, fm, w, pol));
   } else {
-    for (int j = tid; j < ch * kPosChunk; j += blockDim.x) before += perm_keep(cl[j], fbit(fm, j), pol);
+    for (int j = tid; j < ch * CHUNK; j += blockDim.x) before += perm_keep(cl[j], fbit(fm, j), pol);
   }
   before = block_sum_i(before, red);
 
-  const int j = ch * kPosChunk + tid;
+  const int j = ch * CHUNK + tid;
   const bool valid = j < n;
   const bool pf = valid && perm_keep(cl[j], fbit(fm, j), pol);
   const bool win = valid && R > 0 && j >= n - R;          // inside the local window of row n
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ K, co
   if (lane == 0) { wcnt[wave] = __popcll(bp); wrows[wave] = __popcll(ba); }
   __syncthreads();
   int pbefore = 0, abefore = 0, ptotal = 0, atotal = 0;
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     pbefore += (w < wave) ? wcnt[w] : 0;
     abefore += (w < wave) ? wrows[w] : 0;
     ptotal += wcnt[w];
@@ -310,7 +312,7 @@ static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st) {
   const int H = a.B * a.Hkv;
   const int nch = (a.n + kPosChunk - 1) / kPosChunk;
   timed_begin(FG_K_GATHER, st);
-  gather_kernel<T, D><<<dim3(H * nch), dim3(256), 0, st>>>(
+  gather_kernel<T, D, kPosChunk><<<dim3(H * nch), dim3(kPosChunk), 0, st>>>(
       (const T*)a.K, (const T*)a.V, a.cls, a.policy, a.fmask, a.row_offset, a.ring, a.Hkv, a.n, nch, (T*)a.Kc,
       (T*)a.Vc, a.pos, a.len, a.error_word, a.total_rows);
   timed_end(st);
