@@ -419,6 +419,85 @@ def decode_tracking(K_all: np.ndarray, cls_all: np.ndarray, F: np.ndarray, w_l: 
     return bins, score
 
 
+class DynamicFrequentHead:
+    """Generation of one KV head under the local + frequent policy (level 3) with a
+    frequent set that changes during decoding: a key leaving the local window stays
+    if its cumulative attention beats the weakest frequent key, which is evicted
+    in its place.
+
+    The pages rank the frequent set by cumulative attention on the prompt and keep
+    the policy fixed while generating (hyper.ai summary, Method, policy and last
+    paragraphs).  This variant keeps ranking by the same score during generation,
+    reading the budget k_f as fixed: at step p (position p), after the attention
+    output, the key j_out = p + 1 - w_l that the window drops (a cached key of
+    class normal outside the frequent set) is compared with the frequent key of
+    the lowest score (ties: the larger position); j_out replaces it when its score
+    is strictly larger, else j_out is dropped.  Scores: the prompt's cumulative
+    score for prompt keys, 0 for a generated key when it enters, plus
+    sum_g softmax(q_g K^T / sqrt(d)) over the cache after each step (as
+    decode_tracking), so the decision at step p uses the scores through step p - 1.
+    Frequent keys are the cached keys of class normal outside the window's ring.
+    """
+
+    def __init__(self, K: np.ndarray, V: np.ndarray, cls: np.ndarray, F: np.ndarray, w_l: int, cum0: np.ndarray):
+        self.n = len(cls)
+        self.w_l = int(w_l)
+        self.cls = [int(c) for c in cls]
+        kept = kept_positions(cls, F, w_l, LEVEL_LOCAL)
+        self.kv = {int(j): (np.asarray(K[j], np.float64), np.asarray(V[j], np.float64)) for j in kept}
+        self.freq = {int(j) for j in kept if F[j] and cls[j] == TOKEN_NORMAL}
+        self.score = {int(j): float(cum0[j]) for j in kept}
+        self.t = 0
+
+    def _level_self(self, c: int) -> int:
+        return LEVEL_SPECIAL if c == TOKEN_SPECIAL else LEVEL_PUNCT if c == TOKEN_PUNCT else \
+            (LEVEL_LOCAL if self.w_l >= 1 else LEVEL_FULL)
+
+    def step(self, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, c_new: int, force: Optional[bool] = None):
+        """One generated token.  q [G, d].  ``force`` overrides the replacement decision
+        (None: the rule above).  Returns (out [G, d], kept positions after the step,
+        info {candidate, weakest, margin, replaced})."""
+        p = self.n + self.t
+        q = np.asarray(q, np.float64)
+        new = (np.asarray(k_new, np.float64), np.asarray(v_new, np.float64))
+        att = sorted(self.kv)
+        Ks = [self.kv[j][0] for j in att]
+        Vs = [self.kv[j][1] for j in att]
+        if self._level_self(c_new) <= LEVEL_LOCAL:
+            Ks.append(new[0])
+            Vs.append(new[1])
+        d = q.shape[1]
+        out = _masked_softmax_out(q, np.array(Ks).reshape(-1, d), np.array(Vs).reshape(-1, d))
+        info = {"candidate": None, "weakest": None, "margin": None, "replaced": False}
+        j_out = p + 1 - self.w_l
+        if self.w_l >= 2 and j_out in self.kv and j_out not in self.freq and self.cls[j_out] == TOKEN_NORMAL:
+            info["candidate"] = j_out
+            if self.freq:
+                weakest = min(self.freq, key=lambda j: (self.score[j], -j))
+                margin = self.score[j_out] - self.score[weakest]
+                replace = margin > 0.0 if force is None else bool(force)
+                info.update(weakest=weakest, margin=margin, replaced=replace)
+                if replace:
+                    self.freq.discard(weakest)
+                    del self.kv[weakest], self.score[weakest]
+                    self.freq.add(j_out)
+            if not info["replaced"]:
+                del self.kv[j_out], self.score[j_out]
+        if c_new in (TOKEN_SPECIAL, TOKEN_PUNCT) or self.w_l >= 2:
+            self.kv[p] = new
+            self.score[p] = 0.0
+        self.cls.append(int(c_new))
+        rows = sorted(self.kv)
+        if rows:
+            sc = (q @ np.array([self.kv[j][0] for j in rows]).T) / math.sqrt(d)
+            a = np.exp(sc - sc.max(axis=1, keepdims=True))
+            a /= a.sum(axis=1, keepdims=True)
+            for j, w in zip(rows, a.sum(axis=0)):
+                self.score[j] += float(w)
+        self.t += 1
+        return out, np.array(rows, dtype=np.int64), info
+
+
 def decode_masked(K: np.ndarray, V: np.ndarray, cls: np.ndarray, F: np.ndarray, w_l: int, policy: int,
                   q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, new_cls: np.ndarray,
                   steps_subset: Optional[Sequence[int]] = None):
@@ -464,5 +543,5 @@ __all__: Sequence[str] = [
     "budgets", "causal_attention_rows", "attention_output", "column_scores", "frequent_set", "key_levels", "row_bins",
     "recovery_from_bins", "select_policy", "kept_positions", "compact_head", "profile_head",
     "profile_layer", "decode_incremental", "decode_masked", "HeadProfile", "head_type_map",
-    "decode_tracking",
+    "decode_tracking", "DynamicFrequentHead",
 ]

@@ -297,6 +297,76 @@ def test_tracking_compressed_cache_has_no_mass_above_its_policy(policy):
     assert sorted(score) == sorted(int(j) for j in c["caches"][-1])
 
 
+def test_dynamic_frequent_without_replacement_is_the_static_policy():
+    rng = np.random.default_rng(51)
+    for w_l in (0, 1, 2, 5):
+        n, d, G, steps = 40, 8, 2, 12
+        Qg, K, V, cls = _random_head(rng, n, d, G)
+        prof = ref.profile_head(Qg, K, cls, 0.1, 0.2, 0.9)
+        F = prof.F
+        q = rng.standard_normal((steps, G, d))
+        kn, vn = rng.standard_normal((steps, d)), rng.standard_normal((steps, d))
+        nc = np.where(rng.random(steps) < 0.3, ref.TOKEN_PUNCT, ref.TOKEN_NORMAL).astype(np.uint8)
+        outs, caches = ref.decode_incremental(K, V, cls, F, w_l, ref.LEVEL_LOCAL, q, kn, vn, nc)
+        dyn = ref.DynamicFrequentHead(K, V, cls, F, w_l, prof.cum)
+        for t in range(steps):
+            o, kept, info = dyn.step(q[t], kn[t], vn[t], int(nc[t]), force=False)
+            np.testing.assert_allclose(o, outs[t], atol=1e-12)
+            assert np.array_equal(kept, caches[t]), (w_l, t)
+
+
+def test_dynamic_frequent_replaces_the_weakest_key():
+    # keys: 0 special; 3, 5, 7 frequent; the window (w_l = 4) holds the last three positions.
+    # Key 17 carries a large prompt score, so when it leaves the window it replaces the weakest
+    # frequent key: 5 and 7 tie at the lowest score, the larger position (7) goes.
+    n, d, w_l = 20, 4, 4
+    rng = np.random.default_rng(52)
+    K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    cls = np.zeros(n, dtype=np.uint8)
+    cls[0] = ref.TOKEN_SPECIAL
+    F = np.zeros(n, dtype=bool)
+    F[[3, 5, 7]] = True
+    cum0 = np.full(n, 0.5)
+    cum0[3], cum0[5], cum0[7], cum0[17] = 2.0, 0.25, 0.25, 9.0
+    dyn = ref.DynamicFrequentHead(K, V, cls, F, w_l, cum0)
+    assert sorted(dyn.kv) == [0, 3, 5, 7, 17, 18, 19] and dyn.freq == {3, 5, 7}
+    q = np.zeros((1, d))                               # uniform attention: each cached key gains 1/|cache|
+    o, kept, info = dyn.step(q, rng.standard_normal(d), rng.standard_normal(d), ref.TOKEN_NORMAL)   # p = 20
+    assert (info["candidate"], info["weakest"], info["replaced"]) == (17, 7, True)
+    assert abs(info["margin"] - (9.0 - 0.25)) < 1e-12                 # scores through the previous step
+    assert kept.tolist() == [0, 3, 5, 17, 18, 19, 20] and dyn.freq == {3, 5, 17}
+    # step p = 21: key 18 leaves with score 0.5 + 1/7 (+ the step-20 share), below the weakest (5: 0.25 + 1/7)? no:
+    # 18 has 0.5 + 1/7 > 0.25 + 1/7, so it replaces 5
+    o, kept, info = dyn.step(q, rng.standard_normal(d), rng.standard_normal(d), ref.TOKEN_PUNCT)     # p = 21
+    assert (info["candidate"], info["weakest"], info["replaced"]) == (18, 5, True)
+    assert kept.tolist() == [0, 3, 17, 18, 19, 20, 21] and dyn.freq == {3, 17, 18}
+    assert len(dyn.freq) == 3
+
+
+def test_dynamic_frequent_keeps_its_budget_and_evicts_only_weaker_keys():
+    rng = np.random.default_rng(53)
+    n, d, G, steps, w_l = 60, 8, 2, 30, 6
+    Qg, K, V, cls = _random_head(rng, n, d, G)
+    prof = ref.profile_head(Qg, K, cls, 0.1, 0.2, 0.9)
+    # prompt scores scaled down so that keys leaving the window can beat frequent keys
+    dyn = ref.DynamicFrequentHead(K, V, cls, prof.F, w_l, prof.cum * 0.02)
+    budget = len(dyn.freq)
+    replaced = 0
+    for t in range(steps):
+        before = {j: dyn.score[j] for j in dyn.freq}
+        q = rng.standard_normal((G, d)) * 2
+        o, kept, info = dyn.step(q, rng.standard_normal(d), rng.standard_normal(d), ref.TOKEN_NORMAL)
+        assert len(dyn.freq) == budget
+        if info["replaced"]:
+            replaced += 1
+            w = info["weakest"]
+            assert all((s, -j) >= (before[w], -w) for j, s in before.items())   # the weakest went
+            assert info["margin"] > 0 and info["candidate"] in dyn.freq and w not in dyn.kv
+        elif info["candidate"] is not None:
+            assert info["candidate"] not in dyn.kv
+    assert replaced > 0
+
+
 # ---------------------------------------------------------------- multi-prompt head map
 
 def test_head_map_of_identical_prompts_is_the_single_prompt_policy():
