@@ -61,13 +61,16 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     const int64_t* __restrict__ work_offset, int32_t* __restrict__ work, T* __restrict__ Kc, T* __restrict__ Vc,
     int32_t* __restrict__ pos, const int64_t* __restrict__ row_offset, int32_t* __restrict__ len,
     const int32_t* __restrict__ capacity, const int32_t* __restrict__ ring, const uint8_t* __restrict__ policy,
-    uint32_t* __restrict__ error_word, int Hkv, int w_l, int p, int S, int CH, int64_t total_rows, float c) {
+    uint32_t* __restrict__ error_word, float* __restrict__ score, const uint8_t* __restrict__ cls_all, int n_total,
+    int Hkv, int w_l, int p, int S, int CH, int64_t total_rows, float c) {
   static_assert(NT % D == 0, "one output per thread");
   constexpr int NGRP = NT / D;                     // thread groups splitting the item list
   constexpr int kBatch = kMergeBatch;
   constexpr int kWavesPerHead = D / kWave;         // waves reducing the query head's q . k_new
   __shared__ float cm[NGRP][D], cs[NGRP][D], ca[NGRP][D];
   __shared__ float s_wave[NT / kWave];
+  __shared__ unsigned long long s_key[NT / kWave];
+  __shared__ int s_row[NT / kWave];
   const int qh = blockIdx.x, hd = qh / G, g = qh % G;   // query head, its KV head, its index in the group
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int dd = tid % D, grp = tid / D;           // this thread's output dimension and item group
@@ -157,6 +160,62 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
   const bool to_ring = (cls == kNormal) && pol == 3 && w_l >= 2 && R > 0;
   const bool to_perm = cls == kSpecial || (cls == kPunct && pol >= 1) || (cls == kNormal && pol == 4);
   const int slot = R > 0 ? p % R : 0;
+
+  // ---- frequent set re-ranked during generation (score != nullptr): the key the window drops
+  // (the ring slot's occupant, position p + 1 - w_l) replaces the cached frequent key of the
+  // lowest score (ties: the larger position) when its own score is larger.  Frequent keys are the
+  // permanent rows of class normal.  The branch is uniform across the workgroup.
+  if (score != nullptr && pol == 3 && R > 0) {
+    const int64_t srow = base_h + slot;
+    const int j_out = pos[srow];
+    if (j_out >= 0) {
+      const size_t cb = (size_t)(hd / Hkv) * n_total;
+      unsigned long long best = ~0ull;                 // (score bits, 0x7fffffff - position): smallest wins
+      int best_row = -1;
+      for (int r = R + tid; r < L; r += NT) {
+        const int jp = pos[base_h + r];
+        if (jp < 0 || jp >= n_total || cls_all[cb + jp] != kNormal) continue;
+        const unsigned long long key = ((unsigned long long)__float_as_uint(score[base_h + r]) << 32) |
+                                       (unsigned)(0x7fffffff - jp);   // scores are >= 0: bits order like values
+        if (key < best) {
+          best = key;
+          best_row = r;
+        }
+      }
+      for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned long long ok = __shfl_xor(best, o);
+        const int orow = __shfl_xor(best_row, o);
+        if (ok < best) {
+          best = ok;
+          best_row = orow;
+        }
+      }
+      if (lane == 0) {
+        s_key[wave] = best;
+        s_row[wave] = best_row;
+      }
+      __syncthreads();
+      best = s_key[0];
+      best_row = s_row[0];
+      for (int w = 1; w < NT / kWave; ++w)
+        if (s_key[w] < best) {
+          best = s_key[w];
+          best_row = s_row[w];
+        }
+      const float s_out = score[srow];
+      if (best != ~0ull && s_out > __uint_as_float((unsigned)(best >> 32))) {
+        const int64_t drow = base_h + best_row;
+        if (tid < D) {                                 // the same threads write the new token's row below
+          Kc[drow * D + tid] = Kc[srow * D + tid];
+          Vc[drow * D + tid] = Vc[srow * D + tid];
+        }
+        if (tid == 0) {
+          pos[drow] = j_out;
+          score[drow] = s_out;
+        }
+      }
+    }
+  }
   int64_t dst = -1;
   if (to_ring) dst = base_h + slot;
   else if (to_perm && L < cap) dst = base_h + L;
@@ -266,6 +325,11 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(
     for (int i = 0; i < NP; ++i) {
       float vv[E];
       V16::cvt(vr[i], vv);
+      // an empty ring slot's row may never have been written: its weight is 0, and so are its
+      // values here (0 * NaN would be NaN)
+      const bool valid = in[i] && pr[i] >= 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) vv[e] = valid ? vv[e] : 0.f;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float pw = fast_exp2(x[i][g] - m[g]);   // 0 for masked rows
@@ -343,8 +407,8 @@ static hipError_t launch_decode_tg(const DecodeArgs& a, hipStream_t st) {
                             : (small ? decode_merge_kernel<T, D, G, false, 512> : decode_merge_kernel<T, D, G, false, 1024>);
     kern<<<dim3(H * G), dim3(small ? 512 : 1024), 0, st>>>(
         (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work_offset, a.work,
-        (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.error_word, a.Hkv, a.w_l,
-        a.p, a.items_per_head, a.chunk_rows, a.total_rows, c);
+        (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.error_word, a.score,
+        a.cls_all, a.n_total, a.Hkv, a.w_l, a.p, a.items_per_head, a.chunk_rows, a.total_rows, c);
     timed_end(st);
     e = hipGetLastError();
   }

@@ -428,7 +428,8 @@ size_t fg_decode_workspace_size(const fg_cache* c) {
 // launch, the cache and next_pos are left unchanged, k_new / v_new / out unused).
 static fg_status decode_launch(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
                                const uint8_t* new_class, float* out, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream, bool partials_only) {
+                               hipStream_t stream, bool partials_only, float* row_score = nullptr,
+                               const uint8_t* token_class = nullptr, int32_t n_total = 0) {
   if (!cache) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
   fg_status s = check_shape(&cache->shape);
   if (s != FG_OK) return s;
@@ -471,6 +472,9 @@ static fg_status decode_launch(fg_cache* cache, const void* q, const void* k_new
   a.items_per_head = (int)cache->items_per_head;
   a.total_rows = cache->total_rows;
   a.partials_only = partials_only;
+  a.score = row_score;
+  a.cls_all = token_class;
+  a.n_total = n_total;
   hipError_t e = fg::launch_decode(a, stream);
   if (e != hipSuccess) return hip_fail(e, "decode step");
   if (!partials_only) cache->next_pos += 1;
@@ -481,6 +485,17 @@ fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, cons
                          const uint8_t* new_class, float* out, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
   return decode_launch(cache, q, k_new, v_new, new_class, out, workspace, workspace_bytes, stream, false);
+}
+
+fg_status fg_decode_step_dynamic(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                 const uint8_t* new_class, const uint8_t* token_class, int32_t n_total,
+                                 float* row_score, float* out, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (!cache) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
+  if (!token_class || !row_score) return fail(FG_ERR_INVALID_ARG, "token_class and row_score must not be NULL");
+  if (n_total < cache->next_pos) return fail(FG_ERR_INVALID_ARG, "token_class must cover every position so far");
+  return decode_launch(cache, q, k_new, v_new, new_class, out, workspace, workspace_bytes, stream, false, row_score,
+                       token_class, n_total);
 }
 
 fg_status fg_decode_partials(const fg_cache* cache, const void* q, void* workspace, size_t workspace_bytes,

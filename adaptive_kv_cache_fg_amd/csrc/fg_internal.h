@@ -140,6 +140,10 @@ struct DecodeArgs {
   int items_per_head;   // partial-state slots per head
   int64_t total_rows;   // cache rows allocated
   bool partials_only;   // skip the merge launch (the cache is left unchanged)
+  // frequent set re-ranked during generation (nullptr: the static policy)
+  float* score;         // [total_rows] cumulative score per cache row
+  const uint8_t* cls_all;   // [B, n_total] class of every position
+  int n_total;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 

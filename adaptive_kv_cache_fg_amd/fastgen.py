@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.fg_profile_attention.argtypes = [sh, pa, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     L.fg_profile_attention.restype = ctypes.c_int
     L.fg_attention.argtypes, L.fg_attention.restype = [sh, P, P, P, P, P, P], ctypes.c_int
+    L.fg_decode_step_dynamic.argtypes = [ca, P, P, P, P, P, I32, P, P, P, S, P]
+    L.fg_decode_step_dynamic.restype = ctypes.c_int
     L.fg_decode_track_init.argtypes, L.fg_decode_track_init.restype = [ca, P, P, P], ctypes.c_int
     L.fg_decode_track_workspace_size.argtypes, L.fg_decode_track_workspace_size.restype = [ca], S
     L.fg_decode_track.argtypes = [ca, P, P, I32, P, P, P, P, S, P]
@@ -286,6 +288,30 @@ class Cache:
         self._workspace(q.device)
         _check(L.fg_decode_step(ctypes.byref(self.c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(new_class),
                                 _ptr(out), _ptr(self._ws), self._ws.numel(), _stream()), "fg_decode_step")
+        return out
+
+    def decode_step_dynamic(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            new_class: Optional[torch.Tensor], token_class: torch.Tensor, row_score: torch.Tensor,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """fg_decode_step_dynamic: decode with the frequent set re-ranked by row_score (see track())."""
+        s = self.shape
+        dt = self.t["k"].dtype
+        _need(q, "q", dt)
+        _need(k_new, "k_new", dt)
+        _need(v_new, "v_new", dt)
+        _need(token_class, "token_class", torch.uint8)
+        _need(row_score, "row_score", torch.float32)
+        if q.shape != (s.batch, s.n_q_heads, s.head_dim) or k_new.shape != (s.batch, s.n_kv_heads, s.head_dim) \
+                or v_new.shape != k_new.shape or token_class.dim() != 2 or token_class.shape[0] != s.batch:
+            raise ValueError("decode input shapes do not match the cache")
+        if new_class is not None:
+            _need(new_class, "new_class", torch.uint8)
+        if out is None:
+            out = torch.empty((s.batch, s.n_q_heads, s.head_dim), dtype=torch.float32, device=q.device)
+        self._workspace(q.device)
+        _check(lib().fg_decode_step_dynamic(ctypes.byref(self.c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(new_class),
+                                            _ptr(token_class), token_class.shape[1], _ptr(row_score), _ptr(out),
+                                            _ptr(self._ws), self._ws.numel(), _stream()), "fg_decode_step_dynamic")
         return out
 
     def decode_partials(self, q: torch.Tensor) -> None:

@@ -311,6 +311,26 @@ fg_status fg_cache_error(const fg_cache* cache, uint32_t* bits_out, hipStream_t 
  *   workspace fg_decode_track_workspace_size(cache) bytes.  Errors: no step
  *   decoded yet (next_pos == n_prompt) or n_total < next_pos -> FG_ERR_INVALID_ARG.
  */
+/*
+ * fg_decode_step_dynamic -- fg_decode_step with the frequent set re-ranked
+ * during generation (heads of policy 3, local + frequent; every other head as
+ * fg_decode_step).  The policy paragraph of Method ranks the frequent set by
+ * cumulative attention; here the ranking continues while generating with a
+ * fixed budget: after the step's output, the key the local window drops
+ * (position p + 1 - w_l, held in the ring slot the new token takes or frees)
+ * replaces the cached frequent key of the lowest row_score (ties: the larger
+ * position) when its own row_score is larger; otherwise it is dropped as in
+ * fg_decode_step.  Frequent keys are the cached rows of class normal outside
+ * the ring.  row_score [total_rows] fp32 as kept by fg_decode_track_init and
+ * fg_decode_track (call fg_decode_track after every step so the scores are
+ * current); token_class [B, n_total] u8 with n_total >= next_pos (classes of
+ * every earlier position).  Other arguments, outputs and errors as fg_decode_step.
+ */
+fg_status fg_decode_step_dynamic(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                 const uint8_t* new_class, const uint8_t* token_class, int32_t n_total,
+                                 float* row_score, float* out, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 fg_status fg_decode_track_init(const fg_cache* cache, const float* cum_score, float* row_score, hipStream_t stream);
 size_t fg_decode_track_workspace_size(const fg_cache* cache);
 fg_status fg_decode_track(const fg_cache* cache, const void* q, const uint8_t* token_class, int32_t n_total,

@@ -453,10 +453,12 @@ class DynamicFrequentHead:
         return LEVEL_SPECIAL if c == TOKEN_SPECIAL else LEVEL_PUNCT if c == TOKEN_PUNCT else \
             (LEVEL_LOCAL if self.w_l >= 1 else LEVEL_FULL)
 
-    def step(self, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, c_new: int, force: Optional[bool] = None):
-        """One generated token.  q [G, d].  ``force`` overrides the replacement decision
-        (None: the rule above).  Returns (out [G, d], kept positions after the step,
-        info {candidate, weakest, margin, replaced})."""
+    def step(self, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, c_new: int, force: Optional[bool] = None,
+             weakest: Optional[int] = None):
+        """One generated token.  q [G, d].  ``force`` overrides the replacement decision and
+        ``weakest`` the frequent key it evicts (None: the rule above; tests use them to follow
+        a decision that rounding could take either way).  Returns (out [G, d], kept positions
+        after the step, info {candidate, weakest, margin, replaced, runner_up_gap})."""
         p = self.n + self.t
         q = np.asarray(q, np.float64)
         new = (np.asarray(k_new, np.float64), np.asarray(v_new, np.float64))
@@ -468,12 +470,15 @@ class DynamicFrequentHead:
             Vs.append(new[1])
         d = q.shape[1]
         out = _masked_softmax_out(q, np.array(Ks).reshape(-1, d), np.array(Vs).reshape(-1, d))
-        info = {"candidate": None, "weakest": None, "margin": None, "replaced": False}
+        info = {"candidate": None, "weakest": None, "margin": None, "replaced": False, "runner_up_gap": None}
         j_out = p + 1 - self.w_l
         if self.w_l >= 2 and j_out in self.kv and j_out not in self.freq and self.cls[j_out] == TOKEN_NORMAL:
             info["candidate"] = j_out
             if self.freq:
-                weakest = min(self.freq, key=lambda j: (self.score[j], -j))
+                ranked = sorted(self.freq, key=lambda j: (self.score[j], -j))
+                if len(ranked) > 1:
+                    info["runner_up_gap"] = self.score[ranked[1]] - self.score[ranked[0]]
+                weakest = ranked[0] if weakest is None else int(weakest)
                 margin = self.score[j_out] - self.score[weakest]
                 replace = margin > 0.0 if force is None else bool(force)
                 info.update(weakest=weakest, margin=margin, replaced=replace)

@@ -150,6 +150,10 @@ def test_decode_track_rejects_bad_arguments():
     assert need >= 4 * 1 * 5 * 4
     assert L.fg_decode_track(ctypes.byref(c), p, p, 18, p, p, p, p, need - 1, None) == 3
     assert L.fg_decode_track_init(ctypes.byref(c), None, p, None) == 1
+    # the dynamic decode step: classes must cover every earlier position, buffers must exist
+    assert L.fg_decode_step_dynamic(ctypes.byref(c), p, p, p, None, p, 17, p, p, p, 1 << 20, None) == 1
+    assert L.fg_decode_step_dynamic(ctypes.byref(c), p, p, p, None, None, 18, p, p, p, 1 << 20, None) == 1
+    assert L.fg_decode_step_dynamic(ctypes.byref(c), p, p, p, None, p, 18, None, p, p, 1 << 20, None) == 1
 
 
 def test_compact_plan_rejects_bad_budgets():

@@ -65,3 +65,27 @@ def test_plan_that_does_not_fit_is_reported():
     fg.compact(K, V, cls, small, 8, max_new_tokens=steps, reuse=cache, check=False)
     cache.decode_step(qs[0], ks[0], vs[0], ncs[0])
     assert cache.error_bits() == 0
+
+
+def test_unwritten_ring_rows_do_not_leak_into_outputs():
+    # rows of empty ring slots are never written by the compaction; fill the cache's buffers with
+    # NaN first, refill in place, and the decode outputs must equal a cache that held zeros
+    steps = 12
+    spec, K, V, cls, qs, ks, vs, ncs, small, big = _setup(steps)
+    print(f"[capacity] NaN-filled buffers, n={spec.seq_len}", flush=True)
+    Q = _upload(syn.make_layer(spec, 0).Q, spec.dtype)
+    prof = fg.profile(Q, K, cls, spec.r_l, spec.r_f, 0.95)
+    assert (prof.policy.cpu().numpy() == 3).any()             # a local head has a ring
+    clean = fg.compact(K, V, cls, prof, spec.n_q_heads, max_new_tokens=steps)
+    dirty = fg.compact(K, V, cls, prof, spec.n_q_heads, max_new_tokens=steps)
+    clean.t["k"].zero_()
+    clean.t["v"].zero_()
+    dirty.t["k"].fill_(float("nan"))
+    dirty.t["v"].fill_(float("nan"))
+    fg.compact(K, V, cls, prof, spec.n_q_heads, max_new_tokens=steps, reuse=clean)
+    fg.compact(K, V, cls, prof, spec.n_q_heads, max_new_tokens=steps, reuse=dirty)
+    for t in range(steps):
+        a = clean.decode_step(qs[t], ks[t], vs[t], ncs[t])
+        b = dirty.decode_step(qs[t], ks[t], vs[t], ncs[t])
+        assert torch.isfinite(b).all(), t
+        assert torch.equal(a, b), t

@@ -1,0 +1,141 @@
+"""GPU parity of decoding with the frequent set re-ranked during generation
+(fg_decode_step_dynamic + fg_decode_track) against the oracle's
+DynamicFrequentHead, step by step: outputs (decode tolerance), the kept
+positions after every step (exact), and the row scores at the end (tracking
+tolerance).  A replacement decision whose oracle margin, or whose choice of the
+weakest frequent key, lies within rounding of a tie follows the GPU's choice
+(read from its cache), as flagged heads do elsewhere."""
+import numpy as np
+import pytest
+import torch
+
+from adaptive_kv_cache_fg_amd import fastgen as fg
+from oracle import fastgen_ref as ref
+from synth import inputs as syn
+
+pytestmark = pytest.mark.gpu
+
+# window of a score comparison that fp32 accumulation can flip: the score tolerance below
+def _near(a, b, steps_done, G):
+    return abs(a - b) <= 2e-4 * max(abs(a), abs(b)) + 1e-6 * G * (steps_done + 1)
+
+
+@pytest.fixture(scope="module")
+def gpl():
+    import gpu_parity_lib
+    return gpu_parity_lib
+
+
+def _run(gpl, spec, T, steps, score_scale):
+    gpl.log(f"[dynamic] n={spec.seq_len} d={spec.head_dim} {spec.dtype} Hq={spec.n_q_heads} Hkv={spec.n_kv_heads} "
+            f"B={spec.batch} T={T} steps={steps} scale={score_scale}")
+    li = syn.make_layer(spec)
+    ds = syn.make_decode_stream(spec, steps=steps)
+    B, Hq, n, d = li.Q.shape
+    Hkv = li.K.shape[1]
+    G = Hq // Hkv
+    Qd, Kd, Vd = (gpl.upload(x, spec.dtype) for x in (li.Q, li.K, li.V))
+    cls = torch.from_numpy(li.token_class).cuda()
+    cls_all_h = np.ascontiguousarray(np.concatenate([li.token_class, ds.new_class.T], axis=1))
+    cls_all = torch.from_numpy(cls_all_h).cuda()
+    prof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T)
+    cache = fg.compact(Kd, Vd, cls, prof, Hq, max_new_tokens=steps, max_new_kept=steps)
+    score = cache.track_init(prof)
+    score *= score_scale                                  # the caller's choice of starting scores
+    qs, ks, vs = (gpl.upload(x, spec.dtype) for x in (ds.q, ds.k, ds.v))
+    ncs = torch.from_numpy(np.ascontiguousarray(ds.new_class)).cuda()
+    torch.cuda.synchronize()
+    pol = prof.policy.cpu().numpy()
+    F = prof.frequent()
+    cum = prof.cum.cpu().numpy().astype(np.float64) * np.float64(np.float32(score_scale))
+    w_l = ref.budgets(n, spec.r_l, spec.r_f)[1]
+    heads = {(b, h): ref.DynamicFrequentHead(li.K[b, h], li.V[b, h], li.token_class[b], F[b, h], w_l, cum[b, h])
+             for b in range(B) for h in range(Hkv) if pol[b, h] == 3}
+    assert heads, "no head took the local + frequent policy"
+    tol = gpl.DEC_TOL[spec.dtype]
+    replaced = forced = 0
+    for t in range(steps):
+        out = cache.decode_step_dynamic(qs[t], ks[t], vs[t], ncs[t], cls_all, score)
+        cache.track(qs[t], cls_all, prof.freq_mask, score)
+        out_g = out.cpu().numpy().astype(np.float64)
+        kept_g = cache.kept_positions()
+        for (b, h), head in heads.items():
+            hd = b * Hkv + h
+            snap = {j: head.score[j] for j in head.freq}
+            j_out = n + t + 1 - w_l
+            cand = w_l >= 2 and j_out in head.kv and j_out not in head.freq and head.cls[j_out] == 0
+            force = weakest = None
+            if cand and snap:
+                ranked = sorted(snap, key=lambda j: (snap[j], -j))
+                s_w = snap[ranked[0]]
+                gpu_kept = set(kept_g[hd].tolist())
+                near_margin = _near(head.score[j_out], s_w, t, G)
+                near_weakest = len(ranked) > 1 and _near(snap[ranked[1]], s_w, t, G)
+                if near_margin or near_weakest:
+                    forced += 1
+                    force = j_out in gpu_kept
+                    if force:
+                        gone = [j for j in ranked if j not in gpu_kept]
+                        assert len(gone) == 1, (b, h, t, gone)
+                        weakest = gone[0]
+            o, kept, info = head.step(ds.q[t, b, h * G:(h + 1) * G], ds.k[t, b, h], ds.v[t, b, h],
+                                      int(ds.new_class[t, b]), force=force, weakest=weakest)
+            replaced += bool(info["replaced"])
+            want = o
+            got = out_g[b, h * G:(h + 1) * G]
+            assert np.max(np.abs(got - want)) <= tol * max(1e-30, np.max(np.abs(want))), (b, h, t)
+            assert np.array_equal(kept_g[hd], kept), (b, h, t, sorted(set(kept_g[hd]) ^ set(kept)))
+    # the scores of the final caches
+    sc = score.cpu().numpy().astype(np.float64)
+    ro = cache.t["row_offset"].cpu().numpy()
+    ln = cache.t["len"].cpu().numpy()
+    pos = cache.t["pos"].cpu().numpy()
+    for (b, h), head in heads.items():
+        hd = b * Hkv + h
+        rows = slice(ro[hd], ro[hd] + ln[hd])
+        got = {int(j): float(v) for j, v in zip(pos[rows], sc[rows]) if j >= 0}
+        assert sorted(got) == sorted(head.score)
+        for j, v in head.score.items():
+            assert abs(got[j] - v) <= 2e-4 * abs(v) + 1e-6 * G * steps + 1e-6 * abs(cum[b, h]).max(), (b, h, j)
+    assert cache.error_bits() == 0
+    return replaced, forced
+
+
+# scale: factor on the prompt's scores at the start (0: ranking by decode-time attention alone,
+# where keys leaving the window displace frequent keys at almost every step)
+@pytest.mark.parametrize("n,d,dtype,hq,hkv,batch,scale", [
+    (400, 128, "bf16", 8, 4, 2, 0.0),
+    (300, 64, "f32", 4, 4, 1, 0.0),
+    (520, 128, "bf16", 8, 2, 1, 0.02),
+    (700, 128, "bf16", 16, 4, 1, 1.0),
+])
+def test_dynamic_frequent_matches_oracle(gpl, n, d, dtype, hq, hkv, batch, scale):
+    spec = syn.custom_spec(syn.CONFIGS[1], seq_len=n, head_dim=d, dtype=dtype, n_q_heads=hq, n_kv_heads=hkv,
+                           batch=batch, mix="fixed", fixed_types=("local",) * hkv)
+    replaced, forced = _run(gpl, spec, 0.9, 40, scale)
+    gpl.log(f"[dynamic] replacements {replaced}, followed near ties {forced}")
+    if scale == 0.0:
+        assert replaced > 0, "the case exercises no replacement"
+
+
+def test_dynamic_without_policy3_heads_is_the_static_step(gpl):
+    # special and punct heads: the dynamic step equals fg_decode_step bit for bit
+    spec = syn.custom_spec(syn.CONFIGS[1], seq_len=256, head_dim=128, n_q_heads=4, n_kv_heads=2, batch=1,
+                           mix="fixed", fixed_types=("special", "punct"))
+    li = syn.make_layer(spec)
+    ds = syn.make_decode_stream(spec, steps=8)
+    Qd, Kd, Vd = (gpl.upload(x, "bf16") for x in (li.Q, li.K, li.V))
+    cls = torch.from_numpy(li.token_class).cuda()
+    prof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, 0.95)
+    a = fg.compact(Kd, Vd, cls, prof, 4, max_new_tokens=8)
+    b_ = fg.compact(Kd, Vd, cls, prof, 4, max_new_tokens=8)
+    score = b_.track_init(prof)
+    cls_all = torch.from_numpy(np.ascontiguousarray(np.concatenate([li.token_class, ds.new_class.T], 1))).cuda()
+    qs, ks, vs = (gpl.upload(x, "bf16") for x in (ds.q, ds.k, ds.v))
+    ncs = torch.from_numpy(np.ascontiguousarray(ds.new_class)).cuda()
+    assert all(int(x) != 3 for x in prof.policy.cpu().numpy().reshape(-1))
+    for t in range(8):
+        o1 = a.decode_step(qs[t], ks[t], vs[t], ncs[t])
+        o2 = b_.decode_step_dynamic(qs[t], ks[t], vs[t], ncs[t], cls_all, score)
+        assert torch.equal(o1, o2)
+    assert [x.tolist() for x in a.kept_positions()] == [x.tolist() for x in b_.kept_positions()]
