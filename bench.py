@@ -251,6 +251,36 @@ def decode_stability(torch, fg, Kd, Vd, cls, prof, qs, ks, vs, ncs, spec, T) -> 
     rows = float(B * Hkv * n + B * Hkv * (steps + 1) / 2.0)
     track_bytes = rows * (2 * d * e + 12)
     avg_us = 1e3 * float(np.mean(track_ms))
+
+    # the frequent set re-ranked during generation (local + frequent heads) against the static
+    # policy: the same stream through two adaptive caches, one decoded with fg_decode_step_dynamic
+    # (scores tracked after every step), one with fg_decode_step
+    dyn = fg.compact(Kd, Vd, cls, prof, Hq, max_new_tokens=steps, max_new_kept=steps)
+    sta = fg.compact(Kd, Vd, cls, prof, Hq, max_new_tokens=steps, max_new_kept=steps)
+    dscore = dyn.track_init(prof)
+    out2 = torch.empty_like(out)
+    torch.cuda.synchronize()
+    fg.timing_read()
+    fg.timing_enable(True)
+    for t in range(steps):
+        dyn.decode_step_dynamic(qs[t], ks[t], vs[t], ncs[t], cls_all, dscore, out=out)
+        dyn.track(qs[t], cls_all, prof.freq_mask, dscore)
+        sta.decode_step(qs[t], ks[t], vs[t], ncs[t], out=out2)
+    torch.cuda.synchronize()
+    fg.timing_enable(False)
+    recs = fg.timing_read()
+    merges = [ms for k, ms in recs if k == "decode_merge"]       # dynamic and static alternate
+    kd, ks_ = dyn.kept_positions(), sta.kept_positions()
+    moved = int(sum(len(set(a.tolist()) - set(b.tolist())) for a, b in zip(kd, ks_)))
+    n_pol3 = int(np.sum(pol == 3))
+    dynamic = {
+        "local_frequent_heads": n_pol3,
+        "keys_kept_that_the_static_policy_dropped": moved,
+        "merge_us_dynamic": 1e3 * float(np.mean(merges[0::2])) if merges else None,
+        "merge_us_static": 1e3 * float(np.mean(merges[1::2])) if merges else None,
+        "note": "adaptive caches; per-launch events; the dynamic merge launch also scans the permanent rows of "
+                "each local + frequent head for the weakest frequent key",
+    }
     return {
         "steps": steps,
         "tv_distance_mean_share": {"mean": float(tv_mean_share.mean()), "max": float(tv_mean_share.max())},
@@ -258,6 +288,7 @@ def decode_stability(torch, fg, Kd, Vd, cls, prof, qs, ks, vs, ncs, spec, T) -> 
         "prompt_policy_retained_ge_T": float(np.mean(retained >= T - 1e-6)),
         "prompt_policy_retained_min": float(retained.min()),
         "frequent_set_overlap_after_generation": {"mean": float(np.mean(overlap)), "min": float(np.min(overlap))},
+        "dynamic_frequent_set": dynamic,
         "track_kernel": {"avg_us": avg_us, "algorithmic_bytes": track_bytes,
                          "achieved": track_bytes / (avg_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": track_bytes / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
