@@ -183,7 +183,8 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
   static_assert(CHUNK % kWave == 0 && CHUNK <= 1024, "one position per thread, whole waves");
   __shared__ int red[kWaves];
   __shared__ int wcnt[kWaves], wrows[kWaves];
-  __shared__ int src_j[CHUNK], dst_r[CHUNK];
+  __shared__ int src_j[CHUNK], dst_r[CHUNK], zero_r[CHUNK];
+  __shared__ int wzero[kWaves];
 
   const int hd = blockIdx.x / nch, ch = blockIdx.x % nch, b = hd / Hkv;
   const int nw = (n + 31) / 32;
@@ -215,15 +216,18 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
   const bool win = valid && R > 0 && j >= n - R;          // inside the local window of row n
   const bool rf = win && !pf;
   const bool any = pf || rf;
-  const unsigned long long bp = __ballot(pf), ba = __ballot(any);
-  if (lane == 0) { wcnt[wave] = __popcll(bp); wrows[wave] = __popcll(ba); }
+  const bool zs = win && pf;                               // its ring slot stays empty
+  const unsigned long long bp = __ballot(pf), ba = __ballot(any), bz = __ballot(zs);
+  if (lane == 0) { wcnt[wave] = __popcll(bp); wrows[wave] = __popcll(ba); wzero[wave] = __popcll(bz); }
   __syncthreads();
-  int pbefore = 0, abefore = 0, ptotal = 0, atotal = 0;
+  int pbefore = 0, abefore = 0, ptotal = 0, atotal = 0, zbefore = 0, ztotal = 0;
   for (int w = 0; w < kWaves; ++w) {
     pbefore += (w < wave) ? wcnt[w] : 0;
     abefore += (w < wave) ? wrows[w] : 0;
+    zbefore += (w < wave) ? wzero[w] : 0;
     ptotal += wcnt[w];
     atotal += wrows[w];
+    ztotal += wzero[w];
   }
   const unsigned long long below = (1ull << lane) - 1ull;
   if (any) {
@@ -233,11 +237,21 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
     dst_r[e] = (int)(dst - off);
     pos[dst] = j;
   }
-  if (win && pf) pos[off + (j % R)] = -1;                 // its slot stays empty
+  if (zs) {                                               // its slot stays empty; its row is zeroed below
+    pos[off + (j % R)] = -1;
+    zero_r[zbefore + __popcll(bz & below)] = j % R;
+  }
   if (ch == 0 && R > 0) {                                  // window positions before the prompt start
     for (int t = tid; t < R; t += blockDim.x) {
       const int jj = n - R + t;
-      if (jj < 0) pos[off + (((jj % R) + R) % R)] = -1;
+      if (jj < 0) {
+        const int64_t zr = off + (((jj % R) + R) % R);
+        pos[zr] = -1;
+        for (int q = 0; q < kCPR; ++q) {
+          reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Kc) + zr * D * sizeof(T))[q] = make_uint4(0u, 0u, 0u, 0u);
+          reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Vc) + zr * D * sizeof(T))[q] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
     }
   }
   if (ch == nch - 1 && tid == 0) len[hd] = R + before + ptotal;
@@ -245,6 +259,14 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
 
   const T* Ks = K + (size_t)hd * n * D;
   const T* Vs = V + (size_t)hd * n * D;
+  // rows of empty ring slots get zeros: the decode reads every row in use and weights these by 0
+  // (values that were never written could hold NaN bit patterns, and 0 * NaN is NaN)
+  for (int idx = tid; idx < ztotal * kCPR; idx += blockDim.x) {
+    const int e = idx / kCPR, q = idx % kCPR;
+    const size_t d = (size_t)(off + zero_r[e]) * D * sizeof(T) + q * 16;
+    *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Kc) + d) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Vc) + d) = make_uint4(0u, 0u, 0u, 0u);
+  }
   for (int idx = tid; idx < atotal * kCPR; idx += blockDim.x) {
     const int e = idx / kCPR, q = idx % kCPR;
     const size_t s = (size_t)src_j[e] * D * sizeof(T) + q * 16;

@@ -325,11 +325,6 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(
     for (int i = 0; i < NP; ++i) {
       float vv[E];
       V16::cvt(vr[i], vv);
-      // an empty ring slot's row may never have been written: its weight is 0, and so are its
-      // values here (0 * NaN would be NaN)
-      const bool valid = in[i] && pr[i] >= 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) vv[e] = valid ? vv[e] : 0.f;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float pw = fast_exp2(x[i][g] - m[g]);   // 0 for masked rows
