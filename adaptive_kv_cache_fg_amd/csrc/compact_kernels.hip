@@ -10,9 +10,9 @@
 // so a new token always lands in the slot of the key leaving the window.
 //
 // Kernels: a per-head count (plan), one scan over heads for row and work-item
-// offsets, a gather over (head, 256-position chunk) whose workgroups rank
-// their kept keys with a wave ballot prefix and copy rows with 16-byte loads,
-// and the per-head list of decode work items.
+// offsets, and a gather over (head, 256-position chunk) whose workgroups rank
+// their kept keys with a wave ballot prefix and copy rows with 16-byte loads;
+// the last chunk of a head also writes the head's decode work items.
 #include "fg_common.h"
 #include "fg_internal.h"
 
@@ -98,8 +98,6 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ c
   }
 }
 
-// Exclusive prefix sums over heads: rows and decode work items, and the largest
-// item count of a head.  One workgroup.
 // Exclusive prefix sums of the heads' rows and decode work items, one
 // workgroup: each thread sums a contiguous segment of heads, the segment totals
 // are scanned with wave shuffles and one LDS exchange between the waves, then
@@ -177,7 +175,9 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
                                                      const int64_t* __restrict__ row_offset, const int32_t* __restrict__ ring,
                                                      int Hkv, int n, int nch, T* __restrict__ Kc, T* __restrict__ Vc,
                                                      int32_t* __restrict__ pos, int32_t* __restrict__ len,
-                                                     uint32_t* __restrict__ error_word, int64_t total_rows) {
+                                                     uint32_t* __restrict__ error_word, int64_t total_rows,
+                                                     const int64_t* __restrict__ work_offset, int chunk,
+                                                     int32_t* __restrict__ work, int64_t n_work_cap, int S_cap) {
   constexpr int kCPR = D * (int)sizeof(T) / 16;           // 16-byte chunks per row
   constexpr int kWaves = CHUNK / kWave;
   static_assert(CHUNK % kWave == 0 && CHUNK <= 1024, "one position per thread, whole waves");
@@ -194,9 +194,43 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
   const int R = ring[hd];
   const int64_t off = row_offset[hd];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (blockIdx.x == 0 && tid == 0) *error_word = 0u;
-  if (row_offset[hd + 1] > total_rows) {                  // the plan does not fit the cache: head left empty
-    if (ch == nch - 1 && tid == 0) len[hd] = 0;           // (the work list records the error)
+  const int64_t w0 = work_offset[hd], w1 = work_offset[hd + 1];
+  const bool fits_rows = row_offset[hd + 1] <= total_rows;
+  const bool fits = fits_rows && w1 <= n_work_cap && w1 - w0 <= S_cap;
+  // Decode work items of this head: chunks of its capacity, each (head, first row, first absolute
+  // row, rows in use), written by the head's last chunk once its rows in use are known; the decode
+  // keeps the counts current on appends.  A head whose plan exceeds the cache's capacities gets
+  // empty items (head -1), as do the items past the plan's total.
+  auto write_items = [&](int L, bool real) {
+    for (int64_t w = w0 + tid; w < min(w1, n_work_cap); w += blockDim.x) {
+      const int start = (int)((w - w0) * chunk);
+      work[4 * w] = real ? hd : -1;
+      work[4 * w + 1] = real ? start : 0;
+      work[4 * w + 2] = real ? (int32_t)(off + start) : 0;
+      work[4 * w + 3] = real ? min(chunk, max(0, L - start)) : 0;
+    }
+  };
+  if (blockIdx.x == 0) {                                   // one writer of the error word (uniform branch)
+    const int H = (int)(gridDim.x / nch);
+    int bad = 0;
+    for (int h = tid; h < H; h += blockDim.x) {
+      const int64_t a0 = work_offset[h], a1 = work_offset[h + 1];
+      bad |= (row_offset[h + 1] > total_rows || a1 > n_work_cap || a1 - a0 > S_cap) ? 1 : 0;
+    }
+    bad = block_sum_i(bad, red);
+    if (tid == 0) *error_word = bad ? 2u : 0u;             // bit 2: a plan that does not fit; bit 1 cleared
+    for (int64_t w = work_offset[H] + tid; w < n_work_cap; w += blockDim.x) {   // items past the plan's total
+      work[4 * w] = -1;
+      work[4 * w + 1] = 0;
+      work[4 * w + 2] = 0;
+      work[4 * w + 3] = 0;
+    }
+  }
+  if (!fits_rows) {                                        // the plan does not fit the cache: head left empty
+    if (ch == nch - 1) {
+      if (tid == 0) len[hd] = 0;
+      write_items(0, false);
+    }
     return;
   }
 
@@ -254,7 +288,10 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
       }
     }
   }
-  if (ch == nch - 1 && tid == 0) len[hd] = R + before + ptotal;
+  if (ch == nch - 1) {
+    if (tid == 0) len[hd] = R + before + ptotal;
+    write_items(R + before + ptotal, fits);
+  }
   __syncthreads();
 
   const T* Ks = K + (size_t)hd * n * D;
@@ -275,42 +312,6 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
         *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(Ks) + s);
     *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Vc) + d) =
         *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(Vs) + s);
-  }
-}
-
-// Decode work items of one head: chunks of its capacity, each (head, first
-// row, first absolute row, rows in use).  The rows-in-use count of an item is
-// kept current by the decode step's appends.  The cache's buffers are
-// capacities (n_work_cap items, S_cap items per head, total_rows rows): a plan
-// that exceeds them sets bit 2 of error_word, and what does not fit becomes
-// empty items (head -1), as do the items past the plan's total, so a decode
-// grid of n_work_cap items stays valid.
-__global__ __launch_bounds__(256) void worklist_kernel(const int64_t* __restrict__ work_offset,
-                                                       const int64_t* __restrict__ row_offset,
-                                                       const int32_t* __restrict__ len, int chunk,
-                                                       int32_t* __restrict__ work, int64_t n_work_cap, int S_cap,
-                                                       int64_t total_rows, uint32_t* __restrict__ error_word) {
-  const int hd = blockIdx.x, H = gridDim.x;
-  const int64_t w0 = work_offset[hd], w1 = work_offset[hd + 1];
-  const int64_t base = row_offset[hd];
-  const bool fits = row_offset[hd + 1] <= total_rows && w1 <= n_work_cap && w1 - w0 <= S_cap;
-  if (threadIdx.x == 0 && !fits) atomicOr(error_word, 2u);
-  const int L = len[hd];
-  for (int64_t w = w0 + threadIdx.x; w < min(w1, n_work_cap); w += blockDim.x) {
-    const int start = (int)((w - w0) * chunk);
-    const bool real = fits;
-    work[4 * w] = real ? hd : -1;
-    work[4 * w + 1] = real ? start : 0;
-    work[4 * w + 2] = real ? (int32_t)(base + start) : 0;
-    work[4 * w + 3] = real ? min(chunk, max(0, L - start)) : 0;
-  }
-  if (hd == 0) {                                           // items past the plan's total
-    for (int64_t w = work_offset[H] + threadIdx.x; w < n_work_cap; w += blockDim.x) {
-      work[4 * w] = -1;
-      work[4 * w + 1] = 0;
-      work[4 * w + 2] = 0;
-      work[4 * w + 3] = 0;
-    }
   }
 }
 
@@ -336,13 +337,8 @@ static hipError_t launch_gather_t(const GatherArgs& a, hipStream_t st) {
   timed_begin(FG_K_GATHER, st);
   gather_kernel<T, D, kPosChunk><<<dim3(H * nch), dim3(kPosChunk), 0, st>>>(
       (const T*)a.K, (const T*)a.V, a.cls, a.policy, a.fmask, a.row_offset, a.ring, a.Hkv, a.n, nch, (T*)a.Kc,
-      (T*)a.Vc, a.pos, a.len, a.error_word, a.total_rows);
-  timed_end(st);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  timed_begin(FG_K_WORKLIST, st);
-  worklist_kernel<<<dim3(H), dim3(256), 0, st>>>(a.work_offset, a.row_offset, a.len, a.chunk_rows, a.work, a.n_work,
-                                                 a.items_per_head, a.total_rows, a.error_word);
+      (T*)a.Vc, a.pos, a.len, a.error_word, a.total_rows, a.work_offset, a.chunk_rows, a.work, a.n_work,
+      a.items_per_head);
   timed_end(st);
   return hipGetLastError();
 }

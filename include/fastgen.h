@@ -348,8 +348,9 @@ const char* fg_last_error(void);
  * milliseconds) accumulated since the last read. */
 enum {
   FG_K_ROWSTATS = 0, FG_K_COLSUMS = 1, FG_K_SELECT = 2, FG_K_PLAN = 3, FG_K_SCAN = 4,
-  FG_K_GATHER = 5, FG_K_WORKLIST = 6, FG_K_DECODE = 7, FG_K_DECODE_MERGE = 8, FG_K_ATTENTION = 9,
-  FG_K_TRACK = 10, FG_K_COUNT = 11
+  FG_K_GATHER = 5,     /* also writes the decode work list */
+  FG_K_WORKLIST = 6,   /* reserved: no separate launch */
+  FG_K_DECODE = 7, FG_K_DECODE_MERGE = 8, FG_K_ATTENTION = 9, FG_K_TRACK = 10, FG_K_COUNT = 11
 };
 void fg_kernel_timing_enable(int enable);
 int32_t fg_kernel_timing_read(int32_t* kernel_ids, float* ms, int32_t max);
