@@ -37,39 +37,62 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   return t;   // valid in thread 0
 }
 
+// VPT > 0: each thread holds the scores (and band sums) of keys tid + k * kSelThreads,
+// k < VPT, in registers for every pass (n <= VPT * kSelThreads); VPT = 0: every pass
+// reads them from memory (long prompts).
+template <int VPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__ cum, float* __restrict__ band,
                                                              const float2* __restrict__ cs_part, int rchunk,
                                                              const uint8_t* __restrict__ cls, int Hkv, int n, int G,
                                                              int k_f, double T, uint32_t* __restrict__ fmask,
                                                              float* __restrict__ recovery, uint8_t* __restrict__ policy) {
+  constexpr int NV = VPT > 0 ? VPT : 1;
   __shared__ unsigned hist[256];
   __shared__ unsigned s_sel, s_rem;
   __shared__ int wave_cnt[kSelThreads / 64];
   __shared__ double red[kSelThreads / 64];
 
   const int bh = blockIdx.x, b = bh / Hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n_waves = blockDim.x >> 6;
+  const int n_it = (n + kSelThreads - 1) / kSelThreads;   // key batches of kSelThreads
+  float cv[NV], bv[NV];
   if (cs_part) {
     // the column sweep ran in row chunks: add each key's partial sums in chunk order
     const int nbh = gridDim.x;
-    for (int j = threadIdx.x; j < n; j += blockDim.x) {
-      const int nc = (n - (j / kSweepKeysPerWG) * kSweepKeysPerWG + rchunk - 1) / rchunk;
+    for (int it = 0; it < (VPT > 0 ? VPT : n_it); ++it) {
+      const int j = it * kSelThreads + tid;
       float cs = 0.f, bs = 0.f;
-      for (int ch = 0; ch < nc; ++ch) {
-        const float2 v = cs_part[((size_t)ch * nbh + bh) * n + j];
-        cs += v.x;
-        bs += v.y;
+      if (j < n) {
+        const int nc = (n - (j / kSweepKeysPerWG) * kSweepKeysPerWG + rchunk - 1) / rchunk;
+        for (int ch = 0; ch < nc; ++ch) {
+          const float2 v = cs_part[((size_t)ch * nbh + bh) * n + j];
+          cs += v.x;
+          bs += v.y;
+        }
+        cum[(size_t)bh * n + j] = cs;
+        band[(size_t)bh * n + j] = bs;
       }
-      cum[(size_t)bh * n + j] = cs;
-      band[(size_t)bh * n + j] = bs;
+      if (VPT > 0) {
+        cv[it < NV ? it : 0] = cs;
+        bv[it < NV ? it : 0] = bs;
+      }
     }
-    __syncthreads();
+    if (VPT == 0) __syncthreads();
+  } else if (VPT > 0) {
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int j = it * kSelThreads + tid;
+      cv[it] = j < n ? cum[(size_t)bh * n + j] : 0.f;
+      bv[it] = j < n ? band[(size_t)bh * n + j] : 0.f;
+    }
   }
   const float* cu = cum + (size_t)bh * n;
   const float* bd = band + (size_t)bh * n;
   const uint8_t* cl = cls + (size_t)b * n;
   const int nw = (n + 31) / 32;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n_waves = blockDim.x >> 6;
+  auto score_of = [&](int it, int j) -> float { return VPT > 0 ? cv[it < NV ? it : 0] : cu[j]; };
+  auto band_of = [&](int it, int j) -> float { return VPT > 0 ? bv[it < NV ? it : 0] : bd[j]; };
 
   // mode 0: nothing selected, 1: everything, 2: threshold + ties
   const int mode = k_f <= 0 ? 0 : (k_f >= n ? 1 : 2);
@@ -82,9 +105,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
       const int shift = 24 - 8 * pass;
       for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
       __syncthreads();
-      for (int j = tid; j < n; j += blockDim.x) {
-        const uint32_t u = __float_as_uint(cu[j]);
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+#pragma unroll
+      for (int it = 0; it < (VPT > 0 ? VPT : 1); ++it) {
+        if (VPT > 0) {
+          const int j = it * kSelThreads + tid;
+          const uint32_t u = __float_as_uint(score_of(it, j));
+          if (j < n && (u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        } else {
+          for (int j = tid; j < n; j += blockDim.x) {
+            const uint32_t u = __float_as_uint(cu[j]);
+            if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+          }
+        }
       }
       __syncthreads();
       if (wave == 0) {
@@ -121,40 +153,43 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
 
   double m_s = 0.0, m_p = 0.0, m_f = 0.0, m_b = 0.0;
   int run = 0;                                   // equal-to-threshold keys seen at lower indices
-  for (int base = 0; base < n; base += blockDim.x) {
-    const int j = base + tid;
-    const bool valid = j < n;
-    const float v = valid ? cu[j] : 0.f;
-    const uint32_t u = __float_as_uint(v);
-    bool sel = (mode == 1) && valid;
-    if (mode == 2) {
-      const bool eq = valid && u == thr;
-      const unsigned long long bal = __ballot(eq);
-      if (lane == 0) wave_cnt[wave] = __popcll(bal);
-      __syncthreads();
-      int before = 0, total = 0;
-      for (int w = 0; w < n_waves; ++w) {
-        const int cw = wave_cnt[w];
-        before += (w < wave) ? cw : 0;
-        total += cw;
+#pragma unroll
+  for (int it = 0; it < (VPT > 0 ? VPT : 1); ++it) {
+    for (int base = it * kSelThreads; base < (VPT > 0 ? min(n, (it + 1) * kSelThreads) : n); base += blockDim.x) {
+      const int j = base + tid;
+      const bool valid = j < n;
+      const float v = valid ? score_of(it, j) : 0.f;
+      const uint32_t u = __float_as_uint(v);
+      bool sel = (mode == 1) && valid;
+      if (mode == 2) {
+        const bool eq = valid && u == thr;
+        const unsigned long long bal = __ballot(eq);
+        if (lane == 0) wave_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int before = 0, total = 0;
+        for (int w = 0; w < n_waves; ++w) {
+          const int cw = wave_cnt[w];
+          before += (w < wave) ? cw : 0;
+          total += cw;
+        }
+        const int rank = run + before + __popcll(bal & ((1ull << lane) - 1ull));
+        sel = (valid && u > thr) || (eq && rank < take_eq);
+        run += total;
+        __syncthreads();
       }
-      const int rank = run + before + __popcll(bal & ((1ull << lane) - 1ull));
-      sel = (valid && u > thr) || (eq && rank < take_eq);
-      run += total;
-      __syncthreads();
-    }
-    const unsigned long long sb = __ballot(sel);
-    if (lane == 0) {
-      const int w0 = (base + wave * 64) / 32;
-      if (w0 < nw) fmask[(size_t)bh * nw + w0] = (uint32_t)(sb & 0xFFFFFFFFull);
-      if (w0 + 1 < nw) fmask[(size_t)bh * nw + w0 + 1] = (uint32_t)(sb >> 32);
-    }
-    if (valid) {
-      const uint8_t c = cl[j];
-      if (c == kSpecial) m_s += v;
-      else if (c == kPunct) m_p += v;
-      else if (sel) m_f += v;
-      else m_b += bd[j];
+      const unsigned long long sb = __ballot(sel);
+      if (lane == 0) {
+        const int w0 = (base + wave * 64) / 32;
+        if (w0 < nw) fmask[(size_t)bh * nw + w0] = (uint32_t)(sb & 0xFFFFFFFFull);
+        if (w0 + 1 < nw) fmask[(size_t)bh * nw + w0 + 1] = (uint32_t)(sb >> 32);
+      }
+      if (valid) {
+        const uint8_t c = cl[j];
+        if (c == kSpecial) m_s += v;
+        else if (c == kPunct) m_p += v;
+        else if (sel) m_f += v;
+        else m_b += band_of(it, j);
+      }
     }
   }
   m_s = block_sum(m_s, red);
@@ -179,9 +214,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
 
 hipError_t launch_select(const ProfileArgs& a, hipStream_t st) {
   timed_begin(FG_K_SELECT, st);
-  select_kernel<<<dim3(a.B * a.Hkv), dim3(kSelThreads), 0, st>>>(a.cum, a.band, a.cs_part, a.rchunk, a.cls, a.Hkv,
-                                                                  a.n, a.Hq / a.Hkv, a.k_f, a.T, a.fmask,
-                                                                  a.recovery, a.policy);
+  const int per = (a.n + kSelThreads - 1) / kSelThreads;
+  auto kern = per <= 1 ? select_kernel<1> : per <= 2 ? select_kernel<2> : per <= 4 ? select_kernel<4> :
+              per <= 8 ? select_kernel<8> : per <= 16 ? select_kernel<16> : per <= 32 ? select_kernel<32> :
+              select_kernel<0>;
+  kern<<<dim3(a.B * a.Hkv), dim3(kSelThreads), 0, st>>>(a.cum, a.band, a.cs_part, a.rchunk, a.cls, a.Hkv, a.n,
+                                                         a.Hq / a.Hkv, a.k_f, a.T, a.fmask, a.recovery, a.policy);
   timed_end(st);
   return hipGetLastError();
 }
