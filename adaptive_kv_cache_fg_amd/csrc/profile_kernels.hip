@@ -246,11 +246,13 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   LdsLoader<T, D, kRowTile> ldr;
   ldr.init(wave, lane);
   float lpre = 0.f;
-  // tiles run over (query head g, row tile) with the row tile fastest; the
-  // next tile to issue is tracked incrementally (no integer division per tile)
+  // tiles run over (query head g, row tile) with the row tile fastest, from the
+  // last rows down: every key block's rows end at n, so workgroups of one head
+  // running side by side stream the same Q tiles (shared through L2).  The next
+  // tile to issue is tracked incrementally (no integer division per tile).
   int ig = 0, it = 0;
   auto issue = [&](int u) {                                      // tile u = (ig, it) of the sequence
-    const int i0 = i_begin + it * kRowTile;
+    const int i0 = i_begin + (ntiles - 1 - it) * kRowTile;   // last rows first (see below)
     const size_t qh = (size_t)b * Hq + (size_t)h * G + ig;
     ldr.issue(Q + qh * n * D, i0, n, qtile[u & 1], wave);
     if (threadIdx.x < kRowTile) lpre = (i0 + (int)threadIdx.x < i_end) ? lse2[qh * n + i0 + threadIdx.x] : INFINITY;
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   int t_cur = 0;                                                 // row tile of tile u
   for (int u = 0; u < total; ++u) {
     if (u + 1 < total) issue(u + 1);
-    const int i0 = i_begin + t_cur * kRowTile;
+    const int i0 = i_begin + (ntiles - 1 - t_cur) * kRowTile;
     const unsigned char* qt = qtile[u & 1];
     const float* lt = lse_t[u & 1];
     if (i0 + kRowTile - 1 >= j0 && i0 < i_end) {                // wave-uniform: some pair is causal
