@@ -19,6 +19,7 @@
 namespace fg {
 
 constexpr int kPosChunk = 256;
+constexpr int kCopyBatch = 4;     // 16-byte chunks of K and of V per thread in flight in the gather's copy
 
 __device__ __forceinline__ bool fbit(const uint32_t* fm, int j) { return (fm[j >> 5] >> (j & 31)) & 1u; }
 
@@ -304,14 +305,30 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
     *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Kc) + d) = make_uint4(0u, 0u, 0u, 0u);
     *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Vc) + d) = make_uint4(0u, 0u, 0u, 0u);
   }
-  for (int idx = tid; idx < atotal * kCPR; idx += blockDim.x) {
-    const int e = idx / kCPR, q = idx % kCPR;
-    const size_t s = (size_t)src_j[e] * D * sizeof(T) + q * 16;
-    const size_t d = (size_t)(off + dst_r[e]) * D * sizeof(T) + q * 16;
-    *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Kc) + d) =
-        *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(Ks) + s);
-    *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(Vc) + d) =
-        *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(Vs) + s);
+  // the copy: kCopyBatch 16-byte chunks of K and of V per thread loaded before any is stored, so
+  // a thread has 2 * kCopyBatch loads in flight instead of one chunk per memory round trip
+  const int total = atotal * kCPR;
+  const unsigned char* ks8 = reinterpret_cast<const unsigned char*>(Ks);
+  const unsigned char* vs8 = reinterpret_cast<const unsigned char*>(Vs);
+  unsigned char* kc8 = reinterpret_cast<unsigned char*>(Kc);
+  unsigned char* vc8 = reinterpret_cast<unsigned char*>(Vc);
+  for (int base = 0; base < total; base += kCopyBatch * CHUNK) {
+    uint4 kr[kCopyBatch], vr[kCopyBatch];
+    size_t dd[kCopyBatch];
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {               // no branches: lanes past the end copy the last
+      const int idx = min(base + u * CHUNK + tid, total - 1);   // chunk again (the same bytes, same place)
+      const int e = idx / kCPR, q = idx % kCPR;
+      const size_t sb = (size_t)src_j[e] * D * sizeof(T) + q * 16;
+      dd[u] = (size_t)(off + dst_r[e]) * D * sizeof(T) + q * 16;
+      kr[u] = *reinterpret_cast<const uint4*>(ks8 + sb);
+      vr[u] = *reinterpret_cast<const uint4*>(vs8 + sb);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      *reinterpret_cast<uint4*>(kc8 + dd[u]) = kr[u];
+      *reinterpret_cast<uint4*>(vc8 + dd[u]) = vr[u];
+    }
   }
 }
 
