@@ -27,7 +27,7 @@ struct ProfileArgs {
   float* recovery;   // [B*Hkv*5]
   uint8_t* policy;   // [B*Hkv]
   // small grids split the sweeps: key chunks of sweep 1 (partial max/sum per row,
-  // merged by a second launch) and row chunks of sweep 2 (partial column sums,
+  // merged by the column sweep as it loads each row) and row chunks of sweep 2 (partial column sums,
   // added by the select pass); nullptr / chunk >= n means no split
   int kchunk, rchunk;
   float2* rs_part;   // [ceil(n/kchunk), B*Hq, n]

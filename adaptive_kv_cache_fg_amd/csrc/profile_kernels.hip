@@ -172,29 +172,6 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
   }
 }
 
-// Merge of the key chunks' (max, sum) of each row into its log-sum-exp.
-__global__ __launch_bounds__(256) void rowstats_merge_kernel(const float2* __restrict__ rs_part,
-                                                             float* __restrict__ lse2, float* __restrict__ lse_out,
-                                                             int nbh, int n, int kchunk) {
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)nbh * n) return;
-  const int row = (int)(idx % n);
-  const int nc = (min(n, (row / kRowsPerWG + 1) * kRowsPerWG) + kchunk - 1) / kchunk;
-  float M = kNegBig;
-  for (int ch = 0; ch < nc; ++ch) {
-    const float2 v = rs_part[(size_t)ch * nbh * n + idx];
-    if (v.y > 0.f) M = fmaxf(M, v.x);
-  }
-  float L = 0.f;
-  for (int ch = 0; ch < nc; ++ch) {
-    const float2 v = rs_part[(size_t)ch * nbh * n + idx];
-    if (v.y > 0.f) L = fmaf(v.y, fast_exp2(v.x - M), L);
-  }
-  const float v = M + fast_log2(L);
-  lse2[idx] = v;
-  if (lse_out) lse_out[idx] = v * kLn2;
-}
-
 // ---------------------------------------------------------------- sweep 2: column and band sums
 // A wave owns 64 keys as two 32-column MFMA blocks (kc = 0, 1) held in
 // registers; every A operand (32 query rows x KS dims) read from the staged Q
@@ -203,8 +180,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                       const float* __restrict__ lse2, float* __restrict__ cum,
                                                       float* __restrict__ band, float2* __restrict__ cs_part,
-                                                      int Hq, int Hkv, int n, int n_kb, int rchunk, int w_l,
-                                                      float c) {
+                                                      const float2* __restrict__ rs_part, int kchunk,
+                                                      float* __restrict__ lse_out, int Hq, int Hkv, int n,
+                                                      int n_kb, int rchunk, int w_l, float c) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
   constexpr int NK = D / M::KS;
@@ -246,6 +224,14 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   LdsLoader<T, D, kRowTile> ldr;
   ldr.init(wave, lane);
   float lpre = 0.f;
+  // With sweep 1 split over key chunks (rs_part), a row's log-sum-exp is merged here from the
+  // chunks' (max, sum) pairs: the first kPre pairs are loaded with the tile, the merge waits for
+  // the tile's commit; the key block 0 workgroups (which see every row once) write lse_out.
+  constexpr int kPre = 8;
+  float2 pre[kPre];
+  int pre_nc = 0, pre_row = 0;
+  size_t pre_qh = 0;
+  const int nbq = Hq * (int)gridDim.y;                   // B * Hq
   // tiles run over (query head g, row tile) with the row tile fastest, from the
   // last rows down: every key block's rows end at n, so workgroups of one head
   // running side by side stream the same Q tiles (shared through L2).  The next
@@ -255,12 +241,42 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
     const int i0 = i_begin + (ntiles - 1 - it) * kRowTile;   // last rows first (see below)
     const size_t qh = (size_t)b * Hq + (size_t)h * G + ig;
     ldr.issue(Q + qh * n * D, i0, n, qtile[u & 1], wave);
-    if (threadIdx.x < kRowTile) lpre = (i0 + (int)threadIdx.x < i_end) ? lse2[qh * n + i0 + threadIdx.x] : INFINITY;
+    if (threadIdx.x < kRowTile) {
+      const int row = i0 + (int)threadIdx.x;
+      if (rs_part == nullptr) {
+        lpre = row < i_end ? lse2[qh * n + row] : INFINITY;
+      } else {
+        const int rr = min(row, n - 1);
+        pre_nc = (min(n, (rr / kRowsPerWG + 1) * kRowsPerWG) + kchunk - 1) / kchunk;
+        pre_row = row;
+        pre_qh = qh;
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) pre[k] = rs_part[((size_t)min(k, pre_nc - 1) * nbq + qh) * n + rr];
+      }
+    }
     if (++it == ntiles) { it = 0; ++ig; }
   };
   auto commit = [&](int u) {                                     // tile u's lse2 into its LDS slot
     wait_lds_loads();
-    if (threadIdx.x < kRowTile) lse_t[u & 1][threadIdx.x] = lpre;   // rows past the chunk get P = 0
+    if (threadIdx.x < kRowTile) {
+      if (rs_part != nullptr) {
+        float Mx = kNegBig, Ls = 0.f;
+        auto merge = [&](float2 v) {
+          if (v.y > 0.f) {
+            const float mn = fmaxf(Mx, v.x);
+            Ls = Ls * fast_exp2(Mx - mn) + v.y * fast_exp2(v.x - mn);
+            Mx = mn;
+          }
+        };
+#pragma unroll
+        for (int k = 0; k < kPre; ++k)
+          if (k < pre_nc) merge(pre[k]);
+        for (int k = kPre; k < pre_nc; ++k) merge(rs_part[((size_t)k * nbq + pre_qh) * n + pre_row]);
+        lpre = pre_row < i_end ? Mx + fast_log2(Ls) : INFINITY;
+        if (lse_out && kb == 0 && pre_row < i_end) lse_out[pre_qh * n + pre_row] = lpre * kLn2;
+      }
+      lse_t[u & 1][threadIdx.x] = lpre;                           // rows past the chunk get P = 0
+    }
   };
   issue(0);
   commit(0);
@@ -360,19 +376,14 @@ static hipError_t launch_profile_sweeps_t(const ProfileArgs& a, hipStream_t st) 
     timed_begin(FG_K_ROWSTATS, st);
     rowstats_kernel<T, D><<<dim3((unsigned)(a.Hq * rs_groups), a.B), dim3(256), 0, st>>>(
         (const T*)a.Q, (const T*)a.K, a.lse2, a.lse_out, a.rs_part, a.Hq, a.Hkv, a.n, n_rb, a.kchunk, c);
-    hipError_t e = hipGetLastError();
-    if (e == hipSuccess && a.rs_part) {
-      const size_t rows = (size_t)a.B * a.Hq * a.n;
-      rowstats_merge_kernel<<<dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st>>>(
-          a.rs_part, a.lse2, a.lse_out, a.B * a.Hq, a.n, a.kchunk);
-      e = hipGetLastError();
-    }
+      const hipError_t e = hipGetLastError();      // a split sweep 1 is merged by the column sweep
     timed_end(st);
     if (e != hipSuccess) return e;
   }
   timed_begin(FG_K_COLSUMS, st);
   colsums_kernel<T, D><<<dim3((unsigned)(a.Hkv * cs_groups), a.B), dim3(256), 0, st>>>(
-      (const T*)a.Q, (const T*)a.K, a.lse2, a.cum, a.band, a.cs_part, a.Hq, a.Hkv, a.n, n_kb, a.rchunk, a.w_l, c);
+      (const T*)a.Q, (const T*)a.K, a.lse2, a.cum, a.band, a.cs_part, a.lse_ready ? nullptr : a.rs_part, a.kchunk,
+      a.lse_out, a.Hq, a.Hkv, a.n, n_kb, a.rchunk, a.w_l, c);
   timed_end(st);
   return hipGetLastError();
 }

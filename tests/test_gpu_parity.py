@@ -31,6 +31,7 @@ def test_config0_tiny_planted_fp32(lib_mod):
     (200, 128, "bf16", 8, 2, 2),
     (300, 64, "f32", 4, 4, 1),
     (517, 128, "bf16", 8, 1, 1),
+    (2600, 128, "bf16", 2, 2, 1),      # split sweep 1 with 11 key chunks per row: merge past the prefetched 8
 ])
 def test_ragged_shapes(lib_mod, n, d, dtype, hq, hkv, batch):
     types = ("special", "punct", "heavy", "local", "none", "none", "none", "none")[:hkv]
