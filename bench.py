@@ -320,7 +320,7 @@ def main() -> int:
                          "and replayed; eager: every call launched from Python")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1"}))
         return 2
     spec = syn.CONFIGS[args.config]
     if not 0 <= args.layer < spec.layers:
