@@ -10,15 +10,16 @@
 // so a new token always lands in the slot of the key leaving the window.
 //
 // Kernels: a per-head count (plan), one scan over heads for row and work-item
-// offsets, and a gather over (head, 256-position chunk) whose workgroups rank
-// their kept keys with a wave ballot prefix and copy rows with 16-byte loads;
-// the last chunk of a head also writes the head's decode work items.
+// offsets (one workgroup does both for plans of modest size), and a gather
+// over (head, 128-position chunk) whose workgroups rank their kept keys with a
+// wave ballot prefix and copy rows with 16-byte loads; the last chunk of a
+// head also writes the head's decode work items.
 #include "fg_common.h"
 #include "fg_internal.h"
 
 namespace fg {
 
-constexpr int kPosChunk = 256;
+constexpr int kPosChunk = 128;
 constexpr int kCopyBatch = 4;     // 16-byte chunks of K and of V per thread in flight in the gather's copy
 
 __device__ __forceinline__ bool fbit(const uint32_t* fm, int j) { return (fm[j >> 5] >> (j & 31)) & 1u; }
@@ -60,12 +61,13 @@ __device__ __forceinline__ int block_sum_i(int v, int* red) {
   return t;   // valid in every thread
 }
 
-__global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ cls, const uint8_t* __restrict__ policy,
-                                                   const uint32_t* __restrict__ fmask, int Hkv, int n, int w_l,
-                                                   int max_new, int max_new_kept, int32_t* __restrict__ kept_count,
-                                                   int32_t* __restrict__ ring, int32_t* __restrict__ capacity) {
-  __shared__ int red[4];
-  const int hd = blockIdx.x, b = hd / Hkv;
+// Permanent prompt keys (np) and window keys in the ring (nr) of head hd, summed
+// over this thread's share: words t0, t0 + stride, ... and the tail positions
+// likewise.
+__device__ __forceinline__ void head_counts(const uint8_t* __restrict__ cls, const uint8_t* __restrict__ policy,
+                                            const uint32_t* __restrict__ fmask, int Hkv, int n, int w_l, int hd,
+                                            int t0, int stride, int& np_out, int& nr_out) {
+  const int b = hd / Hkv;
   const int nw = (n + 31) / 32;
   const uint8_t* cl = cls + (size_t)b * n;
   const uint32_t* fm = fmask + (size_t)hd * nw;
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ c
   int j0 = 0;                                              // positions below j0 are counted by words
   if ((reinterpret_cast<uintptr_t>(cl) & 3u) == 0) {       // class row 4-byte aligned: 32 positions a step
     const uint32_t* cl32 = reinterpret_cast<const uint32_t*>(cl);
-    for (int w = threadIdx.x; w < n / 32; w += blockDim.x) {
+    for (int w = t0; w < n / 32; w += stride) {
       const uint32_t m = perm_mask_word(cl32, fm, w, pol);
       np += __popc(m);
       if (R > 0) {                                         // normal keys of the window [n - R, n)
@@ -85,14 +87,28 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ c
     }
     j0 = (n / 32) * 32;
   }
-  for (int j = j0 + threadIdx.x; j < n; j += blockDim.x) {
-    const bool p = perm_keep(cl[j], fbit(fm, j), pol);
-    np += p;
-    nr += (!p && R > 0 && j >= n - R);
+  for (int j = j0 + t0; j < n; j += stride) {
+    const bool pk = perm_keep(cl[j], fbit(fm, j), pol);
+    np += pk;
+    nr += (!pk && R > 0 && j >= n - R);
   }
+  np_out = np;
+  nr_out = nr;
+}
+
+__global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ cls, const uint8_t* __restrict__ policy,
+                                                   const uint32_t* __restrict__ fmask, int Hkv, int n, int w_l,
+                                                   int max_new, int max_new_kept, int32_t* __restrict__ kept_count,
+                                                   int32_t* __restrict__ ring, int32_t* __restrict__ capacity) {
+  __shared__ int red[4];
+  const int hd = blockIdx.x;
+  int np, nr;
+  head_counts(cls, policy, fmask, Hkv, n, w_l, hd, (int)threadIdx.x, (int)blockDim.x, np, nr);
   np = block_sum_i(np, red);
   nr = block_sum_i(nr, red);
   if (threadIdx.x == 0) {
+    const int pol = policy[hd];
+    const int R = ring_slots(pol, w_l);
     kept_count[hd] = np + nr;
     ring[hd] = R;
     capacity[hd] = R + np + (pol == 4 ? max_new : max_new_kept);
@@ -103,16 +119,15 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ c
 // workgroup: each thread sums a contiguous segment of heads, the segment totals
 // are scanned with wave shuffles and one LDS exchange between the waves, then
 // every thread writes its segment's offsets.
-constexpr int kScanThreads = 256;
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ capacity, int H, int chunk,
-                                                            int64_t* __restrict__ row_offset,
-                                                            int64_t* __restrict__ work_offset,
-                                                            int64_t* __restrict__ totals) {
-  constexpr int kWaves = kScanThreads / kWave;
+// NT threads; capacity may sit in global memory or in LDS.
+template <int NT>
+__device__ __forceinline__ void scan_heads(const int32_t* capacity, int H, int chunk, int64_t* __restrict__ row_offset,
+                                           int64_t* __restrict__ work_offset, int64_t* __restrict__ totals) {
+  constexpr int kWaves = NT / kWave;
   __shared__ long long wr[kWaves], ww[kWaves];
   __shared__ int wm[kWaves];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int seg = (H + kScanThreads - 1) / kScanThreads;
+  const int seg = (H + NT - 1) / NT;
   const int i0 = min(H, t * seg), i1 = min(H, i0 + seg);
   long long sr = 0, sw = 0;
   int mw = 1;
@@ -167,6 +182,59 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
     totals[1] = tw;
     totals[2] = mx;
   }
+}
+
+constexpr int kScanThreads = 256;
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ capacity, int H, int chunk,
+                                                            int64_t* __restrict__ row_offset,
+                                                            int64_t* __restrict__ work_offset,
+                                                            int64_t* __restrict__ totals) {
+  scan_heads<kScanThreads>(capacity, H, chunk, row_offset, work_offset, totals);
+}
+
+// Plan and scan in one workgroup (one launch instead of two) for small plans:
+// at most kPlanScanMaxWords class words in all (H * ceil(n / 32)); beyond that
+// one workgroup counting every head is slower than the per-head launch plus the
+// scan.  The heads' counts go to LDS (a power-of-two group of threads per
+// head, one LDS atomic per thread and head), the capacities replace them
+// there, and the scan reads them from LDS.  Integer sums: the result does not
+// depend on the order of the atomics.
+constexpr int kPlanScanThreads = 1024;
+constexpr int kPlanScanMaxHeads = 2048;
+constexpr long long kPlanScanMaxWords = 4096;
+__global__ __launch_bounds__(kPlanScanThreads) void plan_scan_kernel(
+    const uint8_t* __restrict__ cls, const uint8_t* __restrict__ policy, const uint32_t* __restrict__ fmask, int Hkv,
+    int n, int w_l, int max_new, int max_new_kept, int H, int chunk, int32_t* __restrict__ kept_count,
+    int32_t* __restrict__ ring, int32_t* __restrict__ capacity, int64_t* __restrict__ row_offset,
+    int64_t* __restrict__ work_offset, int64_t* __restrict__ totals) {
+  __shared__ int s_np[kPlanScanMaxHeads], s_nr[kPlanScanMaxHeads];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < H; i += kPlanScanThreads) {
+    s_np[i] = 0;
+    s_nr[i] = 0;
+  }
+  __syncthreads();
+  int tpg = 1;                                             // threads per head
+  while (2 * tpg * H <= kPlanScanThreads) tpg *= 2;
+  for (int hd = tid / tpg; hd < H; hd += kPlanScanThreads / tpg) {
+    int np, nr;
+    head_counts(cls, policy, fmask, Hkv, n, w_l, hd, tid % tpg, tpg, np, nr);
+    if (np) atomicAdd(&s_np[hd], np);
+    if (nr) atomicAdd(&s_nr[hd], nr);
+  }
+  __syncthreads();
+  for (int hd = tid; hd < H; hd += kPlanScanThreads) {
+    const int pol = policy[hd];
+    const int R = ring_slots(pol, w_l);
+    const int np = s_np[hd], nr = s_nr[hd];
+    const int cap = R + np + (pol == 4 ? max_new : max_new_kept);
+    kept_count[hd] = np + nr;
+    ring[hd] = R;
+    capacity[hd] = cap;
+    s_np[hd] = cap;                                        // the scan's input
+  }
+  __syncthreads();
+  scan_heads<kPlanScanThreads>(s_np, H, chunk, row_offset, work_offset, totals);
 }
 
 template <typename T, int D, int CHUNK>
@@ -334,6 +402,14 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
   const int H = a.B * a.Hkv;
+  if (H <= kPlanScanMaxHeads && (long long)H * ((a.n + 31) / 32) <= kPlanScanMaxWords) {
+    timed_begin(FG_K_PLAN, st);
+    plan_scan_kernel<<<dim3(1), dim3(kPlanScanThreads), 0, st>>>(
+        a.cls, a.policy, a.fmask, a.Hkv, a.n, a.w_l, a.max_new, a.max_new_kept, H, a.chunk_rows, a.kept_count, a.ring,
+        a.capacity, a.row_offset, a.work_offset, a.totals);
+    timed_end(st);
+    return hipGetLastError();
+  }
   timed_begin(FG_K_PLAN, st);
   plan_kernel<<<dim3(H), dim3(256), 0, st>>>(a.cls, a.policy, a.fmask, a.Hkv, a.n, a.w_l, a.max_new, a.max_new_kept,
                                              a.kept_count, a.ring, a.capacity);

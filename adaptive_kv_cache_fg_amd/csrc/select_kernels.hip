@@ -24,17 +24,25 @@ namespace fg {
 
 constexpr int kSelThreads = 1024;
 
-__device__ __forceinline__ double block_sum(double v, double* red) {
+// Block sums of four fp64 values at once (one shuffle ladder and one barrier
+// for all four); the totals are valid in thread 0.
+__device__ __forceinline__ void block_sum4(double (&v)[4], double (*red)[kSelThreads / 64]) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] += __shfl_xor(v[k], o);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) red[k][wave] = v[k];
   __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  double t = 0.0;
   if (threadIdx.x == 0)
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
-  return t;   // valid in thread 0
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      double t = 0.0;
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[k][w];
+      v[k] = t;
+    }
 }
 
 // VPT > 0: each thread holds the scores (and band sums) of keys tid + k * kSelThreads,
@@ -50,7 +58,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
   __shared__ unsigned hist[256];
   __shared__ unsigned s_sel, s_rem;
   __shared__ int wave_cnt[kSelThreads / 64];
-  __shared__ double red[kSelThreads / 64];
+  __shared__ double red[4][kSelThreads / 64];
 
   const int bh = blockIdx.x, b = bh / Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -192,10 +200,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
       }
     }
   }
-  m_s = block_sum(m_s, red);
-  m_p = block_sum(m_p, red);
-  m_f = block_sum(m_f, red);
-  m_b = block_sum(m_b, red);
+  double ms[4] = {m_s, m_p, m_f, m_b};
+  block_sum4(ms, red);
+  m_s = ms[0];
+  m_p = ms[1];
+  m_f = ms[2];
+  m_b = ms[3];
   if (tid == 0) {
     const double denom = (double)G * (double)n;
     double R[5];
