@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
                                                              float* __restrict__ recovery, uint8_t* __restrict__ policy) {
   constexpr int NV = VPT > 0 ? VPT : 1;
   __shared__ unsigned hist[256];
-  __shared__ unsigned s_sel, s_rem;
+  __shared__ unsigned s_sel, s_rem, s_cnt;
   __shared__ int wave_cnt[kSelThreads / 64];
   __shared__ double red[4][kSelThreads / 64];
 
@@ -98,6 +98,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
   const float* cu = cum + (size_t)bh * n;
   const float* bd = band + (size_t)bh * n;
   const uint8_t* cl = cls + (size_t)b * n;
+  uint8_t cv_cls[NV];                             // token classes of this thread's keys, loaded up front
+#pragma unroll
+  for (int it = 0; it < NV; ++it) {
+    const int j = it * kSelThreads + tid;
+    cv_cls[it] = (VPT > 0 && j < n) ? cl[j] : (uint8_t)0;
+  }
   const int nw = (n + 31) / 32;
   auto score_of = [&](int it, int j) -> float { return VPT > 0 ? cv[it < NV ? it : 0] : cu[j]; };
   auto band_of = [&](int it, int j) -> float { return VPT > 0 ? bv[it < NV ? it : 0] : bd[j]; };
@@ -106,6 +112,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
   const int mode = k_f <= 0 ? 0 : (k_f >= n ? 1 : 2);
   uint32_t thr = 0;
   int take_eq = 0;
+  bool all_eq = false;                            // every key equal to the threshold is taken
   if (mode == 2) {
     uint32_t prefix = 0, pmask = 0;
     int remaining = k_f;
@@ -144,7 +151,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
           int acc = excl;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (acc + h[e] >= remaining) { s_sel = (unsigned)(255 - 4 * lane - e); s_rem = (unsigned)(remaining - acc); break; }
+            if (acc + h[e] >= remaining) {
+              s_sel = (unsigned)(255 - 4 * lane - e);
+              s_rem = (unsigned)(remaining - acc);
+              s_cnt = (unsigned)h[e];
+              break;
+            }
             acc += h[e];
           }
         }
@@ -157,6 +169,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
     }
     thr = prefix;
     take_eq = remaining;
+    all_eq = (int)s_cnt == remaining;             // the last pass's bin holds exactly the keys equal to thr
   }
 
   double m_s = 0.0, m_p = 0.0, m_f = 0.0, m_b = 0.0;
@@ -168,8 +181,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
       const bool valid = j < n;
       const float v = valid ? score_of(it, j) : 0.f;
       const uint32_t u = __float_as_uint(v);
-      bool sel = (mode == 1) && valid;
-      if (mode == 2) {
+      bool sel = (mode == 1 || (mode == 2 && all_eq)) && valid && (mode == 1 || u >= thr);
+      if (mode == 2 && !all_eq) {                 // some keys equal to thr are left out: rank them by index
         const bool eq = valid && u == thr;
         const unsigned long long bal = __ballot(eq);
         if (lane == 0) wave_cnt[wave] = __popcll(bal);
@@ -192,7 +205,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
         if (w0 + 1 < nw) fmask[(size_t)bh * nw + w0 + 1] = (uint32_t)(sb >> 32);
       }
       if (valid) {
-        const uint8_t c = cl[j];
+        const uint8_t c = VPT > 0 ? cv_cls[it < NV ? it : 0] : cl[j];
         if (c == kSpecial) m_s += v;
         else if (c == kPunct) m_p += v;
         else if (sel) m_f += v;
