@@ -3,6 +3,7 @@
 // launch; nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -162,11 +163,31 @@ int32_t fg_kernel_timing_read(int32_t* ids, float* ms, int32_t max) {
   return k;
 }
 
+namespace {
+
+// Sweep workgroups that run at once on the current device (two per compute
+// unit); it only steers the chunk size of a split sweep.
+int sweep_slots() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    v = 2 * cus;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+}  // namespace
+
 size_t fg_profile_workspace_size(const fg_shape* s) {
   if (check_shape(s) != FG_OK) return 0;
   const size_t rows_q = (size_t)s->batch * s->n_q_heads * s->seq_len;
   const size_t rows_k = (size_t)s->batch * s->n_kv_heads * s->seq_len;
-  const fg::SweepSplit sp = fg::sweep_split(s->batch, s->n_q_heads, s->n_kv_heads, s->seq_len);
+  const fg::SweepSplit sp = fg::sweep_split(s->batch, s->n_q_heads, s->n_kv_heads, s->seq_len, 512);
   return align256(rows_q * sizeof(float)) + align256(rows_k * sizeof(float)) + align256(sp.rs_bytes) +
          align256(sp.cs_bytes);
 }
@@ -234,7 +255,7 @@ fg_status profile_impl(const fg_shape* shape, const fg_params* params, const voi
   const size_t rows_q = (size_t)a.B * a.Hq * a.n;
   const size_t rows_k = (size_t)a.B * a.Hkv * a.n;
   a.band = band_out ? band_out : reinterpret_cast<float*>(ws + align256(rows_q * sizeof(float)));
-  const fg::SweepSplit sp = fg::sweep_split(a.B, a.Hq, a.Hkv, a.n);
+  const fg::SweepSplit sp = fg::sweep_split(a.B, a.Hq, a.Hkv, a.n, sweep_slots());
   unsigned char* parts = ws + align256(rows_q * sizeof(float)) + align256(rows_k * sizeof(float));
   a.kchunk = sp.kchunk;
   a.rchunk = sp.rchunk;

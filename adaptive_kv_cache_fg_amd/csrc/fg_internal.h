@@ -38,24 +38,76 @@ struct ProfileArgs {
 // Sweep tiling shared by the launcher and the workspace query.
 constexpr int kSweepRowsPerWG = 256;   // query rows per sweep-1 workgroup
 constexpr int kSweepKeysPerWG = 256;   // keys per sweep-2 workgroup
-constexpr int kSplitKeyChunk = 256;    // key chunk of a split sweep 1
-constexpr int kSplitRowChunk = 512;    // row chunk of a split sweep 2
+constexpr int kSplitMinChunk = 256;    // smallest chunk of a split sweep (sizes the partial buffers)
 constexpr long long kSplitBelowGroups = 1024;  // split when the unsplit grid has fewer workgroups
+constexpr int kSplitOverheadItems = 192;       // a workgroup's fixed cost (launch, operand and first-tile loads), in keys (rows) of work
+
+// A block of R keys (sweep 1: the causal keys of a row block) or rows (sweep 2:
+// the rows at or below a key block) is split into split_count(R, S) chunks of
+// nearly equal size at 32-item granularity; chunk ch is
+// [split_begin(R, c, ch), min(R, split_begin(R, c, ch + 1))).  The count is
+// the one a plain split into S-item chunks would give, so every chunk has at
+// most S items and the partial buffers keep their layout.
+__host__ __device__ inline int split_count(int R, int S) { return R <= S ? 1 : (R + S - 1) / S; }
+__host__ __device__ inline int split_begin(int R, int c, int ch) {
+  const int U = (R + 31) / 32;
+  return 32 * (int)(((long long)ch * U) / c);
+}
+
+// Items of block i: sweep 1 row block rb has min(n, 256 (rb + 1)) causal keys,
+// sweep 2 key block kb has n - 256 kb rows at or below it.
+inline int sweep_block_items(bool rows_of_key_block, int n, int i) {
+  return rows_of_key_block ? n - kSweepKeysPerWG * i : (n < kSweepRowsPerWG * (i + 1) ? n : kSweepRowsPerWG * (i + 1));
+}
+
+// Chunk size of a split sweep: the candidate S >= kSplitMinChunk that minimises
+// the estimated span, rounds of `slots` concurrent workgroups times the
+// largest chunk (plus a workgroup's fixed cost) -- a small grid is bound by its
+// last round, not by its total work.
+inline int choose_split_chunk(int n, int nblocks, long long mult, bool rows_of_key_block, int slots) {
+  static const int kCand[] = {256, 288, 320, 352, 384, 448, 512, 576, 640, 768, 896, 1024, 1280, 1536, 1792,
+                              2048, 2560, 3072, 4096, 6144, 8192, 12288, 16384, 24576, 32768};
+  int best = n;
+  long long best_cost = -1;
+  for (int S : kCand) {
+    if (S >= n) break;
+    long long count = 0;
+    int maxc = 0;
+    for (int i = 0; i < nblocks; ++i) {
+      const int R = sweep_block_items(rows_of_key_block, n, i);
+      const int c = split_count(R, S);
+      count += c;
+      const int size = 32 * (((R + 31) / 32 + c - 1) / c) < R ? 32 * (((R + 31) / 32 + c - 1) / c) : R;
+      maxc = size > maxc ? size : maxc;
+    }
+    count *= mult;
+    const long long rounds = (count + slots - 1) / slots;
+    const long long cost = rounds * (maxc + kSplitOverheadItems);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  return best;
+}
+
 struct SweepSplit {
   int kchunk, rchunk;
   bool rs_split, cs_split;
   size_t rs_bytes, cs_bytes;
 };
-inline SweepSplit sweep_split(int B, int Hq, int Hkv, int n) {
+// slots: workgroups that run at once (two per compute unit); it only steers the
+// chunk size, never the buffer sizes.
+inline SweepSplit sweep_split(int B, int Hq, int Hkv, int n, int slots) {
   SweepSplit p{};
   const int n_rb = (n + kSweepRowsPerWG - 1) / kSweepRowsPerWG;
   const int n_kb = (n + kSweepKeysPerWG - 1) / kSweepKeysPerWG;
-  p.rs_split = (long long)B * Hq * n_rb < kSplitBelowGroups && n > kSplitKeyChunk;
-  p.cs_split = (long long)B * Hkv * n_kb < kSplitBelowGroups && n > kSplitRowChunk;
-  p.kchunk = p.rs_split ? kSplitKeyChunk : n_rb * kSweepRowsPerWG;
-  p.rchunk = p.cs_split ? kSplitRowChunk : n;
-  p.rs_bytes = p.rs_split ? (size_t)((n + p.kchunk - 1) / p.kchunk) * B * Hq * n * sizeof(float) * 2 : 0;
-  p.cs_bytes = p.cs_split ? (size_t)((n + p.rchunk - 1) / p.rchunk) * B * Hkv * n * sizeof(float) * 2 : 0;
+  p.rs_split = (long long)B * Hq * n_rb < kSplitBelowGroups && n > kSplitMinChunk;
+  p.cs_split = (long long)B * Hkv * n_kb < kSplitBelowGroups && n > kSplitMinChunk;
+  p.kchunk = p.rs_split ? choose_split_chunk(n, n_rb, (long long)B * Hq, false, slots) : n_rb * kSweepRowsPerWG;
+  p.rchunk = p.cs_split ? choose_split_chunk(n, n_kb, (long long)B * Hkv, true, slots) : n;
+  p.rs_bytes = p.rs_split ? (size_t)split_count(n, kSplitMinChunk) * B * Hq * n * sizeof(float) * 2 : 0;
+  p.cs_bytes = p.cs_split ? (size_t)split_count(n, kSplitMinChunk) * B * Hkv * n * sizeof(float) * 2 : 0;
   return p;
 }
 

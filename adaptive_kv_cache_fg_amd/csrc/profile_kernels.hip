@@ -60,11 +60,13 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
   // splitting (rs_part == nullptr) every row block is one chunk
   int rem = (int)(blockIdx.x / Hq), rb = n_rb - 1, ch = 0;
   for (; rb > 0; --rb) {
-    const int nc = (min(n, (rb + 1) * kRowsPerWG) + kchunk - 1) / kchunk;
+    const int nc = split_count(min(n, (rb + 1) * kRowsPerWG), kchunk);
     if (rem < nc) break;
     rem -= nc;
   }
   ch = rem;
+  const int n_keys = min(n, (rb + 1) * kRowsPerWG);       // causal keys of the row block, split in balanced chunks
+  const int n_ch = split_count(n_keys, kchunk);
   const int b = bh / Hq, hq = bh % Hq, G = Hq / Hkv;
   const T* Qh = Q + (size_t)bh * n * D;
   const T* Kh = K + ((size_t)b * Hkv + hq / G) * n * D;
@@ -81,8 +83,8 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
   }
 
   float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
-  const int kbeg = ch * kchunk;                           // this chunk's keys [kbeg, kend)
-  const int kend = min(min(n, (rb + 1) * kRowsPerWG), kbeg + kchunk);
+  const int kbeg = split_begin(n_keys, n_ch, ch);         // this chunk's keys [kbeg, kend)
+  const int kend = min(n_keys, split_begin(n_keys, n_ch, ch + 1));
   const int ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
   const int qlast = q0 + kRowsPerWave - 1;
 
@@ -196,11 +198,13 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   // without splitting (cs_part == nullptr) every key block is one chunk
   int rem = (int)(blockIdx.x / Hkv), kb = 0;
   for (; kb < n_kb - 1; ++kb) {
-    const int nc = (n - kb * kKeysPerWG + rchunk - 1) / rchunk;
+    const int nc = split_count(n - kb * kKeysPerWG, rchunk);
     if (rem < nc) break;
     rem -= nc;
   }
   const int ch = rem;
+  const int n_rows = n - kb * kKeysPerWG;                 // rows at or below the key block, split in balanced chunks
+  const int n_ch = split_count(n_rows, rchunk);
   const int b = bh / Hkv, h = bh % Hkv, G = Hq / Hkv;
   const T* Kh = K + (size_t)bh * n * D;
 
@@ -217,8 +221,8 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
 
   float cum_acc[2] = {0.f, 0.f}, band_acc[2] = {0.f, 0.f};   // per key; summed per query head first
   float cum_g[2] = {0.f, 0.f}, band_g[2] = {0.f, 0.f};
-  const int i_begin = kb * kKeysPerWG + ch * rchunk;     // this chunk's query rows [i_begin, i_end)
-  const int i_end = min(n, i_begin + rchunk);
+  const int i_begin = kb * kKeysPerWG + split_begin(n_rows, n_ch, ch);   // this chunk's query rows [i_begin, i_end)
+  const int i_end = kb * kKeysPerWG + min(n_rows, split_begin(n_rows, n_ch, ch + 1));
   const int ntiles = (i_end - i_begin + kRowTile - 1) / kRowTile;   // query tiles per query head
   const int total = G * ntiles;
   LdsLoader<T, D, kRowTile> ldr;
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
         lpre = row < i_end ? lse2[qh * n + row] : INFINITY;
       } else {
         const int rr = min(row, n - 1);
-        pre_nc = (min(n, (rr / kRowsPerWG + 1) * kRowsPerWG) + kchunk - 1) / kchunk;
+        pre_nc = split_count(min(n, (rr / kRowsPerWG + 1) * kRowsPerWG), kchunk);
         pre_row = row;
         pre_qh = qh;
 #pragma unroll
@@ -370,8 +374,8 @@ static hipError_t launch_profile_sweeps_t(const ProfileArgs& a, hipStream_t st) 
   const float c = kLog2e / sqrtf((float)D);
   // workgroups per (batch entry, head): key chunks of every row block / row chunks of every key block
   long long rs_groups = 0, cs_groups = 0;
-  for (int rb = 0; rb < n_rb; ++rb) rs_groups += (std::min(a.n, (rb + 1) * kRowsPerWG) + a.kchunk - 1) / a.kchunk;
-  for (int kb = 0; kb < n_kb; ++kb) cs_groups += (a.n - kb * kKeysPerWG + a.rchunk - 1) / a.rchunk;
+  for (int rb = 0; rb < n_rb; ++rb) rs_groups += split_count(std::min(a.n, (rb + 1) * kRowsPerWG), a.kchunk);
+  for (int kb = 0; kb < n_kb; ++kb) cs_groups += split_count(a.n - kb * kKeysPerWG, a.rchunk);
   if (!a.lse_ready) {
     timed_begin(FG_K_ROWSTATS, st);
     rowstats_kernel<T, D><<<dim3((unsigned)(a.Hq * rs_groups), a.B), dim3(256), 0, st>>>(

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
       const int j = it * kSelThreads + tid;
       float cs = 0.f, bs = 0.f;
       if (j < n) {
-        const int nc = (n - (j / kSweepKeysPerWG) * kSweepKeysPerWG + rchunk - 1) / rchunk;
+        const int nc = split_count(n - (j / kSweepKeysPerWG) * kSweepKeysPerWG, rchunk);
         for (int ch = 0; ch < nc; ++ch) {
           const float2 v = cs_part[((size_t)ch * nbh + bh) * n + j];
           cs += v.x;

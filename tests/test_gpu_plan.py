@@ -50,6 +50,8 @@ def _expected(cls, policy, bits, Hkv, w_l, max_new, max_new_kept, chunk):
 
 
 @pytest.mark.parametrize("B,Hkv,n,seed", [
+    (1, 1, 5, 7),           # one head, no whole 32-position word
+    (3, 1, 33, 8),          # one word and a one-position tail per head, unaligned class rows
     (2, 4, 1000, 1),        # one workgroup; n % 32 != 0 and the second class row unaligned
     (1, 3, 257, 2),
     (2, 8, 4096, 3),        # 16 heads x 128 class words: still one workgroup
