@@ -45,7 +45,9 @@ template <> struct Vec16<float> {
 
 // Merge launch: one workgroup per query head merges its KV head's partial
 // states for that query head, adds the new token, writes the output; the
-// workgroup of the group's first query head also updates the KV head's cache.
+// workgroup of the group's first query head also updates the KV head's cache,
+// before its merge (the update reads none of the merge's inputs, so its stores
+// are under way while the merge computes).
 // Every load is issued before its first use: the per-head scalars, the new
 // token's q . k_new and K/V row, and the partial slots in batches of kBatch
 // items per thread (masked by the head's item count afterwards, so they do not
@@ -98,6 +100,88 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     av[k] = pp[2 + dd];
   }
 
+  if (g == 0 && fits) {                           // one cache update per KV head, before the merge
+    // ---- cache update: afterwards the cache holds {j <= p : level(p + 1, j) <= policy}
+    const bool to_ring = (cls == kNormal) && pol == 3 && w_l >= 2 && R > 0;
+    const bool to_perm = cls == kSpecial || (cls == kPunct && pol >= 1) || (cls == kNormal && pol == 4);
+    const int slot = R > 0 ? p % R : 0;
+
+    // ---- frequent set re-ranked during generation (score != nullptr): the key the window drops
+    // (the ring slot's occupant, position p + 1 - w_l) replaces the cached frequent key of the
+    // lowest score (ties: the larger position) when its own score is larger.  Frequent keys are the
+    // permanent rows of class normal.  The branch is uniform across the workgroup.
+    if (score != nullptr && pol == 3 && R > 0) {
+      const int64_t srow = base_h + slot;
+      const int j_out = pos[srow];
+      if (j_out >= 0) {
+        const size_t cb = (size_t)(hd / Hkv) * n_total;
+        unsigned long long best = ~0ull;                 // (score bits, 0x7fffffff - position): smallest wins
+        int best_row = -1;
+        for (int r = R + tid; r < L; r += NT) {
+          const int jp = pos[base_h + r];
+          if (jp < 0 || jp >= n_total || cls_all[cb + jp] != kNormal) continue;
+          const unsigned long long key = ((unsigned long long)__float_as_uint(score[base_h + r]) << 32) |
+                                         (unsigned)(0x7fffffff - jp);   // scores are >= 0: bits order like values
+          if (key < best) {
+            best = key;
+            best_row = r;
+          }
+        }
+        for (int o = 1; o < kWave; o <<= 1) {
+          const unsigned long long ok = __shfl_xor(best, o);
+          const int orow = __shfl_xor(best_row, o);
+          if (ok < best) {
+            best = ok;
+            best_row = orow;
+          }
+        }
+        if (lane == 0) {
+          s_key[wave] = best;
+          s_row[wave] = best_row;
+        }
+        __syncthreads();
+        best = s_key[0];
+        best_row = s_row[0];
+        for (int w = 1; w < NT / kWave; ++w)
+          if (s_key[w] < best) {
+            best = s_key[w];
+            best_row = s_row[w];
+          }
+        const float s_out = score[srow];
+        if (best != ~0ull && s_out > __uint_as_float((unsigned)(best >> 32))) {
+          const int64_t drow = base_h + best_row;
+          if (tid < D) {                                 // the same threads write the new token's row below
+            Kc[drow * D + tid] = Kc[srow * D + tid];
+            Vc[drow * D + tid] = Vc[srow * D + tid];
+          }
+          if (tid == 0) {
+            pos[drow] = j_out;
+            score[drow] = s_out;
+          }
+        }
+      }
+    }
+    int64_t dst = -1;
+    if (to_ring) dst = base_h + slot;
+    else if (to_perm && L < cap) dst = base_h + L;
+    if (dst >= 0 && tid < D) {                       // threads 0..D-1 hold element tid of the new row
+      Kc[dst * D + tid] = T(kv_self);
+      Vc[dst * D + tid] = T(vv_self);
+    }
+    if (tid == 0) {
+      if (pol == 3 && R > 0 && !to_ring) pos[base_h + slot] = -1;   // key p + 1 - w_l leaves the window
+      if (dst >= 0) pos[dst] = p;
+      if (to_perm) {
+        if (dst >= 0) {
+          len[hd] = L + 1;
+          const int64_t wi = w0 + L / CH;                           // the item that holds row L
+          work[4 * wi + 3] = L % CH + 1;
+        } else {
+          atomicOr(error_word, 1u);
+        }
+      }
+    }
+  }
   // ---- the new token's score: lane sums, then the D / 64 waves of one item group in LDS
   // (every wave reduces; only group 0's entries are read)
   const float sw = group_sum<kWave>(qv * kv_self);
@@ -153,88 +237,6 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
       At = fmaf(a, vv_self, At);
     }
     out[(size_t)qh * D + dd] = Lt > 0.f ? At / Lt : 0.f;
-  }
-  if (g != 0 || !fits) return;                    // one cache update per KV head
-
-  // ---- cache update: afterwards the cache holds {j <= p : level(p + 1, j) <= policy}
-  const bool to_ring = (cls == kNormal) && pol == 3 && w_l >= 2 && R > 0;
-  const bool to_perm = cls == kSpecial || (cls == kPunct && pol >= 1) || (cls == kNormal && pol == 4);
-  const int slot = R > 0 ? p % R : 0;
-
-  // ---- frequent set re-ranked during generation (score != nullptr): the key the window drops
-  // (the ring slot's occupant, position p + 1 - w_l) replaces the cached frequent key of the
-  // lowest score (ties: the larger position) when its own score is larger.  Frequent keys are the
-  // permanent rows of class normal.  The branch is uniform across the workgroup.
-  if (score != nullptr && pol == 3 && R > 0) {
-    const int64_t srow = base_h + slot;
-    const int j_out = pos[srow];
-    if (j_out >= 0) {
-      const size_t cb = (size_t)(hd / Hkv) * n_total;
-      unsigned long long best = ~0ull;                 // (score bits, 0x7fffffff - position): smallest wins
-      int best_row = -1;
-      for (int r = R + tid; r < L; r += NT) {
-        const int jp = pos[base_h + r];
-        if (jp < 0 || jp >= n_total || cls_all[cb + jp] != kNormal) continue;
-        const unsigned long long key = ((unsigned long long)__float_as_uint(score[base_h + r]) << 32) |
-                                       (unsigned)(0x7fffffff - jp);   // scores are >= 0: bits order like values
-        if (key < best) {
-          best = key;
-          best_row = r;
-        }
-      }
-      for (int o = 1; o < kWave; o <<= 1) {
-        const unsigned long long ok = __shfl_xor(best, o);
-        const int orow = __shfl_xor(best_row, o);
-        if (ok < best) {
-          best = ok;
-          best_row = orow;
-        }
-      }
-      if (lane == 0) {
-        s_key[wave] = best;
-        s_row[wave] = best_row;
-      }
-      __syncthreads();
-      best = s_key[0];
-      best_row = s_row[0];
-      for (int w = 1; w < NT / kWave; ++w)
-        if (s_key[w] < best) {
-          best = s_key[w];
-          best_row = s_row[w];
-        }
-      const float s_out = score[srow];
-      if (best != ~0ull && s_out > __uint_as_float((unsigned)(best >> 32))) {
-        const int64_t drow = base_h + best_row;
-        if (tid < D) {                                 // the same threads write the new token's row below
-          Kc[drow * D + tid] = Kc[srow * D + tid];
-          Vc[drow * D + tid] = Vc[srow * D + tid];
-        }
-        if (tid == 0) {
-          pos[drow] = j_out;
-          score[drow] = s_out;
-        }
-      }
-    }
-  }
-  int64_t dst = -1;
-  if (to_ring) dst = base_h + slot;
-  else if (to_perm && L < cap) dst = base_h + L;
-  if (dst >= 0 && tid < D) {                       // threads 0..D-1 hold element tid of the new row
-    Kc[dst * D + tid] = T(kv_self);
-    Vc[dst * D + tid] = T(vv_self);
-  }
-  if (tid == 0) {
-    if (pol == 3 && R > 0 && !to_ring) pos[base_h + slot] = -1;   // key p + 1 - w_l leaves the window
-    if (dst >= 0) pos[dst] = p;
-    if (to_perm) {
-      if (dst >= 0) {
-        len[hd] = L + 1;
-        const int64_t wi = w0 + L / CH;                           // the item that holds row L
-        work[4 * wi + 3] = L % CH + 1;
-      } else {
-        atomicOr(error_word, 1u);
-      }
-    }
   }
 }
 
