@@ -60,8 +60,12 @@ __device__ __forceinline__ bf16x8 v_operand(const unsigned char* vt, int k0, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int D, int QB, int KT>
-__global__ __launch_bounds__(256) void attention_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+// KS key groups of 4 waves per workgroup: with KS = 2 the two groups take the
+// first and the second half of the row block's key tiles (same query rows,
+// their own LDS tiles) and are merged through LDS at the end, which halves the
+// longest workgroup of a small grid.
+template <int D, int QB, int KT, int KS>
+__global__ __launch_bounds__(256 * KS) void attention_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                         const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                                         float* __restrict__ lse2, float* __restrict__ lse_out, int Hq,
                                                         int Hkv, int n, int n_rb, float c) {
@@ -74,8 +78,9 @@ __global__ __launch_bounds__(256) void attention_kernel(const __bf16* __restrict
   constexpr int kKRB = D * 2 + kPadBytes;
   constexpr int kVRB = D * 2 + 16 * kAttnVPadSlots;
   static_assert(NU >= 1 && KT % 32 == 0, "key tile must be whole units");
-  __shared__ __attribute__((aligned(16))) unsigned char ktile[2][KT * kKRB];
-  __shared__ __attribute__((aligned(16))) unsigned char vtile[2][KT * kVRB];
+  static_assert(KS == 1 || KS == 2, "one or two key groups");
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[KS][2][KT * kKRB];
+  __shared__ __attribute__((aligned(16))) unsigned char vtile[KS][2][KT * kVRB];
 
   // heaviest row blocks first; the blocks of one head are Hq apart in launch
   // order, so with Hq a multiple of 8 they share an XCD (and its L2) for K, V
@@ -87,11 +92,13 @@ __global__ __launch_bounds__(256) void attention_kernel(const __bf16* __restrict
   const __bf16* Kh = K + kvh;
   const __bf16* Vh = V + kvh;
 
-  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int grp = wave_id() / 4, wave = wave_id() % 4, lane = threadIdx.x & 63;
   const int q0 = rb * RG + wave * RW;                    // this wave's first query row
   const int qlast = q0 + RW - 1;
   const int kend = min(n, (rb + 1) * RG);               // keys any row of the workgroup sees
   const int ntiles = (kend + KT - 1) / KT;
+  const int tpg = (ntiles + KS - 1) / KS;                // key tiles per group (the last group may have fewer)
+  const int t_beg = grp * tpg, t_end = min(ntiles, t_beg + tpg);
 
   bf16x8 qop[QB][NK];
 #pragma unroll
@@ -184,32 +191,70 @@ __global__ __launch_bounds__(256) void attention_kernel(const __bf16* __restrict
   LdsLoader<__bf16, D, KT, kAttnVPadSlots> vload;
   kload.init(wave, lane);
   vload.init(wave, lane);
-  kload.issue(Kh, 0, n, ktile[0], wave);
-  vload.issue(Vh, 0, n, vtile[0], wave);
+  if (t_beg < t_end) {                                   // group-uniform
+    kload.issue(Kh, t_beg * KT, n, ktile[grp][0], wave);
+    vload.issue(Vh, t_beg * KT, n, vtile[grp][0], wave);
+  }
   wait_lds_loads();
   __syncthreads();
   f32x16 acc[2][QB];                                     // [buffer][query block]: one unit of 32 keys
-  for (int t = 0; t < ntiles; ++t) {
+  for (int i = 0; i < tpg; ++i) {                        // every group runs tpg steps (one barrier each)
+    const int t = t_beg + i;
     const int k0 = t * KT;
-    if (t + 1 < ntiles) {                                // in flight during this tile's MFMAs
-      kload.issue(Kh, k0 + KT, n, ktile[(t + 1) & 1], wave);
-      vload.issue(Vh, k0 + KT, n, vtile[(t + 1) & 1], wave);
+    if (t + 1 < t_end) {                                 // in flight during this tile's MFMAs
+      kload.issue(Kh, k0 + KT, n, ktile[grp][(i + 1) & 1], wave);
+      vload.issue(Vh, k0 + KT, n, vtile[grp][(i + 1) & 1], wave);
     }
-    const unsigned char* kt = ktile[t & 1];
-    const unsigned char* vt = vtile[t & 1];
-    // units pipelined within the tile: the scores of unit kh are issued before
-    // the softmax and P V of unit kh - 1
-    int pend = -1;
+    if (t < t_end) {                                     // group-uniform: the last group may run out first
+      const unsigned char* kt = ktile[grp][i & 1];
+      const unsigned char* vt = vtile[grp][i & 1];
+      // units pipelined within the tile: the scores of unit kh are issued before
+      // the softmax and P V of unit kh - 1
+      int pend = -1;
 #pragma unroll
-    for (int kh = 0; kh < NU; ++kh) {
-      const bool act = unit_active(k0 + 32 * kh);
-      if (act) scores(kt, kh, acc[kh & 1]);
+      for (int kh = 0; kh < NU; ++kh) {
+        const bool act = unit_active(k0 + 32 * kh);
+        if (act) scores(kt, kh, acc[kh & 1]);
+        if (pend >= 0) finish(vt, pend, k0 + 32 * pend, acc[pend & 1]);
+        pend = act ? kh : -1;
+      }
       if (pend >= 0) finish(vt, pend, k0 + 32 * pend, acc[pend & 1]);
-      pend = act ? kh : -1;
     }
-    if (pend >= 0) finish(vt, pend, k0 + 32 * pend, acc[pend & 1]);
     wait_lds_loads();
     __syncthreads();
+  }
+  if constexpr (KS == 2) {
+    // group 1 hands its (max, sum, O) to the lane of group 0 that holds the same query
+    // rows and output dims (the tiles are no longer read: the last barrier above)
+    constexpr int kFields = QB * NS * 16 + 2 * QB;
+    static_assert(4 * 64 * kFields * 4 <= (int)sizeof(ktile), "merge area must fit the key tiles");
+    float* xs = reinterpret_cast<float*>(&ktile[0][0][0]) + (size_t)wave * kFields * 64;
+    if (grp == 1) {
+#pragma unroll
+      for (int cb = 0; cb < QB; ++cb) {
+        xs[(2 * cb) * 64 + lane] = m[cb];
+        xs[(2 * cb + 1) * 64 + lane] = l[cb];
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xs[(2 * QB + (cb * NS + s2) * 16 + r) * 64 + lane] = oacc[cb][s2][r];
+      }
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int cb = 0; cb < QB; ++cb) {
+      const float m1 = xs[(2 * cb) * 64 + lane], l1 = xs[(2 * cb + 1) * 64 + lane];
+      const float mn = fmaxf(m[cb], m1);
+      const float a0 = fast_exp2(m[cb] - mn), a1 = fast_exp2(m1 - mn);
+      l[cb] = l[cb] * a0 + l1 * a1;
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          oacc[cb][s2][r] = oacc[cb][s2][r] * a0 + xs[(2 * QB + (cb * NS + s2) * 16 + r) * 64 + lane] * a1;
+      m[cb] = mn;
+    }
   }
 
   // lanes l and l ^ 32 summed disjoint keys of the same query under the same max
@@ -240,15 +285,26 @@ __global__ __launch_bounds__(256) void attention_kernel(const __bf16* __restrict
   }
 }
 
+// Two key groups per workgroup when the grid is bound by its longest workgroup
+// rather than by its total work: the longest workgroup (the last row block)
+// walks 2 n_rb key tiles, the whole grid B Hq n_rb (n_rb + 1) over two
+// workgroups per CU; splitting its keys halves the former and leaves the latter.
 template <int D, int QB, int KT>
 static hipError_t launch_attention_t(const AttentionArgs& a, hipStream_t st) {
   constexpr int RG = 128 * QB;
   const int n_rb = (a.n + RG - 1) / RG;
   const float c = kLog2e / sqrtf((float)D);
+  const bool split = (long long)a.B * a.Hq * (n_rb + 1) < 4LL * a.cus;
   timed_begin(FG_K_ATTENTION, st);
-  attention_kernel<D, QB, KT><<<dim3((unsigned)(a.Hq * n_rb), a.B), dim3(256), 0, st>>>(
-      (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O, a.lse2, a.lse_out, a.Hq, a.Hkv, a.n,
-      n_rb, c);
+  if (split) {
+    attention_kernel<D, QB, KT, 2><<<dim3((unsigned)(a.Hq * n_rb), a.B), dim3(512), 0, st>>>(
+        (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O, a.lse2, a.lse_out, a.Hq, a.Hkv, a.n,
+        n_rb, c);
+  } else {
+    attention_kernel<D, QB, KT, 1><<<dim3((unsigned)(a.Hq * n_rb), a.B), dim3(256), 0, st>>>(
+        (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O, a.lse2, a.lse_out, a.Hq, a.Hkv, a.n,
+        n_rb, c);
+  }
   timed_end(st);
   return hipGetLastError();
 }

@@ -220,6 +220,7 @@ fg::AttentionArgs attention_args(const fg_shape* shape, const void* Q, const voi
   a.K = K;
   a.V = V;
   a.O = O;
+  a.cus = sweep_slots() / 2;
   return a;
 }
 

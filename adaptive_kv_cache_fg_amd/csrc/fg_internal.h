@@ -122,6 +122,7 @@ struct AttentionArgs {
   void* O;           // [B*Hq*n, D] bf16
   float* lse2;       // [B*Hq*n] log2-domain row log-sum-exp, or nullptr
   float* lse_out;    // [B*Hq*n] natural-log copy, or nullptr
+  int cus;           // compute units of the device (steers the launch shape only)
 };
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t st);
 hipError_t launch_select(const ProfileArgs& a, hipStream_t st);

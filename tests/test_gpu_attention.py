@@ -2,7 +2,9 @@
 against the oracle's O = A V, on seeded synthetic layers: ragged shapes across
 several key tiles and row blocks, GQA groups, batch > 1, sharp score
 distributions (the lazy-rescale path), full Llama-1-7B layer size, and sampled
-rows at the 32k-token GQA size.  Tolerances are derived in gpu_parity_lib."""
+rows at the 32k-token GQA size.  The small and the Llama-1-7B shapes run the
+launch with two key groups per workgroup, the 32k shape the one with one.
+Tolerances are derived in gpu_parity_lib."""
 import numpy as np
 import pytest
 import torch
