@@ -21,6 +21,7 @@ namespace fg {
 
 constexpr int kPosChunk = 128;
 constexpr int kCopyBatch = 4;     // 16-byte chunks of K and of V per thread in flight in the gather's copy
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bool fbit(const uint32_t* fm, int j) { return (fm[j >> 5] >> (j & 31)) & 1u; }
 
@@ -392,10 +393,12 @@ __global__ __launch_bounds__(CHUNK) void gather_kernel(const T* __restrict__ K, 
       kr[u] = *reinterpret_cast<const uint4*>(ks8 + sb);
       vr[u] = *reinterpret_cast<const uint4*>(vs8 + sb);
     }
+    // non-temporal stores: the cache rows are not read again by this launch, and streaming them out
+    // past the caches measured 10-15 % faster than ordinary stores (non-temporal loads were slower)
 #pragma unroll
     for (int u = 0; u < kCopyBatch; ++u) {
-      *reinterpret_cast<uint4*>(kc8 + dd[u]) = kr[u];
-      *reinterpret_cast<uint4*>(vc8 + dd[u]) = vr[u];
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, kr[u]), reinterpret_cast<u32x4*>(kc8 + dd[u]));
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, vr[u]), reinterpret_cast<u32x4*>(vc8 + dd[u]));
     }
   }
 }
