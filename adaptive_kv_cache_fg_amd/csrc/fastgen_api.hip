@@ -187,6 +187,7 @@ size_t fg_profile_workspace_size(const fg_shape* s) {
   if (check_shape(s) != FG_OK) return 0;
   const size_t rows_q = (size_t)s->batch * s->n_q_heads * s->seq_len;
   const size_t rows_k = (size_t)s->batch * s->n_kv_heads * s->seq_len;
+  // buffer sizes do not depend on the slot count (it only steers the chunk size)
   const fg::SweepSplit sp = fg::sweep_split(s->batch, s->n_q_heads, s->n_kv_heads, s->seq_len, 512);
   return align256(rows_q * sizeof(float)) + align256(rows_k * sizeof(float)) + align256(sp.rs_bytes) +
          align256(sp.cs_bytes);

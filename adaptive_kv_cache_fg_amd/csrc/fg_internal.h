@@ -77,7 +77,8 @@ inline int choose_split_chunk(int n, int nblocks, long long mult, bool rows_of_k
       const int R = sweep_block_items(rows_of_key_block, n, i);
       const int c = split_count(R, S);
       count += c;
-      const int size = 32 * (((R + 31) / 32 + c - 1) / c) < R ? 32 * (((R + 31) / 32 + c - 1) / c) : R;
+      const int per = 32 * (((R + 31) / 32 + c - 1) / c);   // the largest of the c balanced chunks
+      const int size = per < R ? per : R;
       maxc = size > maxc ? size : maxc;
     }
     count *= mult;
