@@ -129,7 +129,7 @@ const char* fg_kernel_name(int32_t id) {
   static const char* names[FG_K_COUNT] = {"profile_rowstats", "profile_colsums", "profile_select",
                                           "compact_plan",     "compact_scan",    "compact_gather",
                                           "compact_worklist", "decode_partials", "decode_merge",
-                                          "attention",        "decode_track"};
+                                          "attention",        "decode_track",    "profile_rowbins"};
   return (id >= 0 && id < FG_K_COUNT) ? names[id] : "unknown";
 }
 
@@ -314,6 +314,36 @@ fg_status fg_attention(const fg_shape* shape, const void* Q, const void* K, cons
   a.lse_out = lse_out;
   const hipError_t e = fg::launch_attention(a, stream);
   if (e != hipSuccess) return hip_fail(e, "attention");
+  return FG_OK;
+}
+
+fg_status fg_profile_row_bins(const fg_shape* shape, const fg_params* params, const void* Q, const void* K,
+                              const uint8_t* token_class, const uint32_t* freq_mask, const float* lse, float* bins,
+                              hipStream_t stream) {
+  fg_status s = check_shape(shape);
+  if (s != FG_OK) return s;
+  if ((s = check_params(params)) != FG_OK) return s;
+  if (!Q || !K || !token_class || !freq_mask || !lse || !bins)
+    return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(Q) || !aligned16(K)) return fail(FG_ERR_INVALID_ARG, "Q and K must be 16-byte aligned");
+  if (shape->batch > 65535) return fail(FG_ERR_UNSUPPORTED, "more than 65535 batch entries");
+  fg::RowBinsArgs a{};
+  a.dtype = shape->dtype;
+  a.D = shape->head_dim;
+  a.B = shape->batch;
+  a.Hq = shape->n_q_heads;
+  a.Hkv = shape->n_kv_heads;
+  a.n = shape->seq_len;
+  int k_f = 0;
+  budgets(shape, params, &k_f, &a.w_l);
+  a.Q = Q;
+  a.K = K;
+  a.cls = token_class;
+  a.fmask = freq_mask;
+  a.lse = lse;
+  a.bins = bins;
+  const hipError_t e = fg::launch_rowbins(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "row bins");
   return FG_OK;
 }
 

@@ -126,6 +126,18 @@ struct AttentionArgs {
   int cus;           // compute units of the device (steers the launch shape only)
 };
 hipError_t launch_attention(const AttentionArgs& a, hipStream_t st);
+
+// Per-row level bins of the prompt's attention (one sweep over the causal scores).
+struct RowBinsArgs {
+  int dtype, D, B, Hq, Hkv, n, w_l;
+  const void* Q;
+  const void* K;
+  const uint8_t* cls;      // [B, n] token classes
+  const uint32_t* fmask;   // [B*Hkv, ceil(n/32)] frequent-set bits
+  const float* lse;        // [B*Hq*n] natural-log row log-sum-exp of the scaled scores
+  float* bins;             // [B*Hq*n, 5] special, punct, frequent, local, rest
+};
+hipError_t launch_rowbins(const RowBinsArgs& a, hipStream_t st);
 hipError_t launch_select(const ProfileArgs& a, hipStream_t st);
 hipError_t launch_head_map_accumulate(const float* recovery, const uint8_t* policy, double* rec_sum, int32_t* count,
                                       int P, int H, hipStream_t st);

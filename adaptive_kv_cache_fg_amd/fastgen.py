@@ -23,7 +23,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
           4: "cache capacity exceeded", 5: "HIP error"}
 DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 KERNEL_NAMES = ["profile_rowstats", "profile_colsums", "profile_select", "compact_plan", "compact_scan",
-                "compact_gather", "compact_worklist", "decode_partials", "decode_merge", "attention", "decode_track"]
+                "compact_gather", "compact_worklist", "decode_partials", "decode_merge", "attention", "decode_track",
+                "profile_rowbins"]
 
 
 class FgShape(ctypes.Structure):
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.fg_profile_attention.argtypes = [sh, pa, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     L.fg_profile_attention.restype = ctypes.c_int
     L.fg_attention.argtypes, L.fg_attention.restype = [sh, P, P, P, P, P, P], ctypes.c_int
+    L.fg_profile_row_bins.argtypes = [sh, pa, P, P, P, P, P, P, P]
+    L.fg_profile_row_bins.restype = ctypes.c_int
     L.fg_decode_step_dynamic.argtypes = [ca, P, P, P, P, P, I32, P, P, P, S, P]
     L.fg_decode_step_dynamic.restype = ctypes.c_int
     L.fg_decode_track_init.argtypes, L.fg_decode_track_init.restype = [ca, P, P, P], ctypes.c_int
@@ -215,6 +218,27 @@ def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, want_lse: bool 
     _check(lib().fg_attention(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse), _stream()),
            "fg_attention")
     return out, lse
+
+
+def row_bins(Q: torch.Tensor, K: torch.Tensor, token_class: torch.Tensor, prof: Profile) -> torch.Tensor:
+    """fg_profile_row_bins: [B, Hq, n, 5] attention mass of each query row on the special, punct,
+    frequent, local and remaining keys, from the frequent set and row log-sum-exps of ``prof``
+    (a profile of the same Q, K, classes, made with want_lse=True)."""
+    _need(Q, "Q")
+    _need(K, "K")
+    _need(token_class, "token_class", torch.uint8)
+    if prof.lse is None:
+        raise ValueError("row_bins needs the profile's row log-sum-exps: profile(..., want_lse=True)")
+    shape = make_shape(Q, K)
+    B, Hq, n, _ = Q.shape
+    if tuple(prof.lse.shape) != (B, Hq, n) or prof.freq_mask.shape[:2] != K.shape[:2]:
+        raise ValueError("the profile does not belong to these Q, K")
+    bins = torch.empty((B, Hq, n, 5), dtype=torch.float32, device=Q.device)
+    params = FgParams(prof.r_l, prof.r_f, prof.T)
+    _check(lib().fg_profile_row_bins(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), _ptr(K),
+                                     _ptr(token_class), _ptr(prof.freq_mask), _ptr(prof.lse), _ptr(bins),
+                                     _stream()), "fg_profile_row_bins")
+    return bins
 
 
 class HeadMap:

@@ -137,6 +137,28 @@ fg_status fg_profile_attention(const fg_shape* shape, const fg_params* params,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fg_profile_row_bins -- per query row, the attention mass on each shortlist
+ * level (hyper.ai summary of "Model Tells You What to Discard", Method: the
+ * constraint equation taken row by row, with the levels of the shortlist
+ * equation).  For batch entry b, query head hq (KV head h = hq / G) and row i:
+ *   bins[b,hq,i,l] = sum_{j <= i, level(i,j) = l} A_ij,  A_ij = softmax_j(q_i . k_j / sqrt(d)),
+ * level 0 special, 1 punct, 2 frequent (j in F of (b,h)), 3 local (i - j < w_l,
+ * w_l = floor(r_l n)), 4 the rest; a key takes the first level that holds it.
+ * Summed over the rows and the G query heads of (b,h) and divided by G n, the
+ * running sums of bins[..., 0..k] are fg_profile's recovery R_k; per row they
+ * give the kept share of each row (the worst-served rows of a head).
+ * Q, K, token_class as fg_profile (16-byte aligned Q, K); freq_mask and lse
+ * as fg_profile's outputs for the same inputs and params (lse: its lse_out,
+ * [B*Hq*n] fp32 natural log).  bins [B*Hq*n*5] fp32, caller-allocated.  Only
+ * params->r_l is read (T and r_f are checked but unused).  No workspace.
+ * FG_ERR_INVALID_ARG for NULL pointers or misaligned Q, K; FG_ERR_UNSUPPORTED
+ * for shapes fg_profile rejects or more than 65535 batch entries.
+ */
+fg_status fg_profile_row_bins(const fg_shape* shape, const fg_params* params, const void* Q, const void* K,
+                              const uint8_t* token_class, const uint32_t* freq_mask, const float* lse, float* bins,
+                              hipStream_t stream);
+
+/*
  * Multi-prompt head map (jisaku.com glossary entry "FastGen", section
  * Profiling phase: heads are typed once from sample prompts, the map is saved
  * and applied at inference).  Profile P prompts (one fg_profile call with
@@ -350,7 +372,8 @@ enum {
   FG_K_ROWSTATS = 0, FG_K_COLSUMS = 1, FG_K_SELECT = 2, FG_K_PLAN = 3, FG_K_SCAN = 4,
   FG_K_GATHER = 5,     /* also writes the decode work list */
   FG_K_WORKLIST = 6,   /* reserved: no separate launch */
-  FG_K_DECODE = 7, FG_K_DECODE_MERGE = 8, FG_K_ATTENTION = 9, FG_K_TRACK = 10, FG_K_COUNT = 11
+  FG_K_DECODE = 7, FG_K_DECODE_MERGE = 8, FG_K_ATTENTION = 9, FG_K_TRACK = 10,
+  FG_K_ROWBINS = 11, FG_K_COUNT = 12
 };
 void fg_kernel_timing_enable(int enable);
 int32_t fg_kernel_timing_read(int32_t* kernel_ids, float* ms, int32_t max);
