@@ -63,7 +63,9 @@ __global__ __launch_bounds__(256, 2) void rowbins_kernel(const T* __restrict__ Q
   constexpr int NK = D / M::KS;
   constexpr int kRB = D * (int)sizeof(T) + kPadBytes;
   __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kBinKeyTile * kRB];
-  __shared__ __attribute__((aligned(16))) uint16_t ind[2][6][kBinKeyTile];   // levels 0..3, all ones, all zeros
+  // indicator rows: levels 0..3, all ones, all zeros; the row stride is padded by 16 bytes so that the
+  // lanes reading the same keys of different rows hit different banks
+  __shared__ __attribute__((aligned(16))) uint16_t ind[2][6][kBinKeyTile + 8];
   __shared__ __attribute__((aligned(16))) uint8_t kcode[2][kBinKeyTile];
 
   const int hq = (int)(blockIdx.x % Hq), rb = n_rb - 1 - (int)(blockIdx.x / Hq);   // heaviest row blocks first

@@ -155,6 +155,9 @@ def prompt_attention(torch, fg, Qd, Kd, Vd, cls, spec, T, sweep_flops, reps=20) 
     attn_us = time_graph(lambda: fg.attention(Qd, Kd, Vd, out=O))
     fused_us = time_graph(lambda: fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T, V=Vd))
     prof_us = time_graph(lambda: fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T))
+    # the optional per-row level bins (a third sweep; not part of the profiling step)
+    lprof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T, want_lse=True)
+    bins_us = time_graph(lambda: fg.row_bins(Qd, Kd, cls, lprof))
     # the fused call gives the same attention output and the same decisions as the two separate calls
     fused = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T, V=Vd)
     plain = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T)
@@ -199,6 +202,8 @@ def prompt_attention(torch, fg, Qd, Kd, Vd, cls, spec, T, sweep_flops, reps=20) 
         "attention_kernel": {"avg_us": kern["attention"], "algorithmic_flops": attn_flops, "achieved": ach,
                              "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_MFMA_PEAK_TFLOPS},
         "fused_kernels_us": kern,
+        "row_bins_us": bins_us,
+        "row_bins_score_tflops": sweep_flops / (bins_us * 1e-6) / 1e12,
         "torch_sdpa_us": sdpa_us,
         "prompt_tok_s_attention_only": B * n / (attn_us * 1e-6),
         "prompt_tok_s_attention_with_profiling": B * n / (fused_us * 1e-6),
