@@ -120,6 +120,24 @@ def test_attention_rejects_bad_arguments():
     assert L.fg_profile_attention(*args, p, p, o, p, p, p, p, None, None, p, need - 1, None) == 3
 
 
+def test_row_bins_rejects_bad_arguments():
+    """fg_profile_row_bins checks its arguments before any launch (no GPU needed)."""
+    L = fgb.lib()
+    p = ctypes.c_void_p(0x1000)
+    sh = fgb.FgShape(1, 4, 4, 16, 128, 0)
+    params = fgb.FgParams(0.3, 0.3, 0.95)
+    call = L.fg_profile_row_bins
+    assert call(ctypes.byref(sh), ctypes.byref(params), p, p, p, p, None, p, None) == 1           # no lse
+    assert call(ctypes.byref(sh), ctypes.byref(params), p, p, p, None, p, p, None) == 1           # no freq_mask
+    assert call(ctypes.byref(sh), ctypes.byref(params), p, p, p, p, p, None, None) == 1           # no bins
+    assert call(ctypes.byref(sh), ctypes.byref(params), ctypes.c_void_p(0x1004), p, p, p, p, p, None) == 1
+    assert call(ctypes.byref(fgb.FgShape(1, 4, 4, 16, 96, 0)), ctypes.byref(params), p, p, p, p, p, p, None) == 2
+    assert call(ctypes.byref(fgb.FgShape(70000, 1, 1, 16, 64, 0)), ctypes.byref(params), p, p, p, p, p, p,
+                None) == 2
+    assert call(ctypes.byref(sh), ctypes.byref(fgb.FgParams(0.3, 0.3, 0.0)), p, p, p, p, p, p, None) == 1
+    assert call(None, ctypes.byref(params), p, p, p, p, p, p, None) == 1
+
+
 def test_head_map_rejects_bad_arguments():
     L = fgb.lib()
     p = ctypes.c_void_p(0x1000)
