@@ -102,3 +102,35 @@ def test_row_bins_needs_lse():
     prof = fg.profile(Q, K, cls, spec.r_l, spec.r_f, spec.T[0])
     with pytest.raises(ValueError):
         fg.row_bins(Q, K, cls, prof)
+
+
+def test_row_bins_long_gqa_sampled_rows():
+    """The 32k GQA shape (32 query heads on 8 KV heads, n = 32768): rows sum to 1 and
+    reproduce fg_profile's recovery on every head; on sampled rows of three query heads the
+    special and punct bins (which do not depend on the frequent set) match the oracle's
+    attention row restricted to those classes."""
+    print("[rowbins] long GQA n=32768, sampled rows", flush=True)
+    spec = syn.CONFIGS[4]
+    li = syn.make_layer(spec)
+    Q, K = _upload(li.Q, spec.dtype), _upload(li.K, spec.dtype)
+    cls = torch.from_numpy(li.token_class).cuda()
+    prof = fg.profile(Q, K, cls, spec.r_l, spec.r_f, spec.T[0], want_lse=True)
+    bins_d = fg.row_bins(Q, K, cls, prof)
+    rec = prof.recovery.cpu().numpy()
+    bins = bins_d.cpu().numpy().astype(np.float64)
+    del bins_d
+    B, Hq, n, _ = bins.shape
+    G = Hq // spec.n_kv_heads
+    np.testing.assert_allclose(bins.sum(axis=-1), 1.0, atol=BIN_TOL)
+    per_head = bins.reshape(B, spec.n_kv_heads, G * n, 5).sum(axis=2) / (G * n)
+    np.testing.assert_allclose(np.cumsum(per_head, axis=-1)[..., :4], rec[..., :4], atol=1e-4)
+    rng = np.random.default_rng(44)
+    c = li.token_class[0]
+    for hq in (0, 13, 31):
+        h = hq // G
+        for i in sorted(set(rng.integers(0, n, size=6).tolist()) | {0, n - 1}):
+            A = ref.causal_attention_rows(li.Q[0, hq, i:i + 1].astype(np.float64), li.K[0, h].astype(np.float64), i)[0]
+            want0 = A[c == ref.TOKEN_SPECIAL].sum()
+            want1 = A[c == ref.TOKEN_PUNCT].sum()
+            assert abs(bins[0, hq, i, 0] - want0) <= BIN_TOL, (hq, i)
+            assert abs(bins[0, hq, i, 1] - want1) <= BIN_TOL, (hq, i)
