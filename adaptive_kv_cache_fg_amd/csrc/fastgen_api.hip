@@ -327,6 +327,8 @@ fg_status fg_profile_row_bins(const fg_shape* shape, const fg_params* params, co
     return fail(FG_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(Q) || !aligned16(K)) return fail(FG_ERR_INVALID_ARG, "Q and K must be 16-byte aligned");
   if (shape->batch > 65535) return fail(FG_ERR_UNSUPPORTED, "more than 65535 batch entries");
+  if ((double)shape->n_q_heads * ((shape->seq_len + 255) / 256) * 256 > 4294967295.0)
+    return fail(FG_ERR_UNSUPPORTED, "too many query heads x row blocks for one launch");
   fg::RowBinsArgs a{};
   a.dtype = shape->dtype;
   a.D = shape->head_dim;

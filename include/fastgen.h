@@ -152,7 +152,8 @@ fg_status fg_profile_attention(const fg_shape* shape, const fg_params* params,
  * [B*Hq*n] fp32 natural log).  bins [B*Hq*n*5] fp32, caller-allocated.  Only
  * params->r_l is read (T and r_f are checked but unused).  No workspace.
  * FG_ERR_INVALID_ARG for NULL pointers or misaligned Q, K; FG_ERR_UNSUPPORTED
- * for shapes fg_profile rejects or more than 65535 batch entries.
+ * for shapes fg_profile rejects, more than 65535 batch entries, or more than
+ * 2^32 threads in one launch (256 per query head and 256-row block).
  */
 fg_status fg_profile_row_bins(const fg_shape* shape, const fg_params* params, const void* Q, const void* K,
                               const uint8_t* token_class, const uint32_t* freq_mask, const float* lse, float* bins,

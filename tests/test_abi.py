@@ -135,6 +135,8 @@ def test_row_bins_rejects_bad_arguments():
     assert call(ctypes.byref(fgb.FgShape(70000, 1, 1, 16, 64, 0)), ctypes.byref(params), p, p, p, p, p, p,
                 None) == 2
     assert call(ctypes.byref(sh), ctypes.byref(fgb.FgParams(0.3, 0.3, 0.0)), p, p, p, p, p, p, None) == 1
+    assert call(ctypes.byref(fgb.FgShape(1, 1024, 128, 1 << 24, 64, 0)), ctypes.byref(params), p, p, p, p, p, p,
+                None) == 2                                                                     # grid too large
     assert call(None, ctypes.byref(params), p, p, p, p, p, p, None) == 1
 
 
