@@ -158,11 +158,16 @@ class Profile:
 
 
 def profile(Q: torch.Tensor, K: torch.Tensor, token_class: torch.Tensor, r_l: float, r_f: float, T: float,
-            want_lse: bool = False, want_band: bool = False, V: Optional[torch.Tensor] = None) -> Profile:
+            want_lse: bool = False, want_band: bool = False, V: Optional[torch.Tensor] = None,
+            policy_out: Optional[torch.Tensor] = None) -> Profile:
     """fg_profile: per (b, KV head) cumulative scores, frequent set, recovery R_0..R_4 and policy.
 
     With V (bf16 only) this is fg_profile_attention: the prompt's attention
     output is computed in the same pass and returned as ``Profile.out``.
+    ``policy_out`` (uint8, B*Hkv elements, contiguous) receives the policies in
+    place of a new tensor: passing a cache's policy buffer (``cache.t["policy"]``)
+    lets ``compact(..., reuse=cache)`` skip its copy of the policies; that cache
+    is then stale until the compaction refills it.
     """
     _need(Q, "Q")
     _need(K, "K")
@@ -171,7 +176,13 @@ def profile(Q: torch.Tensor, K: torch.Tensor, token_class: torch.Tensor, r_l: fl
     B, Hq, n, _ = Q.shape
     Hkv = K.shape[1]
     dev = Q.device
-    policy = torch.empty((B, Hkv), dtype=torch.uint8, device=dev)
+    if policy_out is None:
+        policy = torch.empty((B, Hkv), dtype=torch.uint8, device=dev)
+    else:
+        _need(policy_out, "policy_out", torch.uint8)
+        if policy_out.numel() != B * Hkv:
+            raise ValueError(f"policy_out must hold {B * Hkv} elements")
+        policy = policy_out.view(B, Hkv)
     cum = torch.empty((B, Hkv, n), dtype=torch.float32, device=dev)
     rec = torch.empty((B, Hkv, 5), dtype=torch.float32, device=dev)
     fmask = torch.empty((B, Hkv, (n + 31) // 32), dtype=torch.int32, device=dev)
@@ -441,8 +452,10 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
                              _ptr(prof.freq_mask), int(max_new_tokens), int(max_new_kept), _ptr(kept_count),
                              _ptr(ring), _ptr(capacity), _ptr(row_offset), _ptr(work_offset), _ptr(totals),
                              _stream()), "fg_compact_plan")
+    same_policy = reuse is not None and prof.policy.data_ptr() == reuse.t["policy"].data_ptr()
     if reuse is not None and not check:
-        reuse.t["policy"].copy_(prof.policy.reshape(-1))
+        if not same_policy:
+            reuse.t["policy"].copy_(prof.policy.reshape(-1))
         _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),
                             _ptr(reuse.t["policy"]), _ptr(prof.freq_mask), ctypes.byref(reuse.c), _stream()),
                "fg_compact")
@@ -452,7 +465,8 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
         c = reuse.c
         if total_rows > c.total_rows or n_work > c.n_work or per_head > c.items_per_head:
             raise ValueError("reuse: the new plan does not fit the cache's buffers")
-        reuse.t["policy"].copy_(prof.policy.reshape(-1))
+        if not same_policy:
+            reuse.t["policy"].copy_(prof.policy.reshape(-1))
         _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),
                             _ptr(reuse.t["policy"]), _ptr(prof.freq_mask), ctypes.byref(c), _stream()), "fg_compact")
         return reuse

@@ -354,7 +354,9 @@ def main() -> int:
     B, Hq, n, d = li.Q.shape
 
     def prompt_phase(reuse=None, check=True):
-        prof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T)
+        # refilling a cache: the profile writes its policies straight into the cache's buffer
+        prof = fg.profile(Qd, Kd, cls, spec.r_l, spec.r_f, T,
+                          policy_out=None if reuse is None else reuse.t["policy"])
         cache = fg.compact(Kd, Vd, cls, prof, Hq, max_new_tokens=steps_dec, max_new_kept=max_new_kept,
                            reuse=reuse, check=check)
         return prof, cache

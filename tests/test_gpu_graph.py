@@ -87,3 +87,46 @@ def test_decode_partials_leaves_the_cache_unchanged():
     for t in range(steps):
         cache.decode_partials(qs[t])                  # repeated: still no effect
         assert torch.equal(cache.decode_step(qs[t], ks[t], vs[t], ncs[t]), ref_out[t]), t
+
+
+def test_prompt_graph_with_policies_written_into_the_cache():
+    """The prompt phase captured as a graph, with the profile writing its policies straight
+    into the cache's policy buffer (no copy): every replay, after eager profiles that overwrite
+    that buffer with other policies, restores the policies and kept sets of the eager run."""
+    hq = hkv = 4
+    spec = syn.custom_spec(syn.CONFIGS[1], seq_len=900, n_q_heads=hq, n_kv_heads=hkv, mix="fixed",
+                           fixed_types=("special", "punct", "local", "none"), batch=2)
+    steps = 8
+    print(f"[graph] prompt phase, policies in place, n={spec.seq_len}", flush=True)
+    li = syn.make_layer(spec, 0)
+    Q, K, V = (_upload(x, spec.dtype) for x in (li.Q, li.K, li.V))
+    cls = torch.from_numpy(li.token_class).cuda()
+    T = spec.T[0]
+    prof = fg.profile(Q, K, cls, spec.r_l, spec.r_f, T)
+    cache = fg.compact(K, V, cls, prof, hq, max_new_tokens=steps)
+    torch.cuda.synchronize()
+    pol0 = prof.policy.reshape(-1).clone()
+    kept0 = cache.kept_positions()
+    assert torch.equal(cache.t["policy"], pol0)
+
+    def prompt():
+        p = fg.profile(Q, K, cls, spec.r_l, spec.r_f, T, policy_out=cache.t["policy"])
+        fg.compact(K, V, cls, p, hq, max_new_tokens=steps, reuse=cache, check=False)
+
+    prompt()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        prompt()
+    torch.cuda.synchronize()
+    Qx = torch.flip(Q, dims=[2]).contiguous()                 # other scores, other policies
+    for rep in range(3):
+        other = fg.profile(Qx, K, cls, spec.r_l, spec.r_f, 0.01, policy_out=cache.t["policy"])
+        torch.cuda.synchronize()
+        assert other.policy.data_ptr() == cache.t["policy"].data_ptr()
+        assert not torch.equal(cache.t["policy"], pol0), "the eager profile should change the policies"
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cache.t["policy"], pol0), rep
+        kept = cache.kept_positions()
+        assert all(np.array_equal(a, b) for a, b in zip(kept, kept0)), rep
