@@ -134,3 +134,13 @@ def test_row_bins_long_gqa_sampled_rows():
             want1 = A[c == ref.TOKEN_PUNCT].sum()
             assert abs(bins[0, hq, i, 0] - want0) <= BIN_TOL, (hq, i)
             assert abs(bins[0, hq, i, 1] - want1) <= BIN_TOL, (hq, i)
+
+
+@pytest.mark.parametrize("r_l,r_f", [(0.0, 0.0), (1.0, 1.0), (0.004, 0.3), (0.3, 0.0)])
+def test_row_bins_degenerate_budgets(r_l, r_f):
+    """No local window (w_l = 0), a window covering every pair (w_l = n), a one-key window,
+    an empty frequent set."""
+    print(f"[rowbins] budgets r_l={r_l} r_f={r_f}", flush=True)
+    spec = syn.custom_spec(syn.CONFIGS[1], seq_len=260, n_q_heads=4, n_kv_heads=4, mix="fixed",
+                           fixed_types=("special", "punct", "local", "none"), r_l=r_l, r_f=r_f)
+    _run(spec)
