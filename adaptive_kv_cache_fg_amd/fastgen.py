@@ -180,8 +180,8 @@ def profile(Q: torch.Tensor, K: torch.Tensor, token_class: torch.Tensor, r_l: fl
         policy = torch.empty((B, Hkv), dtype=torch.uint8, device=dev)
     else:
         _need(policy_out, "policy_out", torch.uint8)
-        if policy_out.numel() != B * Hkv:
-            raise ValueError(f"policy_out must hold {B * Hkv} elements")
+        if policy_out.numel() != B * Hkv or policy_out.device != dev:
+            raise ValueError(f"policy_out must hold {B * Hkv} elements on {dev}")
         policy = policy_out.view(B, Hkv)
     cum = torch.empty((B, Hkv, n), dtype=torch.float32, device=dev)
     rec = torch.empty((B, Hkv, 5), dtype=torch.float32, device=dev)
