@@ -64,7 +64,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     int32_t* __restrict__ pos, const int64_t* __restrict__ row_offset, int32_t* __restrict__ len,
     const int32_t* __restrict__ capacity, const int32_t* __restrict__ ring, const uint8_t* __restrict__ policy,
     uint32_t* __restrict__ error_word, float* __restrict__ score, const uint8_t* __restrict__ cls_all, int n_total,
-    int Hkv, int w_l, int p, int S, int CH, int64_t total_rows, float c) {
+    int Hkv, int w_l, int p, int S, int CH, int64_t total_rows, int64_t n_work, float c) {
   static_assert(NT % D == 0, "one output per thread");
   constexpr int NGRP = NT / D;                     // thread groups splitting the item list
   constexpr int kBatch = kMergeBatch;
@@ -79,13 +79,16 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
   const float* hpart = part + (size_t)hd * S * G * (D + 2) + (size_t)g * (D + 2);   // slot k at k * G * (D + 2)
 
   // ---- every load up front, unconditional (straight-line code, so none waits on another)
-  const int64_t w0 = work_offset[hd];
-  const int n_items = (int)min<int64_t>(work_offset[hd + 1] - w0, S);   // more only if the plan did not fit
+  const int64_t w0 = work_offset[hd], w1 = work_offset[hd + 1];
   const int pol = policy[hd];
   const uint8_t cls = HAS_CLASS ? new_class[hd / Hkv] : kNormal;
   const int R = ring[hd];
   const int64_t base_h = row_offset[hd];
-  const bool fits = row_offset[hd + 1] <= total_rows;   // else the plan did not fit: no update
+  // the head's rows, its work items and its partial slots all lie inside the cache's buffers (the
+  // compaction's own test): else the plan did not fit (error bit 2), the head's items are empty,
+  // none of its slots is merged and its cache gets no update
+  const bool fits = row_offset[hd + 1] <= total_rows && w1 <= n_work && w1 - w0 <= S;
+  const int n_items = fits ? (int)(w1 - w0) : 0;
   const int cap = capacity[hd];
   const int L = len[hd];
   const float qv = to_f32(q[(size_t)qh * D + dd]);
@@ -405,7 +408,7 @@ static hipError_t launch_decode_tg(const DecodeArgs& a, hipStream_t st) {
     kern<<<dim3(H * G), dim3(small ? 512 : 1024), 0, st>>>(
         (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work_offset, a.work,
         (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.error_word, a.score,
-        a.cls_all, a.n_total, a.Hkv, a.w_l, a.p, a.items_per_head, a.chunk_rows, a.total_rows, c);
+        a.cls_all, a.n_total, a.Hkv, a.w_l, a.p, a.items_per_head, a.chunk_rows, a.total_rows, a.n_work, c);
     timed_end(st);
     e = hipGetLastError();
   }

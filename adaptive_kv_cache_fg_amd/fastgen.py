@@ -421,9 +421,13 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
     """fg_compact_plan + one read of the totals + fg_compact: the ragged cache of one layer.
 
     With ``reuse``, that cache's buffers are refilled in place (same device addresses, so a
-    captured decode graph stays valid).  ``check=False`` (reuse only) skips the read of the new
-    totals, so nothing synchronises the host and the call can be captured in a graph; a plan
-    that does not fit the buffers then shows up as bit 2 of ``error_bits()``.
+    captured decode graph stays valid).  ``check=True`` plans into scratch tensors, reads the
+    totals and copies the plan into the cache only when it fits; a plan that does not fit raises
+    ValueError and leaves the cache's plan and rows untouched (if the profile already wrote its
+    policies into the cache's buffer, the cache is marked unusable: decoding it fails until a
+    compaction refills it).  ``check=False`` (reuse only) plans straight into the cache and skips
+    the read of the new totals, so nothing synchronises the host and the call can be captured in
+    a graph; a plan that does not fit the buffers then shows up as bit 2 of ``error_bits()``.
     """
     _need(K, "K")
     _need(V, "V", K.dtype)
@@ -441,16 +445,19 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
         if (reuse.shape.batch, reuse.shape.n_kv_heads, reuse.shape.seq_len, reuse.shape.head_dim,
                 reuse.shape.n_q_heads) != (B, Hkv, n, d, n_q_heads) or reuse.t["k"].dtype != K.dtype:
             raise ValueError("reuse: cache shape does not match")
-        kept_count, ring, capacity = reuse.kept_count, reuse.t["ring"], reuse.t["capacity"]
-        row_offset, work_offset, totals = reuse.t["row_offset"], reuse.t["work_offset"], reuse.t["totals"]
+    if reuse is not None and not check:
+        plan = {"kept_count": reuse.kept_count, "ring": reuse.t["ring"], "capacity": reuse.t["capacity"],
+                "row_offset": reuse.t["row_offset"], "work_offset": reuse.t["work_offset"],
+                "totals": reuse.t["totals"]}
     else:
-        kept_count, ring, capacity = torch.empty(H, **i32), torch.empty(H, **i32), torch.empty(H, **i32)
-        row_offset, work_offset = torch.empty(H + 1, **i64), torch.empty(H + 1, **i64)
-        totals = torch.empty(3, **i64)
+        plan = {"kept_count": torch.empty(H, **i32), "ring": torch.empty(H, **i32),
+                "capacity": torch.empty(H, **i32), "row_offset": torch.empty(H + 1, **i64),
+                "work_offset": torch.empty(H + 1, **i64), "totals": torch.empty(3, **i64)}
     L = lib()
     _check(L.fg_compact_plan(ctypes.byref(shape), ctypes.byref(params), _ptr(token_class), _ptr(prof.policy),
-                             _ptr(prof.freq_mask), int(max_new_tokens), int(max_new_kept), _ptr(kept_count),
-                             _ptr(ring), _ptr(capacity), _ptr(row_offset), _ptr(work_offset), _ptr(totals),
+                             _ptr(prof.freq_mask), int(max_new_tokens), int(max_new_kept),
+                             _ptr(plan["kept_count"]), _ptr(plan["ring"]), _ptr(plan["capacity"]),
+                             _ptr(plan["row_offset"]), _ptr(plan["work_offset"]), _ptr(plan["totals"]),
                              _stream()), "fg_compact_plan")
     same_policy = reuse is not None and prof.policy.data_ptr() == reuse.t["policy"].data_ptr()
     if reuse is not None and not check:
@@ -460,11 +467,16 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
                             _ptr(reuse.t["policy"]), _ptr(prof.freq_mask), ctypes.byref(reuse.c), _stream()),
                "fg_compact")
         return reuse
-    total_rows, n_work, per_head = (int(x) for x in totals.cpu().tolist())   # the one host synchronisation
+    total_rows, n_work, per_head = (int(x) for x in plan["totals"].cpu().tolist())   # the one host synchronisation
     if reuse is not None:
         c = reuse.c
         if total_rows > c.total_rows or n_work > c.n_work or per_head > c.items_per_head:
+            if same_policy:
+                c.next_pos = -1        # its policies are the new prompt's, its rows the old one's: unusable
             raise ValueError("reuse: the new plan does not fit the cache's buffers")
+        reuse.kept_count.copy_(plan["kept_count"])
+        for name in ("ring", "capacity", "row_offset", "work_offset", "totals"):
+            reuse.t[name].copy_(plan[name])
         if not same_policy:
             reuse.t["policy"].copy_(prof.policy.reshape(-1))
         _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),
@@ -474,9 +486,9 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
         "k": torch.empty((max(total_rows, 1), d), dtype=K.dtype, device=dev),
         "v": torch.empty((max(total_rows, 1), d), dtype=K.dtype, device=dev),
         "pos": torch.empty(max(total_rows, 1), **i32),
-        "row_offset": row_offset, "len": torch.empty(H, **i32), "capacity": capacity, "ring": ring,
-        "policy": prof.policy.reshape(-1).clone(), "work_offset": work_offset, "totals": totals,
-        "work": torch.empty(max(4 * n_work, 4), **i32),
+        "row_offset": plan["row_offset"], "len": torch.empty(H, **i32), "capacity": plan["capacity"],
+        "ring": plan["ring"], "policy": prof.policy.reshape(-1).clone(), "work_offset": plan["work_offset"],
+        "totals": plan["totals"], "work": torch.empty(max(4 * n_work, 4), **i32),
         "error_word": torch.empty(1, **i32),
     }
     c = FgCache()
@@ -486,7 +498,7 @@ def compact(K: torch.Tensor, V: torch.Tensor, token_class: torch.Tensor, prof: P
     c.total_rows, c.n_work, c.items_per_head = total_rows, n_work, per_head
     _check(L.fg_compact(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(token_class),
                         _ptr(t["policy"]), _ptr(prof.freq_mask), ctypes.byref(c), _stream()), "fg_compact")
-    return Cache(shape, t, c, kept_count)
+    return Cache(shape, t, c, plan["kept_count"])
 
 
 def kept_counts(K: torch.Tensor, token_class: torch.Tensor, prof: Profile, n_q_heads: int) -> torch.Tensor:

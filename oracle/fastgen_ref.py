@@ -292,6 +292,15 @@ class HeadProfile:
 
 
 def topk_tie_flag(cum: np.ndarray, k_f: int, tau: float) -> tuple:
+    """(flag, relative gap) of the frequent set's boundary.
+
+    With the scores sorted in descending order, s_(k) is the k-th largest (the
+    weakest key of F) and s_(k+1) the largest key left out.  The choice of F is
+    fragile under rounding when s_(k) - s_(k+1) <= tau * s_(k), or when s_(k)
+    has underflowed below 2^-100 (every score of the boundary is then a rounding
+    residue).  With no boundary (k_f <= 0 or k_f >= n) F is every key or none
+    and nothing is flagged.
+    """
     n = len(cum)
     if k_f <= 0 or k_f >= n:
         return False, float("inf")
@@ -299,6 +308,14 @@ def topk_tie_flag(cum: np.ndarray, k_f: int, tau: float) -> tuple:
     sk, sk1 = s[k_f - 1], s[k_f]
     gap = (sk - sk1) / sk if sk > 0 else 0.0
     return bool(sk - sk1 <= tau * sk or sk < UNDERFLOW_FLOOR), float(gap)
+
+
+def near_t_flag(R: np.ndarray, T: float) -> bool:
+    """A policy choice that rounding could change: some R_k of the four partial
+    shortlist entries (k = 0..3) lies within NEAR_T_WINDOW of T.  R_4 = 1 by
+    definition and never decides, so it is not tested."""
+    R = np.asarray(R, dtype=np.float64)
+    return bool(np.any(np.abs(R[:LEVEL_FULL] - T) <= NEAR_T_WINDOW))
 
 
 def profile_head(Qg: np.ndarray, K: np.ndarray, cls: np.ndarray, r_l: float, r_f: float, T: float,
@@ -314,7 +331,7 @@ def profile_head(Qg: np.ndarray, K: np.ndarray, cls: np.ndarray, r_l: float, r_f
     R = recovery_from_bins(bins)
     policy = select_policy(R, T)
     kept = kept_positions(cls, F, w_l, policy)
-    near = bool(np.any(np.abs(R[:LEVEL_FULL] - T) <= NEAR_T_WINDOW))
+    near = near_t_flag(R, T)
     tie, gap = topk_tie_flag(cs["cum"], k_f, tau)
     return HeadProfile(k_f, w_l, cs["lse"], cs["cum"], cs["band"], F, bins, R, policy, kept, near, tie, gap)
 

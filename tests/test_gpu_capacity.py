@@ -4,6 +4,8 @@ fg_compact treats the cache's total_rows / n_work / items_per_head as capacities
 a smaller plan refills the buffers exactly like a fresh cache, and a plan that
 does not fit sets bit 2 of error_word and leaves those heads empty, with every
 write inside the buffers (the kernels bound-check against the capacities)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -89,3 +91,72 @@ def test_unwritten_ring_rows_do_not_leak_into_outputs():
         b = dirty.decode_step(qs[t], ks[t], vs[t], ncs[t])
         assert torch.isfinite(b).all(), t
         assert torch.equal(a, b), t
+
+
+def test_refill_whose_rows_fit_but_items_do_not():
+    """A refill plan with room for its rows but more decode work items than the cache holds:
+    the heads past the item capacity get no cache update (no write past the work list), the
+    error word reports the plan, and the heads that fit decode exactly like a fresh cache."""
+    spec = syn.custom_spec(syn.CONFIGS[1], seq_len=200, n_q_heads=4, n_kv_heads=4, mix="fixed",
+                           fixed_types=("none", "none", "none", "none"), batch=1)
+    li = syn.make_layer(spec, 0)
+    Q, K, V = (_upload(x, spec.dtype) for x in (li.Q, li.K, li.V))
+    cls = torch.from_numpy(li.token_class).cuda()
+    n_special = int(np.count_nonzero(li.token_class == syn.TOKEN_SPECIAL))
+    assert n_special == 2
+    prof = fg.profile(Q, K, cls, spec.r_l, spec.r_f, 0.95)
+    pol = lambda *p: torch.tensor(p, dtype=torch.uint8, device="cuda")      # noqa: E731
+    old = fg.apply_head_map(prof, pol(4, 4, 0, 0))
+    new = fg.apply_head_map(prof, pol(4, 4, 4, 0))
+    print(f"[capacity] rows fit, work items do not, n={spec.seq_len}", flush=True)
+    cache = fg.compact(K, V, cls, old, 4, max_new_tokens=184, max_new_kept=2)
+    assert fg.lib().fg_decode_chunk_rows(ctypes.byref(cache.shape)) == 128
+    assert cache.t["capacity"].cpu().tolist() == [384, 384, 4, 4]
+    assert (cache.c.total_rows, cache.c.n_work, cache.c.items_per_head) == (776, 8, 3)
+    fresh = fg.compact(K, V, cls, new, 4, max_new_tokens=57, max_new_kept=3)
+    assert fresh.t["capacity"].cpu().tolist() == [257, 257, 257, 5]
+    assert (fresh.c.total_rows, fresh.c.n_work, fresh.c.items_per_head) == (776, 10, 3)
+    # the cache's work list followed by a guard band inside the same allocation
+    nw = int(cache.c.n_work)
+    sentinel = 0x5A5A5A5A
+    work = torch.full((4 * nw + 256,), sentinel, dtype=torch.int32, device="cuda")
+    work[: 4 * nw] = cache.t["work"][: 4 * nw]
+    cache.t["work"] = work
+    cache.c.work = work.data_ptr()
+    fg.compact(K, V, cls, new, 4, max_new_tokens=57, max_new_kept=3, reuse=cache, check=False)
+    ds = syn.make_decode_stream(spec, 0, 3)
+    special = torch.ones(1, dtype=torch.uint8, device="cuda")               # every head appends the token
+    for t in range(3):
+        q, k, v = (_upload(x[t], spec.dtype) for x in (ds.q, ds.k, ds.v))
+        got = cache.decode_step(q, k, v, special)
+        want = fresh.decode_step(q, k, v, special)
+        assert torch.isfinite(got).all(), t
+        assert torch.equal(got[:, :2], want[:, :2]), t                      # heads 0 and 1 fit
+    torch.cuda.synchronize()
+    assert bool((work[4 * nw:] == sentinel).all()), "a write landed past the work list"
+    assert cache.error_bits() & 2
+    for h in (0, 1):
+        assert np.array_equal(cache.kept_positions()[h], fresh.kept_positions()[h]), h
+
+
+def test_failed_checked_refill_cannot_be_decoded():
+    """compact(reuse=..., check=True) with a plan that does not fit raises, and when the profile
+    already wrote its policies into the cache, decoding that cache is refused until a refill."""
+    steps = 4
+    spec, K, V, cls, qs, ks, vs, ncs, small, big = _setup(steps)
+    print(f"[capacity] failed checked refill, n={spec.seq_len}", flush=True)
+    Q = _upload(syn.make_layer(spec, 0).Q, spec.dtype)
+    cache = fg.compact(K, V, cls, small, 8, max_new_tokens=steps)
+    want = cache.decode_step(qs[0], ks[0], vs[0], ncs[0]).clone()
+    row_offset = cache.t["row_offset"].clone()
+    prof = fg.profile(Q, K, cls, spec.r_l, spec.r_f, 1.0, policy_out=cache.t["policy"])
+    with pytest.raises(ValueError):
+        fg.compact(K, V, cls, prof, 8, max_new_tokens=steps, reuse=cache, check=True)
+    assert torch.equal(cache.t["row_offset"], row_offset)                  # the plan was not copied in
+    with pytest.raises(fg.FastGenError):
+        cache.decode_step(qs[0], ks[0], vs[0], ncs[0])
+    # a fitting refill makes it usable again
+    fg.compact(K, V, cls, small, 8, max_new_tokens=steps, reuse=cache, check=True)
+    got = cache.decode_step(qs[0], ks[0], vs[0], ncs[0])
+    assert torch.equal(got, want)
+    assert cache.error_bits() == 0
