@@ -625,6 +625,36 @@ fg_status fg_decode_track(const fg_cache* cache, const void* q, const uint8_t* t
   return FG_OK;
 }
 
+fg_status fg_peak_mfma_bf16(const void* operands, float* out, int32_t iters, int32_t blocks, hipStream_t stream) {
+  if (!operands || !out) return fail(FG_ERR_INVALID_ARG, "operands and out must not be NULL");
+  if (!aligned16(operands)) return fail(FG_ERR_INVALID_ARG, "operands must be 16-byte aligned");
+  if (iters < 1 || blocks < 1) return fail(FG_ERR_INVALID_ARG, "iters and blocks must be >= 1");
+  const hipError_t e = fg::launch_peak_mfma(operands, out, iters, blocks, stream);
+  if (e != hipSuccess) return hip_fail(e, "peak mfma");
+  return FG_OK;
+}
+
+fg_status fg_peak_exp(float* out, int32_t iters, int32_t blocks, hipStream_t stream) {
+  if (!out) return fail(FG_ERR_INVALID_ARG, "out must not be NULL");
+  if (iters < 1 || blocks < 1) return fail(FG_ERR_INVALID_ARG, "iters and blocks must be >= 1");
+  const hipError_t e = fg::launch_peak_exp(out, iters, blocks, stream);
+  if (e != hipSuccess) return hip_fail(e, "peak exp");
+  return FG_OK;
+}
+
+fg_status fg_peak_copy(const void* src, void* dst, size_t bytes, int32_t nontemporal, int32_t blocks,
+                       hipStream_t stream) {
+  if (!src || !dst) return fail(FG_ERR_INVALID_ARG, "src and dst must not be NULL");
+  if (!aligned16(src) || !aligned16(dst)) return fail(FG_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0) return fail(FG_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (blocks < 1) return fail(FG_ERR_INVALID_ARG, "blocks must be >= 1");
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return fail(FG_ERR_INVALID_ARG, "src and dst overlap");
+  const hipError_t e = fg::launch_peak_copy(src, dst, bytes, nontemporal != 0, blocks, stream);
+  if (e != hipSuccess) return hip_fail(e, "peak copy");
+  return FG_OK;
+}
+
 fg_status fg_cache_error(const fg_cache* cache, uint32_t* bits_out, hipStream_t stream) {
   if (!cache || !cache->error_word) return fail(FG_ERR_INVALID_ARG, "cache or error_word is NULL");
   hipError_t e = hipStreamSynchronize(stream);

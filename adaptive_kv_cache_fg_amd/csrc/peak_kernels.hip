@@ -1,0 +1,104 @@
+// Micro-benchmarks of the chip's own ceilings, against which the profiling and
+// decode kernels are reported next to the vendor figures.  They take no part
+// in the method: bf16 MFMA issue rate, transcendental (v_exp_f32) rate, and
+// a plain 16-byte-vector copy through HBM.
+#include "fg_common.h"
+#include "fg_internal.h"
+
+namespace fg {
+
+// kChains independent 32x32x16 bf16 accumulator chains per wave, operands in
+// registers (random bf16 values loaded once from the caller's buffer), so the
+// loop is nothing but MFMAs; the sums are stored so the compiler keeps them.
+constexpr int kMfmaChains = 4;
+__global__ __launch_bounds__(256) void peak_mfma_kernel(const bf16x8* __restrict__ src, float* __restrict__ out,
+                                                        int iters) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const bf16x8 a = src[t & 1023];
+  const bf16x8 b = src[(t + 512) & 1023];
+  f32x16 acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  out[t] = s;
+}
+
+// kExpChains independent chains x <- 2^(-x) per lane (the negation is a free
+// source modifier, the values settle near 0.64 and stay finite), so the loop is
+// nothing but v_exp_f32.
+constexpr int kExpChains = 8;
+__global__ __launch_bounds__(256) void peak_exp_kernel(float* __restrict__ out, int iters) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  float x[kExpChains];
+#pragma unroll
+  for (int c = 0; c < kExpChains; ++c) x[c] = 0.01f * c + 1e-6f * (t & 1023);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kExpChains; ++c) x[c] = __builtin_amdgcn_exp2f(-x[c]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kExpChains; ++c) s += x[c];
+  out[t] = s;
+}
+
+// Grid-stride copy of 16-byte chunks, kCopyUnroll loads in flight per thread
+// before their stores; the stores optionally non-temporal (as the gather's).
+constexpr int kCopyUnroll = 4;
+template <bool NT>
+__global__ __launch_bounds__(256) void peak_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                        size_t n16) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t base = (size_t)blockIdx.x * 256 + threadIdx.x; base < n16; base += stride * kCopyUnroll) {
+    uint4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const size_t i = base + u * stride;
+      if (i < n16) v[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const size_t i = base + u * stride;
+      if (i < n16) {
+        if (NT)
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v[u]), reinterpret_cast<u32x4*>(dst + i));
+        else
+          dst[i] = v[u];
+      }
+    }
+  }
+}
+
+hipError_t launch_peak_mfma(const void* operands, float* out, int iters, int blocks, hipStream_t st) {
+  peak_mfma_kernel<<<dim3(blocks), dim3(256), 0, st>>>(static_cast<const bf16x8*>(operands), out, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_peak_exp(float* out, int iters, int blocks, hipStream_t st) {
+  peak_exp_kernel<<<dim3(blocks), dim3(256), 0, st>>>(out, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, bool nontemporal, int blocks, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  if (nontemporal)
+    peak_copy_kernel<true><<<dim3(blocks), dim3(256), 0, st>>>(static_cast<const uint4*>(src),
+                                                                static_cast<uint4*>(dst), n16);
+  else
+    peak_copy_kernel<false><<<dim3(blocks), dim3(256), 0, st>>>(static_cast<const uint4*>(src),
+                                                                 static_cast<uint4*>(dst), n16);
+  return hipGetLastError();
+}
+
+}  // namespace fg

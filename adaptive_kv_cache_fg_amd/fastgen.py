@@ -99,6 +99,9 @@ def lib() -> ctypes.CDLL:
     L.fg_kernel_timing_read.argtypes = [ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_float), I32]
     L.fg_kernel_timing_read.restype = I32
     L.fg_kernel_name.argtypes, L.fg_kernel_name.restype = [I32], ctypes.c_char_p
+    L.fg_peak_mfma_bf16.argtypes, L.fg_peak_mfma_bf16.restype = [P, P, I32, I32, P], ctypes.c_int
+    L.fg_peak_exp.argtypes, L.fg_peak_exp.restype = [P, I32, I32, P], ctypes.c_int
+    L.fg_peak_copy.argtypes, L.fg_peak_copy.restype = [P, P, S, I32, I32, P], ctypes.c_int
     _ = D, I64
     _lib = L
     return L
@@ -529,3 +532,35 @@ def timing_read(max_records: int = 1 << 16):
     ms = (ctypes.c_float * max_records)()
     k = lib().fg_kernel_timing_read(ids, ms, max_records)
     return [(KERNEL_NAMES[ids[i]], float(ms[i])) for i in range(k)]
+
+
+def peak_mfma_bf16(operands: torch.Tensor, out: torch.Tensor, iters: int, blocks: int) -> float:
+    """fg_peak_mfma_bf16; returns the flops of the call (4 chains x 32768 flops x iters per wave)."""
+    _need(operands, "operands", torch.bfloat16)
+    _need(out, "out", torch.float32)
+    if operands.numel() < 8192 or out.numel() < blocks * 256:
+        raise ValueError("operands must hold 8192 bf16 values and out blocks * 256 floats")
+    _check(lib().fg_peak_mfma_bf16(_ptr(operands), _ptr(out), int(iters), int(blocks), _stream()),
+           "fg_peak_mfma_bf16")
+    return float(blocks) * 4 * 4 * 32768 * iters
+
+
+def peak_exp(out: torch.Tensor, iters: int, blocks: int) -> float:
+    """fg_peak_exp; returns the exponentials of the call (8 chains x iters per thread)."""
+    _need(out, "out", torch.float32)
+    if out.numel() < blocks * 256:
+        raise ValueError("out must hold blocks * 256 floats")
+    _check(lib().fg_peak_exp(_ptr(out), int(iters), int(blocks), _stream()), "fg_peak_exp")
+    return float(blocks) * 256 * 8 * iters
+
+
+def peak_copy(src: torch.Tensor, dst: torch.Tensor, nontemporal: bool, blocks: int) -> int:
+    """fg_peak_copy of src's bytes into dst; returns the bytes moved (read + written)."""
+    _need(src, "src")
+    _need(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    _check(lib().fg_peak_copy(_ptr(src), _ptr(dst), nbytes, 1 if nontemporal else 0, int(blocks), _stream()),
+           "fg_peak_copy")
+    return 2 * nbytes

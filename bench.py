@@ -1,25 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of FastGen's hot path on one MI355X.
 
-One step = the whole path over one synthetic Llama-1-7B attention layer
-(32 heads, head_dim 128, prompt 2048, batch 1, bf16, T = 0.95, r_l = r_f = 0.3):
-  fg_profile  (row statistics sweep, column-sum sweep, top-k + recovery + policy)
-  fg_compact  (plan, one read of the totals, gather into the ragged cache)
-  256 x fg_decode_step over that cache (split-K partials + combine/append/evict).
-Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+Default workload: the Llama-1-65B-shaped stack -- 80 attention layers x 64 heads,
+head_dim 128, bf16, batch 16, prompt 2048, T = 0.95, r_l = r_f = 0.3, 1024
+decode steps.  One step is the whole path over that batch:
+  prompt phase: for every layer, fg_profile (row statistics sweep, column-sum
+      sweep, top-k + recovery + policy) and fg_compact (plan, gather refilling
+      that layer's cache);
+  decode: 1024 generated tokens, each decoded through every layer's cache in
+      turn (fg_decode_step: split-K partials, then combine / append / evict).
+Inputs (per layer Q, K, V; 16 decode inputs per layer, cycled; the full class
+sequence of the generated tokens) are drawn on the device and resident in HBM
+before timing.  The prompt phase is captured as one HIP graph and the decode
+loop as graphs of 16 tokens each (``--mode eager`` launches every call from
+Python); before timing, one replayed step is checked bit for bit against an
+eager run.
 
-The prompt phase (profile, then a compaction that refills the cache's buffers
-without a host read of the totals) and the 256-step decode loop are each
-captured once as a HIP graph and replayed (``--mode eager`` launches every call
-from Python instead).
-
-Prints ONE JSON line.  ``value`` is profile+compact prompt tokens/s; decode
-tokens/s, per-kernel durations, the roofline of the dominant kernel and the CPU
-oracle timed on the host cores are reported beside it.  Per-kernel durations
-are HIP events on the launch stream: the prompt kernels and the decode merge
-launch on one eager pass each (events around every launch), the decode
-split-K launch as a graph of 256 fg_decode_partials launches (events around the
-replay).
+Prints ONE JSON line.  ``value`` is profile+compact prompt tokens/s over the
+whole stack (B * n / prompt-phase time); decode tokens/s (B * steps / decode
+time), per-kernel figures, the roofline of the dominant kernel, whole-phase
+fractions of the MFMA and HBM ceilings, the chip's measured ceilings and the
+CPU oracle (sampled heads, extrapolated) are reported beside it.
+``--config 1`` (or ``--layer L`` of a stack) times one attention layer instead,
+with the optional full-cache, prompt-attention and decode-stability blocks.
 """
 from __future__ import annotations
 
@@ -39,6 +42,9 @@ from synth import inputs as syn  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+# v_exp_f32 at half rate: 8 lanes / clock / SIMD x 4 SIMD x 256 CU x 2.4 GHz (1e12 exponentials / s)
+EXP_PEAK_T_PER_S = 8 * 4 * 256 * 2.4e9 / 1e12
+METRIC = "profile+compact prompt tok/s & decode tok/s on 1 MI355X; % MFMA / HBM peak"
 
 
 # ---------------------------------------------------------------- CPU baseline (the oracle)
@@ -108,17 +114,19 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of ``kernel`` from profiles/traffic.json (FETCH_SIZE + WRITE_SIZE,
-    scaled by the calibration copy), or None when absent or taken on other kernel sources."""
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of ``kernel`` in ``workload`` from profiles/traffic.json (FETCH_SIZE +
+    WRITE_SIZE, scaled by the calibration copy), or None when absent, taken on another workload,
+    or taken on other kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("sources_digest") != kernel_sources_digest():
+    entry = t.get("workloads", {}).get(workload)
+    if not entry or entry.get("sources_digest") != kernel_sources_digest():
         return None
-    v = t.get("bytes_per_launch", {}).get(kernel)
+    v = entry.get("bytes_per_launch", {}).get(kernel)
     return float(v) if v is not None else None
 
 
@@ -305,37 +313,9 @@ def decode_stability(torch, fg, Kd, Vd, cls, prof, qs, ks, vs, ncs, spec, T) -> 
     }
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=1, help="workload id (1 = Llama-1-7B layer)")
-    ap.add_argument("--layer", type=int, default=0, help="layer of a multi-layer workload")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-heads", type=int, default=16)
-    ap.add_argument("--no-full-baseline", action="store_true",
-                    help="skip the full-cache decode baseline (every head keeps every key)")
-    ap.add_argument("--no-attention", action="store_true",
-                    help="skip the prompt-attention measurement (profiling's marginal cost over attention)")
-    ap.add_argument("--no-stability", action="store_true",
-                    help="skip the decode-time stability measurement over full caches")
-    ap.add_argument("--mode", "--decode-mode", dest="mode", choices=["graph", "eager"], default="graph",
-                    help="graph: the prompt phase and the decode loop each captured once as a HIP graph "
-                         "and replayed; eager: every call launched from Python")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1"}))
-        return 2
-    spec = syn.CONFIGS[args.config]
-    if not 0 <= args.layer < spec.layers:
-        print(json.dumps({"error": f"--layer must be in [0, {spec.layers})"}))
-        return 2
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, args.cpu_sample_heads, args.layer)   # before any GPU call (fork pool)
-
+def bench_layer(args, spec: syn.ConfigSpec, cpu) -> dict:
+    """One attention layer of a workload (its profile, compaction and decode loop), with the
+    optional measurement blocks (full-cache baseline, prompt attention, decode stability)."""
     import torch
     from adaptive_kv_cache_fg_amd import fastgen as fg
 
@@ -350,7 +330,7 @@ def main() -> int:
     ncs = torch.from_numpy(ds.new_class).cuda()
     outs = torch.empty((steps_dec, spec.batch, spec.n_q_heads, spec.head_dim), dtype=torch.float32, device="cuda")
     max_new_kept = int(max(np.count_nonzero(ds.new_class[:, b]) for b in range(spec.batch)))
-    T = spec.T[0]
+    T = float(args.T) if args.T is not None else spec.T[0]
     B, Hq, n, d = li.Q.shape
 
     def prompt_phase(reuse=None, check=True):
@@ -555,7 +535,8 @@ def main() -> int:
                    key=lambda k: kstats[k]["total_us_per_step"])
     dk = kstats[dominant]
     roofline = {"bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"], "unit": dk["unit"],
-                "frac": dk["frac"], "traffic": measured_traffic(dominant), "kernel": dominant}
+                "frac": dk["frac"], "traffic": measured_traffic(dominant, layer_workload_key(spec, args.layer, T)),
+                "kernel": dominant}
 
     # full-cache baseline (outside the timed region): the same decode loop over caches that keep
     # every key (the full policy forced for every head), against the adaptive caches above
@@ -627,7 +608,7 @@ def main() -> int:
     del calib_src, calib_dst
 
     result = {
-        "metric": "profile+compact prompt tok/s & decode tok/s on 1 MI355X; % MFMA / HBM peak",
+        "metric": METRIC,
         "value": prompt_tok_s,
         "unit": "prompt tok/s (profile+compact)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -649,6 +630,484 @@ def main() -> int:
         "kernels": kstats,
         "cpu_baseline": cpu,
     }
+    return result
+
+
+# ---------------------------------------------------------------- workload keys
+def layer_workload_key(spec: syn.ConfigSpec, layer: int, T: float) -> str:
+    return f"{spec.name}/layer{layer}/T{T}"
+
+
+def stack_workload_key(spec: syn.ConfigSpec, T: float, layers: int, steps: int) -> str:
+    return f"{spec.name}/stack{layers}/T{T}/steps{steps}"
+
+
+# ---------------------------------------------------------------- CPU baseline of a stack (the oracle)
+def _oracle_stack_head(args):
+    """Oracle profile + compact of one (layer, batch entry, KV head), then its decode over the
+    workload's generated tokens; per-head wall seconds of each part (1 BLAS thread)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import fastgen_ref as ref
+    spec_id, layer, b, h, steps = args
+    spec = syn.CONFIGS[spec_id]
+    G = spec.group
+    with threadpool_limits(1):
+        li = syn.make_layer(spec, layer, batch=[b], heads=[h])
+        ds = syn.make_decode_stream(spec, layer, steps, batch=[b], heads=[h])
+        t0 = time.perf_counter()
+        pr = ref.profile_head(li.Q[0, :G], li.K[0, 0], li.token_class[0], spec.r_l, spec.r_f, spec.T[0])
+        ref.compact_head(li.K[0, 0], li.V[0, 0], pr.kept)
+        t1 = time.perf_counter()
+        ref.decode_incremental(li.K[0, 0], li.V[0, 0], li.token_class[0], pr.F, pr.w_l, pr.policy,
+                               ds.q[:, 0, :G], ds.k[:, 0, 0], ds.v[:, 0, 0], ds.new_class[:, 0])
+        t2 = time.perf_counter()
+    return layer, t1 - t0, t2 - t1, pr.policy
+
+
+def cpu_baseline_stack(spec: syn.ConfigSpec, layers_layers: int) -> dict:
+    """The oracle on every KV head of batch entry 0 in two sample layers, one outer (layer 0:
+    broad / local heads) and one middle (layer L/2: special-dominated), timed per head in a fork
+    pool (run before the GPU is touched).  The whole stack is extrapolated from the per-head CPU
+    seconds: each outer and middle layer of the stack costs what its sample layer costs per batch
+    entry, times the batch; wall time = CPU seconds / cores (the heads are independent)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    cores = min(16, len(os.sched_getaffinity(0)))
+    L = layers_layers
+    outer, middle = 0, L // 2
+    steps = spec.decode_steps
+    jobs = [(spec.cfg_id, layer, 0, h, steps) for layer in (outer, middle) for h in range(spec.n_kv_heads)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
+        res = list(ex.map(_oracle_stack_head, jobs))
+    wall = time.perf_counter() - t0
+    prof_s = {outer: 0.0, middle: 0.0}
+    dec_s = {outer: 0.0, middle: 0.0}
+    for layer, tp, td, _ in res:
+        prof_s[layer] += tp
+        dec_s[layer] += td
+    n_outer = sum(1 for l in range(L) if l < 4 or l >= L - 4)
+    n_middle = L - n_outer
+    cpu_prompt = spec.batch * (n_outer * prof_s[outer] + n_middle * prof_s[middle])
+    cpu_decode = spec.batch * (n_outer * dec_s[outer] + n_middle * dec_s[middle])
+    return {"value": spec.batch * spec.seq_len / (cpu_prompt / cores), "unit": "prompt tok/s (profile+compact)",
+            "cores": cores, "kind": "oracle", "extrapolated": True,
+            "decode_tok_s": spec.batch * steps / (cpu_decode / cores),
+            "sample": f"fp64 numpy oracle (1 BLAS thread per worker, {cores} forked workers) on all "
+                      f"{spec.n_kv_heads} KV heads of batch entry 0 in layer {outer} (outer) and layer {middle} "
+                      f"(middle), profile+compact then {steps} decode steps each, inputs from the host "
+                      f"generator of the same recipe; extrapolated linearly in heads to {L} layers "
+                      f"({n_outer} outer, {n_middle} middle) x {spec.batch} batch entries, wall = CPU s / cores",
+            "sample_cpu_seconds": float(sum(r[1] + r[2] for r in res)), "sample_wall_seconds": wall,
+            "whole_stack_cpu_hours": (cpu_prompt + cpu_decode) / 3600.0}
+
+
+# ---------------------------------------------------------------- the chip's own ceilings
+def chip_peaks(torch, fg) -> dict:
+    """Micro-benchmarks (libfastgen's fg_peak_*): bf16 MFMA issue rate, v_exp_f32 rate and a
+    1 GiB HBM copy, each the best over a few occupancies, events around repeated launches."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(reps):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) * 1e-3 / reps
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    ops = torch.randn(8192, generator=g, device="cuda").to(torch.bfloat16)
+    mfma = []
+    for per_cu in (1, 2, 4):
+        blocks = per_cu * cus
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        iters = 8000
+        flops = blocks * 4 * 4 * 32768 * iters
+        t = timed(lambda: fg.peak_mfma_bf16(ops, out, iters, blocks))
+        mfma.append({"waves_per_simd": per_cu, "tflops": flops / t / 1e12, "ms": t * 1e3})
+    exps = []
+    for per_cu in (2, 4, 8):
+        blocks = per_cu * cus
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        iters = 40000
+        n = blocks * 256 * 8 * iters
+        t = timed(lambda: fg.peak_exp(out, iters, blocks))
+        exps.append({"waves_per_simd": per_cu, "t_exp_per_s": n / t / 1e12, "ms": t * 1e3})
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    copies = []
+    for nt in (False, True):
+        for per_cu in (4, 8):
+            blocks = per_cu * cus
+            t = timed(lambda: fg.peak_copy(src, dst, nt, blocks), reps=10)
+            copies.append({"nontemporal": nt, "blocks_per_cu": per_cu, "gbs": 2 * nbytes / t / 1e9})
+    del src, dst
+    best = lambda xs, k: max(x[k] for x in xs)   # noqa: E731
+    clock_ghz = 2.4
+    return {
+        "mfma_bf16": {"measured_tflops": best(mfma, "tflops"), "vendor_tflops": BF16_MFMA_PEAK_TFLOPS,
+                      "runs": mfma, "note": "4 independent 32x32x16 bf16 accumulator chains per wave, "
+                                            "register operands (random bf16)"},
+        "exp": {"measured_t_per_s": best(exps, "t_exp_per_s"), "derived_t_per_s": EXP_PEAK_T_PER_S,
+                "runs": exps, "note": f"v_exp_f32, 8 independent chains per lane; derived figure = "
+                                      f"half rate (8 lanes/clk/SIMD) x 4 SIMD x {cus} CU x {clock_ghz} GHz"},
+        "hbm_copy": {"measured_gbs": best(copies, "gbs"), "vendor_gbs": HBM_PEAK_GBS, "bytes": 2 * nbytes,
+                     "runs": copies, "note": "1 GiB read + 1 GiB written, 16-byte loads and stores"},
+        "compute_units": cus,
+    }
+
+
+# ---------------------------------------------------------------- the whole stack (the headline)
+def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
+    """Every layer of a stack workload: the prompt phase (profile + compaction refilling each
+    layer's cache) over all layers, then the decode loop, each generated token decoded through
+    every layer's cache in turn.  Inputs are drawn on the device before timing starts."""
+    import torch
+    from adaptive_kv_cache_fg_amd import fastgen as fg
+    from synth import device as sdev
+
+    T = float(args.T) if args.T is not None else spec.T[0]
+    L = spec.layers if args.stack_layers is None else args.stack_layers
+    steps_dec = spec.decode_steps if args.decode_steps is None else args.decode_steps
+    B, Hq, Hkv, n, d = spec.batch, spec.n_q_heads, spec.n_kv_heads, spec.seq_len, spec.head_dim
+    G = Hq // Hkv
+    e = 2 if spec.dtype == "bf16" else 4
+    pool_n = min(16, steps_dec)
+    dev = torch.device("cuda")
+    say = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)   # noqa: E731
+
+    # ---- inputs, resident in HBM before any timing
+    t0 = time.perf_counter()
+    lay = [sdev.make_layer_device(spec, l, dev) for l in range(L)]
+    cls = lay[0].token_class                                   # classes depend on the batch entry only
+    ncls_h = np.ascontiguousarray(np.stack([syn.new_token_classes(spec, b, steps_dec) for b in range(B)], axis=1))
+    ncls = torch.from_numpy(ncls_h).to(dev)                    # [steps, B]
+    pools = [sdev.make_decode_stream_device(spec, l, pool_n, dev, classes=ncls_h[:pool_n]) for l in range(L)]
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+    say(f"inputs drawn on the device in {gen_s:.1f} s ({L} layers)")
+    mk = int(max(np.count_nonzero(ncls_h[:, b]) for b in range(B)))
+    outs = torch.empty((L, B, Hq, d), dtype=torch.float32, device=dev)
+    caches = [None] * L
+    profs = [None] * L
+
+    def prompt_phase(check=True):
+        for l in range(L):
+            c = caches[l]
+            prof = fg.profile(lay[l].Q, lay[l].K, cls, spec.r_l, spec.r_f, T,
+                              policy_out=None if c is None else c.t["policy"])
+            caches[l] = fg.compact(lay[l].K, lay[l].V, cls, prof, Hq, max_new_tokens=steps_dec, max_new_kept=mk,
+                                   reuse=c, check=check)
+            profs[l] = prof
+
+    def decode_tokens(t_a, t_b):
+        for t in range(t_a, t_b):
+            i = t % pool_n
+            nc = ncls[t]
+            for l in range(L):
+                pl = pools[l]
+                caches[l].decode_step(pl.q[i], pl.k[i], pl.v[i], nc, out=outs[l])
+
+    # ---- first pass: allocates every cache (one read of the plan's totals per layer)
+    t0 = time.perf_counter()
+    prompt_phase()
+    decode_tokens(0, min(2, steps_dec))
+    torch.cuda.synchronize()
+    say(f"caches allocated in {time.perf_counter() - t0:.1f} s; cache rows "
+        f"{sum(int(c.c.total_rows) for c in caches)}")
+
+    graphs = []
+    pgraph = None
+    mempool = None
+    profs_graph = None
+    if args.mode == "graph":
+        # the prompt phase as one graph; the decode loop as graphs of --graph-tokens tokens each
+        # (a decode step's position is a launch argument, so every graph covers its own tokens)
+        t0 = time.perf_counter()
+        mempool = torch.cuda.graph_pool_handle()
+        pgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pgraph, pool=mempool):
+            prompt_phase(check=False)
+        profs_graph = list(profs)                              # the profiles the prompt graph writes
+        prompt_phase()                                         # eager: host positions back to n
+        torch.cuda.synchronize()
+        for t_a in range(0, steps_dec, args.graph_tokens):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, pool=mempool):
+                decode_tokens(t_a, min(steps_dec, t_a + args.graph_tokens))
+            graphs.append(g)
+        torch.cuda.synchronize()
+        say(f"captured the prompt phase and {len(graphs)} decode graphs in {time.perf_counter() - t0:.1f} s")
+
+    def one_step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if pgraph is not None:
+            pgraph.replay()
+        else:
+            prompt_phase(check=False)
+        if ev is not None:
+            ev[1].record()
+        if graphs:
+            for g in graphs:
+                g.replay()
+        else:
+            decode_tokens(0, steps_dec)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    # correctness guard on the timed configuration: one step as timed, then the same step eagerly
+    # with the plan's totals checked; outputs of the last token, the final caches' positions and the
+    # profiles must agree bit for bit, and no cache may report an error
+    one_step()
+    torch.cuda.synchronize()
+    ref_out = outs.clone()
+    ref_state = [(c.t["pos"].clone(), c.t["len"].clone()) for c in caches]
+    ref_prof = [(p.policy.clone(), p.recovery.clone(), p.cum.clone()) for p in (profs_graph if pgraph else profs)]
+    prompt_phase(check=True)
+    decode_tokens(0, steps_dec)
+    torch.cuda.synchronize()
+    if not torch.equal(ref_out, outs):
+        raise RuntimeError("timed decode and eager decode disagree")
+    for l in range(L):
+        if not (torch.equal(ref_state[l][0], caches[l].t["pos"]) and torch.equal(ref_state[l][1], caches[l].t["len"])):
+            raise RuntimeError(f"layer {l}: caches after the timed and the eager decode disagree")
+        if not all(torch.equal(a, b) for a, b in zip(ref_prof[l], (profs[l].policy, profs[l].recovery, profs[l].cum))):
+            raise RuntimeError(f"layer {l}: timed and eager prompt phases disagree")
+        if caches[l].error_bits() != 0:
+            raise RuntimeError(f"layer {l}: cache error bits set")
+    del ref_out, ref_state, ref_prof
+    say("timed configuration equals an eager run; timing")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        one_step(evs[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prompt_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs]))
+    decode_ms = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in evs]))
+    ms_per_step = wall * 1e3 / args.steps
+    prompt_tok_s = B * n / (prompt_ms * 1e-3)
+    decode_tok_s = B * steps_dec / (decode_ms * 1e-3)
+    say(f"prompt {prompt_ms:.2f} ms ({prompt_tok_s:.4g} tok/s), decode {decode_ms:.1f} ms ({decode_tok_s:.4g} tok/s)")
+
+    # ---- per-kernel figures (outside the timed region)
+    # prompt kernels: one eager prompt phase with the library's events around every launch
+    torch.cuda.synchronize()
+    fg.timing_read()
+    fg.timing_enable(True)
+    prompt_phase(check=False)
+    torch.cuda.synchronize()
+    fg.timing_enable(False)
+    per = {}
+    for name, ms in fg.timing_read():
+        per.setdefault(name, []).append(ms)
+    kstats = {k: {"launches_per_step": float(len(v)), "avg_us": 1e3 * float(np.mean(v)),
+                  "total_us_per_step": 1e3 * float(np.sum(v)), "timing": "events around each launch (eager pass)"}
+              for k, v in per.items()}
+
+    def rows_kept(c):
+        """Cache rows in use that hold a key (pos >= 0), summed over the heads of one layer."""
+        total = int(c.c.total_rows)
+        ro = c.t["row_offset"]
+        idx = torch.arange(total, device=dev, dtype=torch.int64)
+        head = torch.bucketize(idx, ro[1:], right=True).clamp_(max=ro.numel() - 2)
+        in_use = idx < ro[head] + c.t["len"].to(torch.int64)[head]
+        return int((in_use & (c.t["pos"][:total] >= 0)).sum().item())
+
+    def partials_graph_us(reps):
+        """fg_decode_partials (the split-K launch alone, read-only on the caches) for every layer,
+        captured as a graph of `reps` passes over the layers; events around its replay."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, pool=mempool):
+            for r in range(reps):
+                for l in range(L):
+                    caches[l].decode_partials(pools[l].q[r % pool_n])
+        g.replay()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        g.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        del g
+        return 1e3 * ev[0].elapsed_time(ev[1]) / (reps * L)
+
+    # the split-K launch at the first and at the last decode state (rows grow linearly in between)
+    prompt_phase(check=False)
+    torch.cuda.synchronize()
+    kept_start = [rows_kept(c) for c in caches]
+    p_start = partials_graph_us(4)
+    decode_tokens(0, steps_dec)
+    torch.cuda.synchronize()
+    kept_end = [rows_kept(c) for c in caches]
+    p_end = partials_graph_us(4)
+    q_bytes = B * Hq * d * e
+    row_bytes = 2 * d * e + 4
+    mean_rows = 0.5 * (sum(kept_start) + sum(kept_end)) / L          # per layer, mean over the steps
+    part_bytes = mean_rows * row_bytes + q_bytes
+    part_us = 0.5 * (p_start + p_end)
+    step_us = 1e3 * decode_ms / (steps_dec * L)                       # one layer's decode step
+    merge_us = step_us - part_us
+    merge_bytes = B * Hkv * 2 * d * e + B * Hq * d * (e + 4)
+    step_bytes = part_bytes + merge_bytes
+    kstats["decode_partials"] = {
+        "launches_per_step": float(steps_dec * L), "avg_us": part_us, "total_us_per_step": part_us * steps_dec * L,
+        "timing": f"graphs of fg_decode_partials over every layer, events around the replay, at the first "
+                  f"({p_start:.2f} us) and the last ({p_end:.2f} us) decode state; the mean"}
+    kstats["decode_merge"] = {
+        "launches_per_step": float(steps_dec * L), "avg_us": merge_us, "total_us_per_step": merge_us * steps_dec * L,
+        "timing": "timed decode step minus the graph-timed split-K launch"}
+    kstats["decode_step"] = {
+        "launches_per_step": float(steps_dec * L), "avg_us": step_us, "total_us_per_step": 1e3 * decode_ms,
+        "note": "one layer's whole decode step (both launches and the gaps between them), from the timed region"}
+
+    # algorithmic work
+    pairs = n * (n + 1) // 2
+    sweep_flops = B * Hq * 2 * d * pairs                              # per sweep launch (one layer)
+    sweep_exps = B * Hq * pairs
+    kept_prompt = [c.kept_count.to(torch.int64).sum().item() for c in caches]   # prompt keys kept per layer
+    gather_bytes = float(np.mean([k * (2 * 2 * d * e + 4) for k in kept_prompt])) + B * Hkv * (n + n / 8)
+    peak_mfma = BF16_MFMA_PEAK_TFLOPS if spec.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    for k, units, bound in (("profile_rowstats", sweep_flops, "mfma"), ("profile_colsums", sweep_flops, "mfma"),
+                            ("compact_gather", gather_bytes, "hbm"), ("decode_partials", part_bytes, "hbm"),
+                            ("decode_merge", merge_bytes, "hbm"), ("decode_step", step_bytes, "hbm")):
+        if k not in kstats:
+            continue
+        avg_s = kstats[k]["avg_us"] * 1e-6
+        if bound == "mfma":
+            ach = units / avg_s / 1e12
+            kstats[k].update(bound="mfma", achieved=ach, peak=peak_mfma, unit="TFLOP/s", frac=ach / peak_mfma,
+                             algorithmic_flops=units, exps=sweep_exps,
+                             exp_rate_t_per_s=sweep_exps / avg_s / 1e12,
+                             exp_frac=sweep_exps / avg_s / 1e12 / EXP_PEAK_T_PER_S)
+        else:
+            ach = units / avg_s / 1e9
+            kstats[k].update(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,
+                             algorithmic_bytes=units)
+    dominant = max((k for k in ("profile_rowstats", "profile_colsums", "compact_gather", "decode_partials",
+                                "decode_merge") if k in kstats), key=lambda k: kstats[k]["total_us_per_step"])
+    dk = kstats[dominant]
+    key = stack_workload_key(spec, T, L, steps_dec)
+    roofline = {"bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"], "unit": dk["unit"],
+                "frac": dk["frac"], "traffic": measured_traffic(dominant, key), "kernel": dominant}
+
+    # the whole phases against their ceilings
+    prompt_flops = 2 * sweep_flops * L
+    decode_bytes = step_bytes * L * steps_dec
+    phases = {
+        "prompt_mfma_frac": prompt_flops / (prompt_ms * 1e-3) / 1e12 / peak_mfma,
+        "prompt_flops": prompt_flops,
+        "decode_hbm_frac": decode_bytes / (decode_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "decode_bytes": decode_bytes,
+        "decode_cache_bytes_per_token": mean_rows * row_bytes * L,
+        "note": "prompt: both sweeps' algorithmic flops over every layer / prompt-phase time (profile, select, "
+                "plan, gather included); decode: algorithmic bytes of every layer's steps (cache rows kept, "
+                "mean of the first and last state; q, new k/v, fp32 output) / decode time",
+    }
+    pol = np.concatenate([p.policy.cpu().numpy().reshape(-1) for p in profs])
+    full_rows = B * Hkv * (n + (steps_dec - 1) / 2.0) * L
+    compression = {
+        "policy_histogram": np.bincount(pol, minlength=5).tolist(),
+        "prompt_keys_kept_fraction": float(sum(kept_prompt) / (B * Hkv * n * L)),
+        "kv_bytes_full_per_token": full_rows * 2 * d * e,
+        "kv_bytes_adaptive_per_token": mean_rows * L * 2 * d * e,
+        "kv_pruned_fraction": 1.0 - mean_rows * L / full_rows,
+        "note": "KV bytes a decode step reads, mean over the steps: every key kept (full) vs the adaptive caches",
+    }
+    pk = None
+    if not args.no_peaks:
+        pk = chip_peaks(torch, fg)
+        mf, ex, cp = pk["mfma_bf16"]["measured_tflops"], pk["exp"]["measured_t_per_s"], pk["hbm_copy"]["measured_gbs"]
+        for k in ("profile_rowstats", "profile_colsums"):
+            if k in kstats:
+                kstats[k]["frac_of_measured_mfma"] = kstats[k]["achieved"] / mf
+                kstats[k]["exp_frac_of_measured"] = kstats[k]["exp_rate_t_per_s"] / ex
+        for k in ("compact_gather", "decode_partials", "decode_step"):
+            kstats[k]["frac_of_measured_copy"] = kstats[k]["achieved"] / cp
+        phases["prompt_frac_of_measured_mfma"] = phases["prompt_mfma_frac"] * peak_mfma / mf
+        phases["decode_frac_of_measured_copy"] = phases["decode_hbm_frac"] * HBM_PEAK_GBS / cp
+        roofline["frac_of_measured"] = dk["achieved"] / (cp if dk["bound"] == "hbm" else mf)
+
+    # a plain copy of known size, outside the timed region: the reference that scales the
+    # FETCH_SIZE / WRITE_SIZE counters of the kernels above when this script runs under rocprofv3
+    calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
+
+    workload = (f"{spec.name}: {L} layers x {Hq} heads (KV {Hkv}), d={d}, {spec.dtype}, B={B}, n={n}, "
+                f"T={T}, r_l={spec.r_l}, r_f={spec.r_f}, {steps_dec} decode steps through every layer")
+    return {
+        "metric": METRIC, "value": prompt_tok_s, "unit": "prompt tok/s (profile+compact)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+        "data": "synthetic (seeded Llama-shaped post-RoPE Q/K/V with planted head types, drawn on the device)",
+        "config": {"workload": workload, "layers": L, "batch": B, "seq_len": n, "decode_steps": steps_dec, "T": T,
+                   "key": key},
+        "decode_tok_s": decode_tok_s, "mode": args.mode, "prompt_ms": prompt_ms, "decode_ms": decode_ms,
+        "roofline": roofline, "phases": phases, "compression": compression, "kernels": kstats,
+        "peaks": pk, "input_generation_s": gen_s, "cpu_baseline": cpu,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload id (3 = the Llama-1-65B-shaped stack, the default; 1 = one Llama-1-7B layer)")
+    ap.add_argument("--layer", type=int, default=None,
+                    help="one layer of a stack workload instead of the whole stack")
+    ap.add_argument("--T", type=float, default=None, help="recover ratio (default: the workload's first)")
+    ap.add_argument("--stack-layers", type=int, default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--decode-steps", type=int, default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--graph-tokens", type=int, default=16, help="generated tokens per captured decode graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=16)
+    ap.add_argument("--no-peaks", action="store_true", help="skip the chip-ceiling micro-benchmarks")
+    ap.add_argument("--no-full-baseline", action="store_true",
+                    help="one layer: skip the full-cache decode baseline (every head keeps every key)")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="one layer: skip the prompt-attention measurement")
+    ap.add_argument("--no-stability", action="store_true",
+                    help="one layer: skip the decode-time stability measurement over full caches")
+    ap.add_argument("--mode", "--decode-mode", dest="mode", choices=["graph", "eager"], default="graph",
+                    help="graph: the prompt phase and the decode loop captured as HIP graphs and replayed; "
+                         "eager: every call launched from Python")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "bench.py measures one GPU (each box has one); --gpus must be 1. The path "
+                                   "shards by (batch entry, layer, KV head) with no exchange between GPUs."}))
+        return 2
+    spec = syn.CONFIGS[args.config]
+    stack = spec.layers > 1 and args.layer is None
+    if not stack:
+        args.layer = 0 if args.layer is None else args.layer
+        if not 0 <= args.layer < spec.layers:
+            print(json.dumps({"error": f"--layer must be in [0, {spec.layers})"}))
+            return 2
+    cpu = None
+    if not args.no_cpu_baseline:                              # before any GPU call (fork pool)
+        if stack:
+            cpu = cpu_baseline_stack(spec, spec.layers if args.stack_layers is None else args.stack_layers)
+        else:
+            cpu = cpu_baseline(spec, args.cpu_sample_heads, args.layer)
+    result = bench_stack(args, spec, cpu) if stack else bench_layer(args, spec, cpu)
     print(json.dumps(result))
     return 0
 

@@ -360,6 +360,34 @@ fg_status fg_decode_track(const fg_cache* cache, const void* q, const uint8_t* t
                           const uint32_t* freq_mask, float* row_score, float* level_bins, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ measurement */
+
+/*
+ * Micro-benchmarks of the chip's own ceilings.  They take no part in the method;
+ * they measure the rates the profiling and decode kernels are set against:
+ *
+ * fg_peak_mfma_bf16: `blocks` workgroups of 256 threads (4 wave64) each run
+ *   `iters` iterations of 4 independent v_mfma_f32_32x32x16_bf16 accumulator
+ *   chains on register operands: 4 * 32768 * iters flops per wave, i.e.
+ *   blocks * 4 * 4 * 32768 * iters flops per call.  operands: 1024 x 16 bytes of
+ *   bf16 values read once (16-byte aligned); out [blocks * 256] fp32 (sums kept
+ *   so the work is not removed).
+ * fg_peak_exp: `blocks` x 256 threads each run `iters` iterations of 8
+ *   independent chains x <- 2^(-x) (one v_exp_f32 each): blocks * 256 * 8 * iters
+ *   exponentials per call.  out [blocks * 256] fp32.
+ * fg_peak_copy: copy `bytes` (a multiple of 16, both pointers 16-byte aligned,
+ *   not overlapping) from src to dst with 16-byte loads and stores over a
+ *   grid-stride loop of `blocks` x 256 threads; nontemporal != 0 stores
+ *   non-temporally (as the compaction's gather does).
+ * Errors: FG_ERR_INVALID_ARG for NULL or misaligned pointers, iters < 1,
+ * blocks < 1, a byte count that is not a positive multiple of 16, or
+ * overlapping copy buffers; FG_ERR_HIP for a failed launch.
+ */
+fg_status fg_peak_mfma_bf16(const void* operands, float* out, int32_t iters, int32_t blocks, hipStream_t stream);
+fg_status fg_peak_exp(float* out, int32_t iters, int32_t blocks, hipStream_t stream);
+fg_status fg_peak_copy(const void* src, void* dst, size_t bytes, int32_t nontemporal, int32_t blocks,
+                       hipStream_t stream);
+
 /* ------------------------------------------------------------------ diagnostics */
 
 const char* fg_status_string(fg_status status);

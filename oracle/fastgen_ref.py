@@ -112,19 +112,20 @@ def column_scores(Qg: np.ndarray, K: np.ndarray, w_l: int, executor=None) -> Dic
               the profiling kernels, not part of the method's definition);
     lse[g, i] = log sum_{j <= i} exp(q^g_i . k_j / sqrt(d)).
     Row blocks are independent; ``executor`` (e.g. a thread pool) may run them
-    concurrently, their contributions are summed in block order.
+    concurrently, their contributions are summed in block order.  A block of
+    rows r0..r1-1 sees only the keys j < r1 (causal), so only those are scored.
     """
     G, n, _ = Qg.shape
 
     def block(item):
         g, r0, r1 = item
-        S = _causal_scores(Qg[g, r0:r1], K, r0)
+        S = _causal_scores(Qg[g, r0:r1], K[:r1], r0)
         mx = S.max(axis=1, keepdims=True)
         E = np.exp(S - mx)
         Z = E.sum(axis=1, keepdims=True)
         A = E / Z
         i = np.arange(r0, r1)[:, None]
-        j = np.arange(n)[None, :]
+        j = np.arange(r1)[None, :]
         return (mx + np.log(Z))[:, 0], A.sum(axis=0), np.where((i - j >= 0) & (i - j < w_l), A, 0.0).sum(axis=0)
 
     items = _blocks(G, n)
@@ -133,8 +134,8 @@ def column_scores(Qg: np.ndarray, K: np.ndarray, w_l: int, executor=None) -> Dic
     lse = np.zeros((G, n), dtype=np.float64)
     for (g, r0, r1), (l_blk, c_blk, b_blk) in zip(items, _map(block, items, executor)):
         lse[g, r0:r1] = l_blk
-        cum += c_blk
-        band += b_blk
+        cum[:r1] += c_blk
+        band[:r1] += b_blk
     return {"cum": cum, "band": band, "lse": lse}
 
 
@@ -152,7 +153,7 @@ def attention_output(Qg: np.ndarray, K: np.ndarray, V: np.ndarray, executor=None
 
     def block(item):
         g, r0, r1 = item
-        return causal_attention_rows(Qg[g, r0:r1], K, r0) @ V
+        return causal_attention_rows(Qg[g, r0:r1], K[:r1], r0) @ V[:r1]
 
     items = _blocks(G, n)
     out = np.zeros((G, n, V.shape[1]), dtype=np.float64)
@@ -183,7 +184,7 @@ def key_levels(cls: np.ndarray, F: np.ndarray, rows: np.ndarray, w_l: int) -> np
     Fx[: len(F)] = F[: nk]
     i = np.asarray(rows)[:, None]
     j = np.arange(nk)[None, :]
-    lev = np.full((m, nk), LEVEL_FULL, dtype=np.int64)
+    lev = np.full((m, nk), LEVEL_FULL, dtype=np.int8)
     lev = np.where(i - j < w_l, LEVEL_LOCAL, lev)
     lev = np.where(Fx[None, :], LEVEL_FREQUENT, lev)
     lev = np.where((cls == TOKEN_PUNCT)[None, :], LEVEL_PUNCT, lev)
@@ -198,8 +199,8 @@ def row_bins(Qg: np.ndarray, K: np.ndarray, cls: np.ndarray, F: np.ndarray, w_l:
 
     def block(item):
         g, r0, r1 = item
-        A = causal_attention_rows(Qg[g, r0:r1], K, r0)
-        lev = key_levels(cls, F, np.arange(r0, r1), w_l)
+        A = causal_attention_rows(Qg[g, r0:r1], K[:r1], r0)              # keys j < r1 (causal)
+        lev = key_levels(cls[:r1], F[:r1], np.arange(r0, r1), w_l)
         return np.stack([np.where(lev == lv, A, 0.0).sum(axis=1) for lv in range(N_LEVELS)], axis=1)
 
     items = _blocks(G, n)

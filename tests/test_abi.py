@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "fastgen.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fg_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fg_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     for name in names:
         assert hasattr(L, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", str(fgb.LIB_PATH)], capture_output=True, text=True).stdout
-    exported = set(re.findall(r" T (fg_[a-z_]+)", out))
+    exported = set(re.findall(r" T (fg_[a-z0-9_]+)$", out, flags=re.M))
     assert set(names) <= exported
 
 
@@ -216,3 +216,16 @@ def test_status_strings_and_kernel_names():
         return L.fg_decode_chunk_rows(ctypes.byref(fgb.FgShape(1, 4, 4, n, 128, 0)))
     assert [chunk(n) for n in (1, 128, 8192, 8193, 32768, 1 << 20)] == [128, 128, 128, 256, 512, 2048]
     assert L.fg_decode_chunk_rows(ctypes.byref(fgb.FgShape(1, 4, 4, 16, 96, 0))) == 0
+
+
+def test_peak_benchmarks_reject_bad_arguments():
+    L = fgb.lib()
+    p = ctypes.c_void_p(0x1000)
+    assert L.fg_peak_mfma_bf16(None, p, 10, 10, None) == 1
+    assert L.fg_peak_mfma_bf16(ctypes.c_void_p(0x1008), p, 10, 10, None) == 1      # misaligned operands
+    assert L.fg_peak_mfma_bf16(p, p, 0, 10, None) == 1
+    assert L.fg_peak_exp(None, 10, 10, None) == 1
+    assert L.fg_peak_exp(p, 10, 0, None) == 1
+    assert L.fg_peak_copy(p, ctypes.c_void_p(0x100000), 24, 0, 8, None) == 1        # not a multiple of 16
+    assert L.fg_peak_copy(p, ctypes.c_void_p(0x1100), 4096, 0, 8, None) == 1        # overlapping
+    assert L.fg_peak_copy(p, ctypes.c_void_p(0x100000), 0, 0, 8, None) == 1

@@ -93,8 +93,11 @@ def _run(gpl, spec, T, steps, score_scale):
                 ranked = sorted(snap, key=lambda j: (snap[j], -j))
                 s_w = snap[ranked[0]]
                 gpu_kept = set(kept_g[hd].tolist())
+                # rounding decides (a) whether j_out replaces a key when its margin over the weakest is
+                # inside the window, and (b) which key it evicts when it does replace and the two
+                # weakest are inside the window; a clear non-replacement evicts nothing
                 near_margin = _near(head.score[j_out], s_w, t, G)
-                near_weakest = len(ranked) > 1 and _near(snap[ranked[1]], s_w, t, G)
+                near_weakest = len(ranked) > 1 and _near(snap[ranked[1]], s_w, t, G) and head.score[j_out] > s_w
                 if near_margin or near_weakest:
                     forced += 1
                     force = j_out in gpu_kept
