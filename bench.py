@@ -875,8 +875,10 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
     ref_state = [(c.t["pos"].clone(), c.t["len"].clone()) for c in caches]
     ref_prof = [(p.policy.clone(), p.recovery.clone(), p.cum.clone()) for p in (profs_graph if pgraph else profs)]
     prompt_phase(check=True)
-    decode_tokens(0, steps_dec)
-    torch.cuda.synchronize()
+    for t_a in range(0, steps_dec, 256):
+        decode_tokens(t_a, min(steps_dec, t_a + 256))
+        torch.cuda.synchronize()
+        say(f"eager check: {min(steps_dec, t_a + 256)} of {steps_dec} tokens")
     if not torch.equal(ref_out, outs):
         raise RuntimeError("timed decode and eager decode disagree")
     for l in range(L):
@@ -929,14 +931,26 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
 
     def partials_graph_us(reps):
         """fg_decode_partials (the split-K launch alone, read-only on the caches) for every layer,
-        captured as a graph of `reps` passes over the layers; events around its replay."""
+        captured as a graph of `reps` passes over the layers; events around its replay (eager
+        mode: the same launches from Python, events around the loop)."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        if args.mode == "eager":
+            for l in range(L):
+                caches[l].decode_partials(pools[l].q[0])
+            torch.cuda.synchronize()
+            ev[0].record()
+            for r in range(reps):
+                for l in range(L):
+                    caches[l].decode_partials(pools[l].q[r % pool_n])
+            ev[1].record()
+            torch.cuda.synchronize()
+            return 1e3 * ev[0].elapsed_time(ev[1]) / (reps * L)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, pool=mempool):
             for r in range(reps):
                 for l in range(L):
                     caches[l].decode_partials(pools[l].q[r % pool_n])
         g.replay()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
         ev[0].record()
         g.replay()
@@ -1064,6 +1078,116 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
     }
 
 
+# ---------------------------------------------------------------- rocprofv3 summaries
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def _short(name: str) -> str:
+    """Kernel name without namespace, template arguments and parameter list (mangled or not)."""
+    if name.startswith("_ZN"):                           # Itanium mangling: _ZN <len><id> ... then I / E
+        i, parts = 3, []
+        while i < len(name) and name[i].isdigit():
+            j = i
+            while name[j].isdigit():
+                j += 1
+            k = int(name[i:j])
+            parts.append(name[j:j + k])
+            i = j + k
+        if parts:
+            return parts[-1]
+    base = name.split("(")[0]
+    depth, out = 0, []
+    for ch in base:
+        depth += ch == "<"
+        if depth == 0:
+            out.append(ch)
+        depth -= ch == ">"
+    s = "".join(out).strip()
+    return s.split("::")[-1].split(" ")[-1] or name[:48]
+
+
+def summarize_trace(directory: str, title: str, command: str) -> str:
+    """Text summary of a rocprofv3 --kernel-trace --stats run: per kernel, calls and average /
+    min / max dispatch durations from the kernel trace."""
+    trace = _csv_rows(directory, "kernel_trace.csv")
+    per = {}
+    for r in trace:
+        name = _short(r.get("Kernel_Name", ""))
+        t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault(name, []).append(t)
+    total = sum(sum(v) for v in per.values()) or 1.0
+    lines = [f"# {title}", f"# command: {command}",
+             "# durations in microseconds per dispatch (profiler timestamps), from the kernel trace",
+             f"{'kernel':44s} {'calls':>8s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{name[:44]:44s} {len(v):8d} {np.mean(v):9.2f} {np.min(v):9.2f} {np.max(v):9.2f} "
+                     f"{100 * sum(v) / total:6.2f}")
+    return "\n".join(lines) + "\n"
+
+
+def _counter_means(directory: str, counter: str) -> dict:
+    """Mean of one counter per dispatch, by full kernel name (rocprofv3 --pmc counter collection)."""
+    per = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        per.setdefault(r.get("Kernel_Name", ""), []).append(float(r["Counter_Value"]))
+    return {k: (float(np.mean(v)), len(v)) for k, v in per.items()}
+
+
+def record_traffic(fetch_dir: str, write_dir: str, key: str, command: str) -> str:
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what they read for the 256 MiB copy
+    the benchmark issues after its timed region, store the per-launch bytes of the library's
+    kernels in profiles/traffic.json under ``key`` with the current sources' digest, and return
+    a text summary."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    # the calibration copy: of the kernels that read about what they write, the one whose write
+    # volume is closest to CALIB_BYTES (a fill writes without reading)
+    both = [k for k in write if k in fetch and fetch[k][0] > 0.25 * write[k][0] and "fg::" not in k]
+    calib = min(both, key=lambda k: abs(write[k][0] * 1024 - CALIB_BYTES))
+    f_factor = CALIB_BYTES / (fetch[calib][0] * 1024)
+    w_factor = CALIB_BYTES / (write[calib][0] * 1024)
+    names = {"rowstats_kernel": "profile_rowstats", "colsums_kernel": "profile_colsums",
+             "gather_kernel": "compact_gather", "decode_partials_kernel": "decode_partials",
+             "decode_merge_kernel": "decode_merge", "select_kernel": "profile_select"}
+    per_launch = {}
+    lines = [f"# HBM traffic per dispatch, {key}", f"# commands: {command}",
+             "# FETCH_SIZE / WRITE_SIZE: rocprofv3 derived counters in KiB per dispatch, averaged over dispatches;",
+             f"# scaled bytes = FETCH * {f_factor:.4f} + WRITE * {w_factor:.4f} (factors from the {CALIB_BYTES} B copy, "
+             f"kernel {_short(calib)})"]
+    for k, short in names.items():
+        fk = [x for x in fetch if _short(x) == k]
+        wk = [x for x in write if _short(x) == k]
+        if not fk or not wk:
+            continue
+        nf, nw = sum(fetch[x][1] for x in fk), sum(write[x][1] for x in wk)
+        fv = sum(fetch[x][0] * fetch[x][1] for x in fk) / nf        # dispatch-weighted over instantiations
+        wv = sum(write[x][0] * write[x][1] for x in wk) / nw
+        b = fv * 1024 * f_factor + wv * 1024 * w_factor
+        per_launch[short] = b
+        lines.append(f"{k:26s} dispatches {nf:7d}  FETCH_SIZE {fv:13.1f} KiB  WRITE_SIZE {wv:12.1f} KiB  "
+                     f"scaled bytes {b:14.0f}")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    t = {"workloads": t.get("workloads", {})}
+    t["workloads"][key] = {"sources_digest": kernel_sources_digest(), "fetch_factor": f_factor,
+                           "write_factor": w_factor, "bytes_per_launch": per_launch}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+    return "\n".join(lines) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1089,7 +1213,21 @@ def main() -> int:
     ap.add_argument("--mode", "--decode-mode", dest="mode", choices=["graph", "eager"], default="graph",
                     help="graph: the prompt phase and the decode loop captured as HIP graphs and replayed; "
                          "eager: every call launched from Python")
+    ap.add_argument("--summarize-trace", metavar="DIR", default=None,
+                    help="print a summary of a rocprofv3 --kernel-trace run's output directory and exit")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="scale two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json "
+                         "under --key, print the summary and exit")
+    ap.add_argument("--key", default=None, help="workload key for --record-traffic")
+    ap.add_argument("--title", default="", help="title line of --summarize-trace")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.title, args.command), end="")
+        return 0
+    if args.record_traffic:
+        print(record_traffic(args.record_traffic[0], args.record_traffic[1], args.key, args.command), end="")
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py measures one GPU (each box has one); --gpus must be 1. The path "
                                    "shards by (batch entry, layer, KV head) with no exchange between GPUs."}))

@@ -232,41 +232,84 @@ def run_case(spec: syn.ConfigSpec, layer: int = 0, T: Optional[float] = None, st
 
 # ---------------------------------------------------------------- full-size layers, sampled heads
 
-def _oracle_heads(li, spec, heads, T, tau=TIE_TAU):
-    """Oracle profiles of the sampled (b, h) heads; each head's row blocks run on a thread
-    pool (numpy releases the GIL; BLAS limited to one thread per worker)."""
+def _oracle_heads(Qh, Kh, cls_h, spec, heads, T, tau=TIE_TAU):
+    """Oracle profiles of the sampled (b, h) heads from host copies Qh [B, Hq, n, d] / Kh [B, Hkv, n, d]
+    (only the sampled slices need to be filled).  Heads run on an outer thread pool, each head's row
+    blocks on an inner one (numpy releases the GIL; BLAS limited to one thread per worker)."""
     import os
     from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
     G = spec.group
     workers = min(16, len(os.sched_getaffinity(0)))
-    out = {}
-    with threadpool_limits(1), ThreadPoolExecutor(max_workers=workers) as ex:
-        for (b, h) in heads:
-            out[(b, h)] = ref.profile_head(li.Q[b, h * G:(h + 1) * G], li.K[b, h], li.token_class[b],
-                                           spec.r_l, spec.r_f, T, tau=tau, executor=ex)
-            log(f"[oracle] head b={b} h={h} done")
+
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=workers) as inner, \
+            ThreadPoolExecutor(max_workers=max(1, workers // 2)) as outer:
+        def one(bh):
+            b, h = bh
+            return bh, ref.profile_head(Qh[b, h * G:(h + 1) * G], Kh[b, h], cls_h[b], spec.r_l, spec.r_f, T,
+                                        tau=tau, executor=inner)
+        out = {}
+        for k, (bh, pr) in enumerate(outer.map(one, heads)):
+            out[bh] = pr
+            if k % 16 == 15 or k == len(heads) - 1:
+                log(f"[oracle] {k + 1} of {len(heads)} heads done")
     return out
 
 
+class _oracle_pool:
+    """A thread pool for per-head oracle work, BLAS limited to one thread per worker."""
+
+    def __enter__(self):
+        import os
+        from concurrent.futures import ThreadPoolExecutor
+        from threadpoolctl import threadpool_limits
+        self._lim = threadpool_limits(1)
+        self._ex = ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0))))
+        return self._ex
+
+    def __exit__(self, *exc):
+        self._ex.shutdown()
+        self._lim.restore_original_limits()
+        return False
+
+
 def run_fullsize(spec: syn.ConfigSpec, layer: int, sample: List[tuple], decode_sample: List[tuple],
-                 Ts=None, steps: Optional[int] = None) -> dict:
-    """One full-size layer on the GPU; oracle comparisons on sampled heads, forced-mode kept
-    lists for every head, decode outputs on sampled heads at sampled steps, and every head's
-    final cache."""
+                 Ts=None, steps: Optional[int] = None, out_steps: Optional[List[int]] = None) -> dict:
+    """One full-size layer drawn on the device (synth.device), every T of the workload:
+    * every head: column sums total G n, recovery monotone with R_4 = 1, |F| = k_f, the policy the
+      GPU's own recovery implies, the kept list under the GPU's policy and frequent set, and the
+      cache after the last decode step (positions, exact);
+    * the sampled heads against the oracle: lse, cum, band, recovery (1e-4), frequent set and
+      policy (exact unless flagged), compacted bytes;
+    * decode outputs of the decode-sampled heads at every step in ``out_steps`` (default: all)."""
+    from synth import device as sdev
     Ts = list(spec.T) if Ts is None else list(Ts)
     steps = spec.decode_steps if steps is None else steps
+    out_steps = list(range(steps)) if out_steps is None else sorted(set(out_steps))
     log(f"[fullsize] cfg={spec.cfg_id} {spec.name} layer={layer} B={spec.batch} Hq={spec.n_q_heads} "
-        f"Hkv={spec.n_kv_heads} n={spec.seq_len} T={Ts} steps={steps} sample={len(sample)}")
-    li = syn.make_layer(spec, layer)
-    B, Hq, n, d = li.Q.shape
-    Hkv = li.K.shape[1]
+        f"Hkv={spec.n_kv_heads} n={spec.seq_len} T={Ts} steps={steps} sample={len(sample)} "
+        f"decode sample={len(decode_sample)} output steps={len(out_steps)}")
+    li = sdev.make_layer_device(spec, layer, "cuda")
+    Qd, Kd, Vd, cls_d = li.Q, li.K, li.V, li.token_class
+    B, Hq, n, d = Qd.shape
+    Hkv = Kd.shape[1]
     G = Hq // Hkv
-    Qd, Kd, Vd = upload(li.Q, spec.dtype), upload(li.K, spec.dtype), upload(li.V, spec.dtype)
-    cls_d = torch.from_numpy(li.token_class).cuda()
-    orc = _oracle_heads(li, spec, sample, Ts[0])
-    report = {"flagged": 0, "checked": 0, "policies": {}}
-    prof_last = None
+    cls_h = li.token_class_host
+    Kh = sdev.host_f32(Kd)
+    Vh = sdev.host_f32(Vd)
+    Qh = np.zeros((B, Hq, n, d), dtype=np.float32)
+    for (b, h) in sample:
+        Qh[b, h * G:(h + 1) * G] = sdev.host_f32(Qd[b, h * G:(h + 1) * G])
+    orc = _oracle_heads(Qh, Kh, cls_h, spec, sample, Ts[0])
+    ds = sdev.make_decode_stream_device(spec, layer, steps, "cuda")
+    dq_h = {(b, h): sdev.host_f32(ds.q[:, b, h * G:(h + 1) * G]) for (b, h) in decode_sample}
+    dk_h = sdev.host_f32(ds.k)
+    dv_h = sdev.host_f32(ds.v)
+    ncls_h = ds.new_class_host
+    max_kept = int(max(np.count_nonzero(ncls_h[:, b]) for b in range(B)))
+    k_f, w_l = ref.budgets(n, spec.r_l, spec.r_f)
+    report = {"flagged": 0, "checked": 0, "policies": {}, "dec_err": 0.0}
+    tol = DEC_TOL[spec.dtype]
     for T in Ts:
         prof = fg.profile(Qd, Kd, cls_d, spec.r_l, spec.r_f, T, want_lse=True, want_band=True)
         torch.cuda.synchronize()
@@ -275,7 +318,6 @@ def run_fullsize(spec: syn.ConfigSpec, layer: int, sample: List[tuple], decode_s
         cum_g = prof.cum.cpu().numpy().astype(np.float64)
         F_g = prof.frequent()
         # properties of every head
-        k_f, w_l = ref.budgets(n, spec.r_l, spec.r_f)
         assert np.allclose(cum_g.sum(axis=-1), G * n, rtol=1e-4), "column sums must total G*n"
         assert np.all(np.diff(rec_g, axis=-1) >= -1e-6) and np.all(rec_g[..., 4] == 1.0)
         assert np.all(F_g.sum(axis=-1) == min(k_f, n))
@@ -306,56 +348,58 @@ def run_fullsize(spec: syn.ConfigSpec, layer: int, sample: List[tuple], decode_s
                 assert int(pol_g[b, h]) == policy, (b, h, rec_g[b, h], R)
             report["checked"] += 1
         report["policies"][T] = np.bincount(pol_g.reshape(-1), minlength=5).tolist()
-        log(f"[fullsize] T={T}: policies {report['policies'][T]}, sampled heads ok")
-        prof_last = prof
-    # compaction and decode with the last T
-    prof = prof_last
-    pol_g = prof.policy.cpu().numpy()
-    F_g = prof.frequent()
-    k_f, w_l = ref.budgets(n, spec.r_l, spec.r_f)
-    ds = syn.make_decode_stream(spec, layer, steps)
-    max_kept = int(max(np.count_nonzero(ds.new_class[:, b]) for b in range(B)))
-    cache = fg.compact(Kd, Vd, cls_d, prof, Hq, max_new_tokens=steps, max_new_kept=max_kept)
-    kept_g = cache.kept_positions()
-    for b in range(B):
-        for h in range(Hkv):
-            want = ref.kept_positions(li.token_class[b], F_g[b, h], w_l, int(pol_g[b, h]))
-            assert np.array_equal(kept_g[b * Hkv + h], want), (b, h)
-    for (b, h) in decode_sample:
-        pos, kc, vc = cache.rows(b * Hkv + h)
-        sel = torch.from_numpy(pos >= 0).cuda()
-        idx = torch.from_numpy(pos[pos >= 0]).cuda().long()
-        assert torch.equal(kc[sel], Kd[b, h][idx]) and torch.equal(vc[sel], Vd[b, h][idx])
-    check = sorted({0, 1, 2, 3, steps // 4, steps // 2, steps - 1})
-    qs, ks, vs = upload(ds.q, spec.dtype), upload(ds.k, spec.dtype), upload(ds.v, spec.dtype)
-    ncs = torch.from_numpy(ds.new_class).cuda()
-    got = {}
-    for t in range(steps):
-        o = cache.decode_step(qs[t], ks[t], vs[t], ncs[t])
-        if t in check:
-            got[t] = o.cpu().numpy()
-    torch.cuda.synchronize()
-    assert cache.error_bits() == 0
-    final = cache.kept_positions()
-    tol = DEC_TOL[spec.dtype]
-    worst = 0.0
-    for b in range(B):
-        for h in range(Hkv):
-            pol = int(pol_g[b, h])
-            sampled = (b, h) in decode_sample
-            sub = check if sampled else [steps - 1]
-            o_ref, c_ref = ref.decode_masked(li.K[b, h], li.V[b, h], li.token_class[b], F_g[b, h], w_l, pol,
-                                             ds.q[:, b, h * G:(h + 1) * G], ds.k[:, b, h], ds.v[:, b, h],
-                                             ds.new_class[:, b], steps_subset=sub)
-            assert np.array_equal(final[b * Hkv + h], c_ref[-1]), (b, h, "final cache")
-            if sampled:
-                for i, t in enumerate(sub):
-                    o_gpu = got[t][b, h * G:(h + 1) * G]
-                    scale = np.maximum(np.max(np.abs(o_ref[i]), axis=-1), 1e-30)
-                    err = float(np.max(np.max(np.abs(o_gpu - o_ref[i]), axis=-1) / scale))
-                    worst = max(worst, err)
-                    assert err <= tol, (b, h, t, err)
-    report["dec_err"] = worst
-    log(f"[fullsize] ok: checked={report['checked']} flagged={report['flagged']} dec err={worst:.2e} "
-        f"kept fraction={sum(len(k) for k in kept_g) / (B * Hkv * n):.3f}")
+        # compaction: the kept list of every head under the GPU's decisions, bytes of the sampled heads
+        cache = fg.compact(Kd, Vd, cls_d, prof, Hq, max_new_tokens=steps, max_new_kept=max_kept)
+        kept_g = cache.kept_positions()
+        for b in range(B):
+            for h in range(Hkv):
+                want = ref.kept_positions(cls_h[b], F_g[b, h], w_l, int(pol_g[b, h]))
+                assert np.array_equal(kept_g[b * Hkv + h], want), (b, h)
+        for (b, h) in sample:
+            pos, kc, vc = cache.rows(b * Hkv + h)
+            sel = torch.from_numpy(pos >= 0).cuda()
+            idx = torch.from_numpy(pos[pos >= 0]).cuda().long()
+            assert torch.equal(kc[sel], Kd[b, h][idx]) and torch.equal(vc[sel], Vd[b, h][idx])
+        # decode: every step on the device, outputs of the decode-sampled heads kept on the host
+        sel_q = torch.tensor([b * Hq + h * G + g for (b, h) in decode_sample for g in range(G)],
+                             dtype=torch.long, device="cuda")
+        got = np.zeros((len(out_steps), len(decode_sample), G, d), dtype=np.float32)
+        pos_of = {t: i for i, t in enumerate(out_steps)}
+        for t in range(steps):
+            o = cache.decode_step(ds.q[t], ds.k[t], ds.v[t], ds.new_class[t])
+            if t in pos_of:
+                got[pos_of[t]] = o.reshape(B * Hq, d)[sel_q].reshape(len(decode_sample), G, d).cpu().numpy()
+        torch.cuda.synchronize()
+        assert cache.error_bits() == 0
+        final = cache.kept_positions()
+        zq = np.zeros((steps, G, d))
+
+        def final_cache(bh):
+            b, h = bh
+            _, c_ref = ref.decode_masked(Kh[b, h], Vh[b, h], cls_h[b], F_g[b, h], w_l, int(pol_g[b, h]), zq,
+                                         dk_h[:, b, h], dv_h[:, b, h], ncls_h[:, b], steps_subset=[steps - 1])
+            return bh, c_ref[-1]
+
+        def outputs(i):
+            b, h = decode_sample[i]
+            o_ref, _ = ref.decode_masked(Kh[b, h], Vh[b, h], cls_h[b], F_g[b, h], w_l, int(pol_g[b, h]),
+                                         dq_h[(b, h)], dk_h[:, b, h], dv_h[:, b, h], ncls_h[:, b],
+                                         steps_subset=out_steps)
+            scale = np.maximum(np.max(np.abs(o_ref), axis=-1), 1e-30)
+            return i, np.max(np.abs(got[:, i] - o_ref), axis=-1) / scale
+
+        worst = 0.0
+        with _oracle_pool() as ex:
+            for (b, h), want in ex.map(final_cache, [(b, h) for b in range(B) for h in range(Hkv)]):
+                assert np.array_equal(final[b * Hkv + h], want), (b, h, "final cache")
+            for i, err in ex.map(outputs, range(len(decode_sample))):
+                worst = max(worst, float(err.max()))
+                assert err.max() <= tol, (decode_sample[i], int(pol_g[decode_sample[i]]), float(err.max()),
+                                          out_steps[int(np.argmax(err.max(axis=-1)))])
+        report["dec_err"] = max(report["dec_err"], worst)
+        log(f"[fullsize] T={T}: policies {report['policies'][T]}, sampled heads ok, kept lists of "
+            f"{B * Hkv} heads ok, decode err {worst:.2e} over {len(decode_sample)} heads x {len(out_steps)} steps, "
+            f"kept fraction {sum(len(k) for k in kept_g) / (B * Hkv * n):.3f}")
+        del cache, prof
+    log(f"[fullsize] ok: checked={report['checked']} flagged={report['flagged']}")
     return report

@@ -1,6 +1,18 @@
 """GPU parity at the full per-layer sizes of the Llama-1-7B stack, the Llama-1-65B
-stack and the 32k-token GQA workload, on sampled heads (the oracle is fp64 and
-O(n^2) per head), plus properties and forced-mode kept lists for every head."""
+stack and the 32k-token GQA workload, with inputs drawn on the device (the same
+generator the benchmark uses), against the fp64 oracle:
+
+* Llama-1-7B stack (B=8, 32 heads, n=4096): layers 0, 3, 4, 15, 16, 27, 28, 31 --
+  the outer four and the middle of the depth mix -- at T = 0.90, 0.95 and 0.99,
+  each T with its own compaction and 512 decode steps; sampled heads of every
+  planted type in batch entries 0 and 7 (all eight entries in layers 0 and 16);
+* Llama-1-65B stack (B=16, 64 heads, n=2048): layers 0, 3, 4, 40, 75, 76, 79, every
+  KV head of batch entries 0 and 15 against the oracle, 1024 decode steps;
+* 32k GQA (32 query / 8 KV heads): every KV head against the oracle, decode
+  outputs of every head at the first 32 steps and every 16th step after.
+
+In every case every head's kept list and final cache are checked exactly, and
+the decode outputs of the decode-sampled heads at every listed step."""
 import numpy as np
 import pytest
 
@@ -15,32 +27,39 @@ def gpl():
     return gpu_parity_lib
 
 
-def _sample(spec, layer, batch_entries, per_type=2, seed=0):
-    """A few KV heads of every planted type (and unplanted) for the given batch entries."""
+def _by_type(spec, layer, per_type):
+    """Up to per_type KV heads of each planted type (and unplanted) of one layer."""
     types = syn.head_types(spec, layer)
     picks = []
     for kind in ("special", "punct", "heavy", "local", "none"):
-        hs = [h for h, t in enumerate(types) if t == kind][:per_type]
-        picks += hs
-    return [(b, h) for b in batch_entries for h in sorted(set(picks))]
+        picks += [h for h, t in enumerate(types) if t == kind][:per_type]
+    return sorted(set(picks))
 
 
-@pytest.mark.parametrize("layer", [0, 16])
+@pytest.mark.parametrize("layer", [0, 3, 4, 15, 16, 27, 28, 31])
 def test_llama7b_stack_layer(gpl, layer):
     spec = syn.CONFIGS[2]                              # B=8, 32 heads, n=4096, T in {0.90, 0.95, 0.99}
-    sample = _sample(spec, layer, [0, 7])
-    rep = gpl.run_fullsize(spec, layer, sample, decode_sample=sample[:6])
+    batch = list(range(spec.batch)) if layer in (0, 16) else [0, 7]
+    heads = _by_type(spec, layer, 2)
+    sample = [(b, h) for b in batch for h in heads]
+    decode_sample = [(b, h) for b in (0, 7) for h in heads]
+    rep = gpl.run_fullsize(spec, layer, sample, decode_sample)
     assert rep["checked"] == 3 * len(sample)
 
 
-@pytest.mark.parametrize("layer", [0, 40])
+@pytest.mark.parametrize("layer", [0, 3, 4, 40, 75, 76, 79])
 def test_llama65b_stack_layer(gpl, layer):
     spec = syn.CONFIGS[3]                              # B=16, 64 heads, n=2048
-    sample = _sample(spec, layer, [0, 15])
-    gpl.run_fullsize(spec, layer, sample, decode_sample=sample[:6])
+    sample = [(b, h) for b in (0, 15) for h in range(spec.n_kv_heads)]
+    decode_sample = [(b, h) for b in (0, 15) for h in _by_type(spec, layer, 1)]
+    rep = gpl.run_fullsize(spec, layer, sample, decode_sample)
+    assert rep["checked"] == len(sample)
 
 
 def test_long_gqa_32k(gpl):
     spec = syn.CONFIGS[4]                              # 32 query / 8 KV heads, n=32768
-    sample = [(0, 0), (0, 4)]                          # one planted (special) and one unplanted KV head
-    gpl.run_fullsize(spec, 0, sample, decode_sample=sample)
+    heads = [(0, h) for h in range(spec.n_kv_heads)]
+    steps = spec.decode_steps
+    out_steps = sorted(set(range(32)) | set(range(0, steps, 16)) | {steps - 1})
+    rep = gpl.run_fullsize(spec, 0, heads, heads, out_steps=out_steps)
+    assert rep["checked"] == spec.n_kv_heads
