@@ -553,6 +553,62 @@ fg_status fg_decode_step_dynamic(fg_cache* cache, const void* q, const void* k_n
                        token_class, n_total);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------- decode without a caller workspace
+// The partial softmax states of fg_decode_step_noalloc live in this file-scope
+// device array (one copy per GPU, held until the process ends).  Host code
+// never uses the array's name as an address: the device address is taken once
+// per device with hipGetSymbolAddress and kept per device.
+namespace {
+
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of the scratch array (looked up on the first call per device).
+fg_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FG_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fg_decode_noalloc_max_bytes(void) { return kDecodeScratchBytes; }
+
+fg_status fg_decode_step_noalloc(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                 const uint8_t* new_class, float* out, hipStream_t stream) {
+  if (!cache) return fail(FG_ERR_INVALID_ARG, "cache is NULL");
+  fg_status s = check_shape(&cache->shape);
+  if (s != FG_OK) return s;
+  if ((s = check_cache_views(cache, &cache->shape)) != FG_OK) return s;
+  const size_t need = fg_decode_workspace_size(cache);
+  if (need > kDecodeScratchBytes) {
+    g_last_error = "decode state of " + std::to_string(need) + " bytes exceeds the static scratch of " +
+                   std::to_string(kDecodeScratchBytes) + " bytes; use fg_decode_step with a workspace";
+    return FG_ERR_WORKSPACE;
+  }
+  void* ptr = nullptr;
+  if ((s = scratch_for_current_device(&ptr)) != FG_OK) return s;
+  return decode_launch(cache, q, k_new, v_new, new_class, out, ptr, kDecodeScratchBytes, stream, false);
+}
+
 fg_status fg_decode_partials(const fg_cache* cache, const void* q, void* workspace, size_t workspace_bytes,
                              hipStream_t stream) {
   if (!cache) return fail(FG_ERR_INVALID_ARG, "cache is NULL");

@@ -99,6 +99,9 @@ def lib() -> ctypes.CDLL:
     L.fg_kernel_timing_read.argtypes = [ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_float), I32]
     L.fg_kernel_timing_read.restype = I32
     L.fg_kernel_name.argtypes, L.fg_kernel_name.restype = [I32], ctypes.c_char_p
+    L.fg_decode_noalloc_max_bytes.argtypes, L.fg_decode_noalloc_max_bytes.restype = [], S
+    L.fg_decode_step_noalloc.argtypes = [ca, P, P, P, P, P, P]
+    L.fg_decode_step_noalloc.restype = ctypes.c_int
     L.fg_peak_mfma_bf16.argtypes, L.fg_peak_mfma_bf16.restype = [P, P, I32, I32, P], ctypes.c_int
     L.fg_peak_exp.argtypes, L.fg_peak_exp.restype = [P, I32, I32, P], ctypes.c_int
     L.fg_peak_copy.argtypes, L.fg_peak_copy.restype = [P, P, S, I32, I32, P], ctypes.c_int
@@ -326,6 +329,27 @@ class Cache:
         self._workspace(q.device)
         _check(L.fg_decode_step(ctypes.byref(self.c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(new_class),
                                 _ptr(out), _ptr(self._ws), self._ws.numel(), _stream()), "fg_decode_step")
+        return out
+
+    def decode_step_noalloc(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            new_class: Optional[torch.Tensor], out: torch.Tensor) -> torch.Tensor:
+        """fg_decode_step_noalloc: the same step with the library's static decode scratch instead of a
+        workspace; allocates nothing (``out`` [B, Hq, d] fp32 is required)."""
+        s = self.shape
+        dt = self.t["k"].dtype
+        _need(q, "q", dt)
+        _need(k_new, "k_new", dt)
+        _need(v_new, "v_new", dt)
+        _need(out, "out", torch.float32)
+        if q.shape != (s.batch, s.n_q_heads, s.head_dim) or k_new.shape != (s.batch, s.n_kv_heads, s.head_dim) \
+                or v_new.shape != k_new.shape or out.shape != q.shape:
+            raise ValueError("decode input shapes do not match the cache")
+        if new_class is not None:
+            _need(new_class, "new_class", torch.uint8)
+            if new_class.shape != (s.batch,):
+                raise ValueError("new_class must be [B]")
+        _check(lib().fg_decode_step_noalloc(ctypes.byref(self.c), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                            _ptr(new_class), _ptr(out), _stream()), "fg_decode_step_noalloc")
         return out
 
     def decode_step_dynamic(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,

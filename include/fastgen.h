@@ -297,6 +297,25 @@ fg_status fg_decode_step(fg_cache* cache, const void* q, const void* k_new, cons
                          const uint8_t* new_class, float* out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fg_decode_step_noalloc -- fg_decode_step for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, arguments, outputs and errors, but the partial
+ * softmax states live in a static device array of the library instead of a
+ * caller workspace.  Nothing is allocated: no hipMalloc, no hipFree.
+ * Limit: fg_decode_workspace_size(cache) must not exceed
+ * fg_decode_noalloc_max_bytes() (16 MiB); a larger cache returns
+ * FG_ERR_WORKSPACE with a message (use fg_decode_step with a workspace).
+ * The array is per GPU (it holds its memory until the process ends) and keeps
+ * the last call's contents; every slot the merge reads is written by the same
+ * call first, so nothing needs clearing.  All calls on one GPU share it:
+ * calls that overlap on one GPU (different streams, or several host threads)
+ * race and give wrong outputs -- issue them in order on one stream.
+ */
+size_t fg_decode_noalloc_max_bytes(void);
+fg_status fg_decode_step_noalloc(fg_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                 const uint8_t* new_class, float* out, hipStream_t stream);
+
 /* fg_decode_partials -- only the first (split-K) launch of fg_decode_step for
  * the next position: reads the cache and q [B,Hq,d] and writes the partial
  * states into workspace; the cache, its next_pos and any output are left
