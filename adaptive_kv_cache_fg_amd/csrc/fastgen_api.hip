@@ -29,6 +29,8 @@ fg_status hip_fail(hipError_t e, const char* where) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr float kLog2eHost = 1.4426950408889634f;
+
 size_t elem_size(int dtype) { return dtype == FG_DTYPE_BF16 ? 2 : 4; }
 
 fg_status check_shape(const fg_shape* s) {
@@ -129,7 +131,8 @@ const char* fg_kernel_name(int32_t id) {
   static const char* names[FG_K_COUNT] = {"profile_rowstats", "profile_colsums", "profile_select",
                                           "compact_plan",     "compact_scan",    "compact_gather",
                                           "compact_worklist", "decode_partials", "decode_merge",
-                                          "attention",        "decode_track",    "profile_rowbins"};
+                                          "attention",        "decode_track",    "profile_rowbins",
+                                          "profile_rowbins_reduce"};
   return (id >= 0 && id < FG_K_COUNT) ? names[id] : "unknown";
 }
 
@@ -343,9 +346,57 @@ fg_status fg_profile_row_bins(const fg_shape* shape, const fg_params* params, co
   a.cls = token_class;
   a.fmask = freq_mask;
   a.lse = lse;
+  a.lse_scale = kLog2eHost;
   a.bins = bins;
   const hipError_t e = fg::launch_rowbins(a, stream);
   if (e != hipSuccess) return hip_fail(e, "row bins");
+  return FG_OK;
+}
+
+size_t fg_profile_rows_workspace_size(const fg_shape* s) {
+  if (check_shape(s) != FG_OK) return 0;
+  return fg_profile_workspace_size(s) + align256((size_t)s->batch * s->n_q_heads * s->seq_len * 5 * sizeof(float));
+}
+
+fg_status fg_profile_rows(const fg_shape* shape, const fg_params* params, const void* Q, const void* K,
+                          const uint8_t* token_class, uint8_t* policy, float* cum_score, float* recovery,
+                          uint32_t* freq_mask, float* row_min, float* bins_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  fg_status s = check_shape(shape);
+  if (s != FG_OK) return s;
+  if ((s = check_params(params)) != FG_OK) return s;
+  if (shape->batch > 65535) return fail(FG_ERR_UNSUPPORTED, "more than 65535 batch entries");
+  if ((double)shape->n_q_heads * ((shape->seq_len + 255) / 256) * 256 > 4294967295.0)
+    return fail(FG_ERR_UNSUPPORTED, "too many query heads x row blocks for one launch");
+  const size_t need = fg_profile_rows_workspace_size(shape);
+  if (!workspace || workspace_bytes < need) return fail(FG_ERR_WORKSPACE, "profile workspace too small");
+  // the sweeps and the top-k: lse2 (log2 domain) at the start of the workspace, cum, F
+  s = profile_impl(shape, params, Q, K, nullptr, token_class, nullptr, policy, cum_score, recovery, freq_mask,
+                   nullptr, nullptr, workspace, workspace_bytes, stream);
+  if (s != FG_OK) return s;
+  const size_t bins_off = fg_profile_workspace_size(shape);
+  float* bins = bins_out ? bins_out : reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bins_off);
+  fg::RowBinsArgs a{};
+  a.dtype = shape->dtype;
+  a.D = shape->head_dim;
+  a.B = shape->batch;
+  a.Hq = shape->n_q_heads;
+  a.Hkv = shape->n_kv_heads;
+  a.n = shape->seq_len;
+  int k_f = 0;
+  budgets(shape, params, &k_f, &a.w_l);
+  a.Q = Q;
+  a.K = K;
+  a.cls = token_class;
+  a.fmask = freq_mask;
+  a.lse = static_cast<const float*>(workspace);            // the sweeps' lse2
+  a.lse_scale = 1.0f;
+  a.bins = bins;
+  hipError_t e = fg::launch_rowbins(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "row bins");
+  e = fg::launch_rowbins_reduce(bins, shape->batch * shape->n_kv_heads, shape->n_q_heads / shape->n_kv_heads,
+                                shape->seq_len, params->T, recovery, policy, row_min, stream);
+  if (e != hipSuccess) return hip_fail(e, "row bins reduce");
   return FG_OK;
 }
 

@@ -134,10 +134,14 @@ struct RowBinsArgs {
   const void* K;
   const uint8_t* cls;      // [B, n] token classes
   const uint32_t* fmask;   // [B*Hkv, ceil(n/32)] frequent-set bits
-  const float* lse;        // [B*Hq*n] natural-log row log-sum-exp of the scaled scores
+  const float* lse;        // [B*Hq*n] row log-sum-exp of the scaled scores, natural log (times lse_scale:
+  float lse_scale;         //   log2(e) for natural-log input, 1 for the sweeps' own log2-domain values)
   float* bins;             // [B*Hq*n, 5] special, punct, frequent, local, rest
 };
 hipError_t launch_rowbins(const RowBinsArgs& a, hipStream_t st);
+// R_k from the row bins of each (b, KV head), policy, and the least kept share over the rows.
+hipError_t launch_rowbins_reduce(const float* bins, int H, int G, int n, double T, float* recovery, uint8_t* policy,
+                                 float* row_min, hipStream_t st);
 hipError_t launch_select(const ProfileArgs& a, hipStream_t st);
 hipError_t launch_head_map_accumulate(const float* recovery, const uint8_t* policy, double* rec_sum, int32_t* count,
                                       int P, int H, hipStream_t st);

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
 // tile feeds both blocks.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                      const float* __restrict__ lse2, float* __restrict__ cum,
+                                                      float* __restrict__ lse2, float* __restrict__ cum,
                                                       float* __restrict__ band, float2* __restrict__ cs_part,
                                                       const float2* __restrict__ rs_part, int kchunk,
                                                       float* __restrict__ lse_out, int Hq, int Hkv, int n,
@@ -230,7 +230,8 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   float lpre = 0.f;
   // With sweep 1 split over key chunks (rs_part), a row's log-sum-exp is merged here from the
   // chunks' (max, sum) pairs: the first kPre pairs are loaded with the tile, the merge waits for
-  // the tile's commit; the key block 0 workgroups (which see every row once) write lse_out.
+  // the tile's commit; the key block 0 workgroups (which see every row once) write the merged
+  // lse2 (so it is complete after either sweep layout) and lse_out.
   constexpr int kPre = 8;
   float2 pre[kPre];
   int pre_nc = 0, pre_row = 0;
@@ -277,7 +278,10 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
           if (k < pre_nc) merge(pre[k]);
         for (int k = kPre; k < pre_nc; ++k) merge(rs_part[((size_t)k * nbq + pre_qh) * n + pre_row]);
         lpre = pre_row < i_end ? Mx + fast_log2(Ls) : INFINITY;
-        if (lse_out && kb == 0 && pre_row < i_end) lse_out[pre_qh * n + pre_row] = lpre * kLn2;
+        if (kb == 0 && pre_row < i_end) {                        // every row once: the merged statistics
+          lse2[pre_qh * n + pre_row] = lpre;                     // (nothing reads lse2 in a split sweep)
+          if (lse_out) lse_out[pre_qh * n + pre_row] = lpre * kLn2;
+        }
       }
       lse_t[u & 1][threadIdx.x] = lpre;                           // rows past the chunk get P = 0
     }

@@ -56,8 +56,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void rowbins_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                       const uint8_t* __restrict__ cls,
                                                       const uint32_t* __restrict__ fmask,
-                                                      const float* __restrict__ lse, float* __restrict__ bins,
-                                                      int Hq, int Hkv, int n, int n_rb, int w_l, float c) {
+                                                      const float* __restrict__ lse, float lse_scale,
+                                                      float* __restrict__ bins, int Hq, int Hkv, int n, int n_rb,
+                                                      int w_l, float c) {
   using M = Mfma<T>;
   using op_t = typename M::op_t;
   constexpr int NK = D / M::KS;
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void rowbins_kernel(const T* __restrict__ Q
     const int qr = min(qrow[cb], n - 1);                  // rows past n are computed and dropped
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) qop[cb][kk] = global_operand<T, D>(Qh + (size_t)qr * D, kk, lane);
-    lse2[cb] = lse[bh * n + qr] * kLog2e;
+    lse2[cb] = lse[bh * n + qr] * lse_scale;
   }
   // bins^T of this wave's two 32-row blocks: accumulator row = level (0..3 kept
   // levels, 4 row total), column = query row
@@ -231,7 +232,84 @@ static hipError_t launch_rowbins_t(const RowBinsArgs& a, hipStream_t st) {
   const float c = kLog2e / sqrtf((float)D);
   timed_begin(FG_K_ROWBINS, st);
   rowbins_kernel<T, D><<<dim3((unsigned)(a.Hq * n_rb), a.B), dim3(256), 0, st>>>(
-      (const T*)a.Q, (const T*)a.K, a.cls, a.fmask, a.lse, a.bins, a.Hq, a.Hkv, a.n, n_rb, a.w_l, c);
+      (const T*)a.Q, (const T*)a.K, a.cls, a.fmask, a.lse, a.lse_scale, a.bins, a.Hq, a.Hkv, a.n, n_rb, a.w_l, c);
+  timed_end(st);
+  return hipGetLastError();
+}
+
+// Recovery of the row route: per (b, KV head) hd, whose G query heads' rows are
+// the G n consecutive rows [hd G n, (hd + 1) G n) of bins, the per-level sums in
+// fp64 (each thread a fixed stride of rows, then a fixed reduction tree),
+// R_k = (sum_{l <= k} mass_l) / (G n) for k <= 3 and R_4 = 1 by definition,
+// policy = min{k : R_k >= T}, and row_min[k] = the least kept share
+// sum_{l <= k} bins[i][l] over the rows (row_min[4]: the least row total).
+constexpr int kReduceThreads = 256;
+__global__ __launch_bounds__(kReduceThreads) void rowbins_reduce_kernel(const float* __restrict__ bins, int G, int n,
+                                                                        double T, float* __restrict__ recovery,
+                                                                        uint8_t* __restrict__ policy,
+                                                                        float* __restrict__ row_min) {
+  __shared__ double s_sum[kReduceThreads / kWave][4];
+  __shared__ float s_min[kReduceThreads / kWave][5];
+  const int hd = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long rows = (long long)G * n;
+  const float* base = bins + (size_t)hd * rows * 5;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  float mn[5] = {INFINITY, INFINITY, INFINITY, INFINITY, INFINITY};
+  for (long long r = tid; r < rows; r += kReduceThreads) {
+    const float* o = base + r * 5;
+    const double b0 = o[0], b1 = o[1], b2 = o[2], b3 = o[3], b4 = o[4];
+    s[0] += b0;
+    s[1] += b1;
+    s[2] += b2;
+    s[3] += b3;
+    const double c1 = b0 + b1, c2 = c1 + b2, c3 = c2 + b3;
+    mn[0] = fminf(mn[0], (float)b0);
+    mn[1] = fminf(mn[1], (float)c1);
+    mn[2] = fminf(mn[2], (float)c2);
+    mn[3] = fminf(mn[3], (float)c3);
+    mn[4] = fminf(mn[4], (float)(c3 + b4));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+    for (int l = 0; l < 4; ++l) s[l] += __shfl_xor(s[l], o);
+#pragma unroll
+    for (int l = 0; l < 5; ++l) mn[l] = fminf(mn[l], __shfl_xor(mn[l], o));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int l = 0; l < 4; ++l) s_sum[wave][l] = s[l];
+#pragma unroll
+    for (int l = 0; l < 5; ++l) s_min[wave][l] = mn[l];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double acc = 0.0;
+    int pol = 4;
+    for (int l = 0; l < 4; ++l) {
+      double t = 0.0;
+      for (int w = 0; w < kReduceThreads / kWave; ++w) t += s_sum[w][l];
+      acc += t;
+      const double R = acc / (double)rows;
+      recovery[(size_t)hd * 5 + l] = (float)R;
+      if (pol == 4 && R >= T) pol = l;
+    }
+    recovery[(size_t)hd * 5 + 4] = 1.0f;
+    policy[hd] = (uint8_t)pol;
+    if (row_min) {
+      for (int l = 0; l < 5; ++l) {
+        float m = s_min[0][l];
+        for (int w = 1; w < kReduceThreads / kWave; ++w) m = fminf(m, s_min[w][l]);
+        row_min[(size_t)hd * 5 + l] = m;
+      }
+    }
+  }
+}
+
+hipError_t launch_rowbins_reduce(const float* bins, int H, int G, int n, double T, float* recovery, uint8_t* policy,
+                                 float* row_min, hipStream_t st) {
+  timed_begin(FG_K_ROWBINS_REDUCE, st);
+  rowbins_reduce_kernel<<<dim3(H), dim3(kReduceThreads), 0, st>>>(bins, G, n, T, recovery, policy, row_min);
   timed_end(st);
   return hipGetLastError();
 }

@@ -24,7 +24,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 KERNEL_NAMES = ["profile_rowstats", "profile_colsums", "profile_select", "compact_plan", "compact_scan",
                 "compact_gather", "compact_worklist", "decode_partials", "decode_merge", "attention", "decode_track",
-                "profile_rowbins"]
+                "profile_rowbins", "profile_rowbins_reduce"]
 
 
 class FgShape(ctypes.Structure):
@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
     L.fg_attention.argtypes, L.fg_attention.restype = [sh, P, P, P, P, P, P], ctypes.c_int
     L.fg_profile_row_bins.argtypes = [sh, pa, P, P, P, P, P, P, P]
     L.fg_profile_row_bins.restype = ctypes.c_int
+    L.fg_profile_rows_workspace_size.argtypes, L.fg_profile_rows_workspace_size.restype = [sh], S
+    L.fg_profile_rows.argtypes = [sh, pa, P, P, P, P, P, P, P, P, P, P, S, P]
+    L.fg_profile_rows.restype = ctypes.c_int
     L.fg_decode_step_dynamic.argtypes = [ca, P, P, P, P, P, I32, P, P, P, S, P]
     L.fg_decode_step_dynamic.restype = ctypes.c_int
     L.fg_decode_track_init.argtypes, L.fg_decode_track_init.restype = [ca, P, P, P], ctypes.c_int
@@ -154,6 +157,8 @@ class Profile:
     r_f: float
     T: float
     out: Optional[torch.Tensor] = None   # [B, Hq, n, d] attention output (profile with V only)
+    row_min: Optional[torch.Tensor] = None   # [B, Hkv, 5] least kept share of a row (profile_rows only)
+    bins: Optional[torch.Tensor] = None      # [B, Hq, n, 5] per-row level bins (profile_rows only)
 
     def frequent(self) -> np.ndarray:
         """Host bool array [B, Hkv, n] of the frequent set (synchronises)."""
@@ -213,6 +218,43 @@ def profile(Q: torch.Tensor, K: torch.Tensor, token_class: torch.Tensor, r_l: fl
                                       _ptr(fmask), _ptr(lse), _ptr(band), _ptr(ws), ws_bytes, _stream()),
                "fg_profile_attention")
     return Profile(policy, cum, rec, fmask, lse, band, r_l, r_f, T, out)
+
+
+def profile_rows(Q: torch.Tensor, K: torch.Tensor, token_class: torch.Tensor, r_l: float, r_f: float, T: float,
+                 want_bins: bool = False, policy_out: Optional[torch.Tensor] = None) -> Profile:
+    """fg_profile_rows: fg_profile with recovery from the per-row level bins, plus ``row_min``
+    [B, Hkv, 5] (the least kept share of any row under each shortlist entry) and, with
+    ``want_bins``, ``bins`` [B, Hq, n, 5]."""
+    _need(Q, "Q")
+    _need(K, "K")
+    _need(token_class, "token_class", torch.uint8)
+    shape = make_shape(Q, K)
+    B, Hq, n, _ = Q.shape
+    Hkv = K.shape[1]
+    dev = Q.device
+    if policy_out is None:
+        policy = torch.empty((B, Hkv), dtype=torch.uint8, device=dev)
+    else:
+        _need(policy_out, "policy_out", torch.uint8)
+        if policy_out.numel() != B * Hkv or policy_out.device != dev:
+            raise ValueError(f"policy_out must hold {B * Hkv} elements on {dev}")
+        policy = policy_out.view(B, Hkv)
+    cum = torch.empty((B, Hkv, n), dtype=torch.float32, device=dev)
+    rec = torch.empty((B, Hkv, 5), dtype=torch.float32, device=dev)
+    fmask = torch.empty((B, Hkv, (n + 31) // 32), dtype=torch.int32, device=dev)
+    row_min = torch.empty((B, Hkv, 5), dtype=torch.float32, device=dev)
+    bins = torch.empty((B, Hq, n, 5), dtype=torch.float32, device=dev) if want_bins else None
+    L = lib()
+    ws_bytes = L.fg_profile_rows_workspace_size(ctypes.byref(shape))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    params = FgParams(r_l, r_f, T)
+    _check(L.fg_profile_rows(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), _ptr(K), _ptr(token_class),
+                             _ptr(policy), _ptr(cum), _ptr(rec), _ptr(fmask), _ptr(row_min), _ptr(bins), _ptr(ws),
+                             ws_bytes, _stream()), "fg_profile_rows")
+    prof = Profile(policy, cum, rec, fmask, None, None, r_l, r_f, T)
+    prof.row_min = row_min
+    prof.bins = bins
+    return prof
 
 
 def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, want_lse: bool = False,

@@ -99,6 +99,7 @@ def cpu_baseline(spec: syn.ConfigSpec, sample_heads: int, layer: int = 0) -> dic
 
 # ---------------------------------------------------------------- HBM traffic from counters
 CALIB_BYTES = 256 << 20
+CALIB_BLOCKS = 1000          # the calibration copy's grid (1000 x 256 threads), unlike any other copy launched
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -128,6 +129,17 @@ def measured_traffic(kernel: str, workload: str):
         return None
     v = entry.get("bytes_per_launch", {}).get(kernel)
     return float(v) if v is not None else None
+
+
+def calibration_copy(torch, fg) -> None:
+    """A copy of known size (CALIB_BYTES read, CALIB_BYTES written) with a grid of its own, outside
+    any timed region: under rocprofv3 --pmc, what FETCH_SIZE / WRITE_SIZE read for it scales the
+    counters of the other kernels (record_traffic)."""
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    fg.peak_copy(src, dst, False, CALIB_BLOCKS)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 # ---------------------------------------------------------------- GPU path
@@ -599,13 +611,7 @@ def bench_layer(args, spec: syn.ConfigSpec, cpu) -> dict:
     if not args.no_stability:
         stab = decode_stability(torch, fg, Kd, Vd, cls, prof, qs, ks, vs, ncs, spec, T)
 
-    # a plain copy of known size, outside the timed region: the reference that scales the
-    # FETCH_SIZE / WRITE_SIZE counters of the kernels above when this script runs under rocprofv3
-    calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
-    calib_dst = torch.empty_like(calib_src)
-    calib_dst.copy_(calib_src)
-    torch.cuda.synchronize()
-    del calib_src, calib_dst
+    calibration_copy(torch, fg)
 
     result = {
         "metric": METRIC,
@@ -798,10 +804,12 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
     caches = [None] * L
     profs = [None] * L
 
+    profile_fn = fg.profile_rows if args.route == "rows" else fg.profile
+
     def prompt_phase(check=True):
         for l in range(L):
             c = caches[l]
-            prof = fg.profile(lay[l].Q, lay[l].K, cls, spec.r_l, spec.r_f, T,
+            prof = profile_fn(lay[l].Q, lay[l].K, cls, spec.r_l, spec.r_f, T,
                               policy_out=None if c is None else c.t["policy"])
             caches[l] = fg.compact(lay[l].K, lay[l].V, cls, prof, Hq, max_new_tokens=steps_dec, max_new_kept=mk,
                                    reuse=c, check=check)
@@ -919,6 +927,20 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
     kstats = {k: {"launches_per_step": float(len(v)), "avg_us": 1e3 * float(np.mean(v)),
                   "total_us_per_step": 1e3 * float(np.sum(v)), "timing": "events around each launch (eager pass)"}
               for k, v in per.items()}
+    row_route = None
+    if args.route == "columns" and not args.no_row_route:
+        # the other recovery route (per-row level bins, fg_profile_rows) on every layer, one eager pass
+        # with events around each launch; the cache refill is not needed for its cost
+        fg.timing_read()
+        fg.timing_enable(True)
+        for l in range(L):
+            fg.profile_rows(lay[l].Q, lay[l].K, cls, spec.r_l, spec.r_f, T)
+        torch.cuda.synchronize()
+        fg.timing_enable(False)
+        rr = {}
+        for name, ms in fg.timing_read():
+            rr.setdefault(name, []).append(ms)
+        row_route = {k: {"avg_us": 1e3 * float(np.mean(v)), "launches": len(v)} for k, v in rr.items()}
 
     def rows_kept(c):
         """Cache rows in use that hold a key (pos >= 0), summed over the heads of one layer."""
@@ -1011,6 +1033,20 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
             ach = units / avg_s / 1e9
             kstats[k].update(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,
                              algorithmic_bytes=units)
+    if row_route is not None:
+        rb = row_route.get("profile_rowbins")
+        if rb:
+            ach = sweep_flops / (rb["avg_us"] * 1e-6) / 1e12
+            rb.update(bound="mfma", achieved=ach, peak=peak_mfma, unit="TFLOP/s", frac=ach / peak_mfma,
+                      note="score flops only (the binning products add half as many again)")
+        per_layer = sum(v["avg_us"] * v["launches"] for v in row_route.values()) / L
+        cols_layer = sum(kstats[k]["total_us_per_step"] for k in ("profile_rowstats", "profile_colsums",
+                                                                   "profile_select") if k in kstats) / L
+        row_route = {"kernels": row_route, "profile_rows_us_per_layer": per_layer,
+                     "profile_columns_us_per_layer": cols_layer,
+                     "note": "fg_profile_rows (recovery from the per-row level bins, plus the least kept share "
+                             "of any row) against fg_profile (recovery from the column sums), events around each "
+                             "launch, every layer; bench.py --route rows times the prompt phase with it"}
     dominant = max((k for k in ("profile_rowstats", "profile_colsums", "compact_gather", "decode_partials",
                                 "decode_merge") if k in kstats), key=lambda k: kstats[k]["total_us_per_step"])
     dk = kstats[dominant]
@@ -1055,13 +1091,7 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
         phases["decode_frac_of_measured_copy"] = phases["decode_hbm_frac"] * HBM_PEAK_GBS / cp
         roofline["frac_of_measured"] = dk["achieved"] / (cp if dk["bound"] == "hbm" else mf)
 
-    # a plain copy of known size, outside the timed region: the reference that scales the
-    # FETCH_SIZE / WRITE_SIZE counters of the kernels above when this script runs under rocprofv3
-    calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
-    calib_dst = torch.empty_like(calib_src)
-    calib_dst.copy_(calib_src)
-    torch.cuda.synchronize()
-    del calib_src, calib_dst
+    calibration_copy(torch, fg)
 
     workload = (f"{spec.name}: {L} layers x {Hq} heads (KV {Hkv}), d={d}, {spec.dtype}, B={B}, n={n}, "
                 f"T={T}, r_l={spec.r_l}, r_f={spec.r_f}, {steps_dec} decode steps through every layer")
@@ -1074,6 +1104,7 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
                    "key": key},
         "decode_tok_s": decode_tok_s, "mode": args.mode, "prompt_ms": prompt_ms, "decode_ms": decode_ms,
         "roofline": roofline, "phases": phases, "compression": compression, "kernels": kstats,
+        "route": args.route, "row_route": row_route,
         "peaks": pk, "input_generation_s": gen_s, "cpu_baseline": cpu,
     }
 
@@ -1133,13 +1164,36 @@ def summarize_trace(directory: str, title: str, command: str) -> str:
 
 
 def _counter_means(directory: str, counter: str) -> dict:
-    """Mean of one counter per dispatch, by full kernel name (rocprofv3 --pmc counter collection)."""
+    """Mean of one counter per dispatch, by short kernel name (rocprofv3 --pmc counter collection);
+    the calibration copy (peak_copy_kernel launched with CALIB_BLOCKS workgroups) under its own key."""
     per = {}
     for r in _csv_rows(directory, "counter_collection.csv"):
         if r.get("Counter_Name") != counter:
             continue
-        per.setdefault(r.get("Kernel_Name", ""), []).append(float(r["Counter_Value"]))
+        k = _short(r.get("Kernel_Name", ""))
+        if k == "peak_copy_kernel" and int(float(r.get("Grid_Size", 0))) == CALIB_BLOCKS * 256:
+            k = "calibration_copy"
+        per.setdefault(k, []).append(float(r["Counter_Value"]))
     return {k: (float(np.mean(v)), len(v)) for k, v in per.items()}
+
+
+def summarize_counters(directories, title: str, command: str) -> str:
+    """Per library kernel, the mean per dispatch of every counter in rocprofv3 --pmc runs."""
+    per = {}
+    for directory in directories:
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            k = _short(r.get("Kernel_Name", ""))
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for v in per.values() for c in v})
+    lines = [f"# {title}", f"# commands: {command}", "# mean per dispatch over the dispatches of the run",
+             f"{'kernel':28s} {'dispatches':>10s} " + " ".join(f"{c:>22s}" for c in names)]
+    for k, v in sorted(per.items()):
+        if not k.endswith("_kernel") or k.startswith(("elementwise", "vectorized")):
+            continue
+        cnt = max(len(x) for x in v.values())
+        lines.append(f"{k[:28]:28s} {cnt:10d} " + " ".join(
+            f"{np.mean(v[c]):22.4g}" if c in v else f"{'-':>22s}" for c in names))
+    return "\n".join(lines) + "\n"
 
 
 def record_traffic(fetch_dir: str, write_dir: str, key: str, command: str) -> str:
@@ -1149,10 +1203,7 @@ def record_traffic(fetch_dir: str, write_dir: str, key: str, command: str) -> st
     a text summary."""
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
-    # the calibration copy: of the kernels that read about what they write, the one whose write
-    # volume is closest to CALIB_BYTES (a fill writes without reading)
-    both = [k for k in write if k in fetch and fetch[k][0] > 0.25 * write[k][0] and "fg::" not in k]
-    calib = min(both, key=lambda k: abs(write[k][0] * 1024 - CALIB_BYTES))
+    calib = "calibration_copy"
     f_factor = CALIB_BYTES / (fetch[calib][0] * 1024)
     w_factor = CALIB_BYTES / (write[calib][0] * 1024)
     names = {"rowstats_kernel": "profile_rowstats", "colsums_kernel": "profile_colsums",
@@ -1161,16 +1212,12 @@ def record_traffic(fetch_dir: str, write_dir: str, key: str, command: str) -> st
     per_launch = {}
     lines = [f"# HBM traffic per dispatch, {key}", f"# commands: {command}",
              "# FETCH_SIZE / WRITE_SIZE: rocprofv3 derived counters in KiB per dispatch, averaged over dispatches;",
-             f"# scaled bytes = FETCH * {f_factor:.4f} + WRITE * {w_factor:.4f} (factors from the {CALIB_BYTES} B copy, "
-             f"kernel {_short(calib)})"]
+             f"# scaled bytes = FETCH * {f_factor:.4f} + WRITE * {w_factor:.4f} (factors from the {CALIB_BYTES} B "
+             f"calibration copy: FETCH {fetch[calib][0]:.1f} KiB, WRITE {write[calib][0]:.1f} KiB)"]
     for k, short in names.items():
-        fk = [x for x in fetch if _short(x) == k]
-        wk = [x for x in write if _short(x) == k]
-        if not fk or not wk:
+        if k not in fetch or k not in write:
             continue
-        nf, nw = sum(fetch[x][1] for x in fk), sum(write[x][1] for x in wk)
-        fv = sum(fetch[x][0] * fetch[x][1] for x in fk) / nf        # dispatch-weighted over instantiations
-        wv = sum(write[x][0] * write[x][1] for x in wk) / nw
+        (fv, nf), (wv, _) = fetch[k], write[k]
         b = fv * 1024 * f_factor + wv * 1024 * w_factor
         per_launch[short] = b
         lines.append(f"{k:26s} dispatches {nf:7d}  FETCH_SIZE {fv:13.1f} KiB  WRITE_SIZE {wv:12.1f} KiB  "
@@ -1201,6 +1248,10 @@ def main() -> int:
     ap.add_argument("--stack-layers", type=int, default=None, help=argparse.SUPPRESS)
     ap.add_argument("--decode-steps", type=int, default=None, help=argparse.SUPPRESS)
     ap.add_argument("--graph-tokens", type=int, default=16, help="generated tokens per captured decode graph")
+    ap.add_argument("--route", choices=["columns", "rows"], default="columns",
+                    help="recovery route of the prompt phase: column sums (fg_profile) or per-row level bins "
+                         "(fg_profile_rows)")
+    ap.add_argument("--no-row-route", action="store_true", help="skip timing the per-row route beside the default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=16)
     ap.add_argument("--no-peaks", action="store_true", help="skip the chip-ceiling micro-benchmarks")
@@ -1218,12 +1269,17 @@ def main() -> int:
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="scale two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json "
                          "under --key, print the summary and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
+                    help="print per-kernel counter means of rocprofv3 --pmc runs and exit")
     ap.add_argument("--key", default=None, help="workload key for --record-traffic")
     ap.add_argument("--title", default="", help="title line of --summarize-trace")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.title, args.command), end="")
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.title, args.command), end="")
         return 0
     if args.record_traffic:
         print(record_traffic(args.record_traffic[0], args.record_traffic[1], args.key, args.command), end="")

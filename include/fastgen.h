@@ -160,6 +160,29 @@ fg_status fg_profile_row_bins(const fg_shape* shape, const fg_params* params, co
                               hipStream_t stream);
 
 /*
+ * fg_profile_rows -- fg_profile with the per-row level bins as the recovery
+ * route (the constraint equation of Method read row by row: each row's kept
+ * share under each shortlist entry, then averaged).  The sweeps and the top-k
+ * run as in fg_profile (cum_score, freq_mask as there); then the row-bins sweep
+ * (fg_profile_row_bins) bins every row of every query head on the matrix cores,
+ * and a reduction per (b, KV head) gives
+ *   R_k = (1 / (G n)) sum_g sum_i sum_{l <= k} bins[g][i][l]   (fp64 sums), R_4 = 1,
+ *   policy = min { k : R_k >= T },
+ *   row_min[k] = min over the G n rows of sum_{l <= k} bins[g][i][l]  (the least
+ *                kept share of any row; row_min[4] = the least row total),
+ * written to recovery [B*Hkv*5], policy [B*Hkv] and row_min [B*Hkv*5] (optional,
+ * NULL to skip).  R_k equals fg_profile's column-sum route up to rounding.
+ * bins_out [B*Hq*n*5] fp32 (optional) receives the bins; else they live in the
+ * workspace of fg_profile_rows_workspace_size(shape) bytes.  Errors as
+ * fg_profile and fg_profile_row_bins.
+ */
+size_t fg_profile_rows_workspace_size(const fg_shape* shape);
+fg_status fg_profile_rows(const fg_shape* shape, const fg_params* params, const void* Q, const void* K,
+                          const uint8_t* token_class, uint8_t* policy, float* cum_score, float* recovery,
+                          uint32_t* freq_mask, float* row_min, float* bins_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Multi-prompt head map (jisaku.com glossary entry "FastGen", section
  * Profiling phase: heads are typed once from sample prompts, the map is saved
  * and applied at inference).  Profile P prompts (one fg_profile call with
@@ -421,7 +444,7 @@ enum {
   FG_K_GATHER = 5,     /* also writes the decode work list */
   FG_K_WORKLIST = 6,   /* reserved: no separate launch */
   FG_K_DECODE = 7, FG_K_DECODE_MERGE = 8, FG_K_ATTENTION = 9, FG_K_TRACK = 10,
-  FG_K_ROWBINS = 11, FG_K_COUNT = 12
+  FG_K_ROWBINS = 11, FG_K_ROWBINS_REDUCE = 12, FG_K_COUNT = 13
 };
 void fg_kernel_timing_enable(int enable);
 int32_t fg_kernel_timing_read(int32_t* kernel_ids, float* ms, int32_t max);

@@ -76,12 +76,15 @@ def brute_force_head(Qg: np.ndarray, K: np.ndarray, cls: np.ndarray, k_f: int, w
         return sorted(j for j in keep if j <= i)
 
     distance = np.zeros(5)
+    worst = np.zeros(5)                                     # the largest per-row distance of each entry
     for entry in range(5):
         tot = 0.0
         for g in range(G):
             for i in range(n):
                 approx = _restricted_row(Qg[g, i], K, kept_for_row(entry, i))
-                tot += 0.5 * np.abs(rows[g][i] - approx).sum()
+                dist_i = 0.5 * np.abs(rows[g][i] - approx).sum()
+                tot += dist_i
+                worst[entry] = max(worst[entry], dist_i)
         distance[entry] = tot / (G * n)
     cost = np.array([len([j for j in kept_for_row(e, n) if j < n]) for e in range(5)])
     feasible = [e for e in range(5) if distance[e] <= 1.0 - T]
@@ -93,6 +96,7 @@ def brute_force_head(Qg: np.ndarray, K: np.ndarray, cls: np.ndarray, k_f: int, w
         "F": np.array([j in F for j in range(n)]),
         "distance": distance,
         "recovery": 1.0 - distance,
+        "worst_row_recovery": 1.0 - worst,
         "cost": cost,
         "policy": int(policy),
         "kept": np.array([j for j in kept_for_row(policy, n) if j < n], dtype=np.int64),

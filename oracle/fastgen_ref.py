@@ -227,6 +227,15 @@ def recovery_from_bins(bins: np.ndarray) -> np.ndarray:
     return R
 
 
+def row_min_share(bins: np.ndarray) -> np.ndarray:
+    """The least kept share of any row under each shortlist entry: for entry k, the minimum
+    over the query heads g and rows i of sum_{l <= k} bins[g, i, l] -- the constraint of the
+    Method section (second paragraph) read per row and taken at its worst row instead of
+    averaged.  Entry 4 is the least row total (1 up to rounding).  A diagnostic beside R_k."""
+    cum = np.cumsum(np.asarray(bins, dtype=np.float64), axis=-1)
+    return cum.reshape(-1, N_LEVELS).min(axis=0)
+
+
 def select_policy(R: np.ndarray, T: float) -> int:
     """Cheapest shortlist entry meeting R_k >= T (costs are non-decreasing along the list)."""
     for k in range(N_LEVELS):
@@ -564,7 +573,7 @@ def pairs_causal(n: int) -> int:
 
 __all__: Sequence[str] = [
     "budgets", "causal_attention_rows", "attention_output", "column_scores", "frequent_set", "key_levels", "row_bins",
-    "recovery_from_bins", "select_policy", "kept_positions", "compact_head", "profile_head",
+    "recovery_from_bins", "row_min_share", "select_policy", "kept_positions", "compact_head", "profile_head",
     "profile_layer", "decode_incremental", "decode_masked", "HeadProfile", "head_type_map",
     "decode_tracking", "DynamicFrequentHead",
 ]

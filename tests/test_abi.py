@@ -211,7 +211,8 @@ def test_status_strings_and_kernel_names():
     L = fgb.lib()
     assert L.fg_status_string(0) == b"ok"
     assert L.fg_status_string(4) == b"cache capacity exceeded"
-    assert [L.fg_kernel_name(i).decode() for i in range(12)] == fgb.KERNEL_NAMES
+    assert [L.fg_kernel_name(i).decode() for i in range(len(fgb.KERNEL_NAMES))] == fgb.KERNEL_NAMES
+    assert L.fg_kernel_name(len(fgb.KERNEL_NAMES)) == b"unknown"
     def chunk(n):
         return L.fg_decode_chunk_rows(ctypes.byref(fgb.FgShape(1, 4, 4, n, 128, 0)))
     assert [chunk(n) for n in (1, 128, 8192, 8193, 32768, 1 << 20)] == [128, 128, 128, 256, 512, 2048]

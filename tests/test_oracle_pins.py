@@ -133,6 +133,9 @@ def test_brute_force_matches_oracle():
         np.testing.assert_allclose(prof.cum, bf["cum"], rtol=0, atol=1e-12)
         # the literal constraint: 1 - mean half-L1 distance == retained mass
         np.testing.assert_allclose(prof.R, bf["recovery"], rtol=0, atol=1e-12)
+        # the worst row: the least kept share equals one minus the largest per-row half-L1 distance
+        if not prof.topk_tie:
+            np.testing.assert_allclose(ref.row_min_share(prof.bins), bf["worst_row_recovery"], rtol=0, atol=1e-12)
         if not prof.topk_tie:
             assert np.array_equal(prof.F, bf["F"])
         if not prof.near_T and not prof.topk_tie:
@@ -721,3 +724,25 @@ def test_mistake_wrong_precedence_is_caught(monkeypatch):
     monkeypatch.setattr(ref, "key_levels", swapped)
     with pytest.raises(AssertionError):
         test_brute_force_matches_oracle()
+
+
+@pytest.mark.parametrize("n,k_f,w_l", [(64, 19, 19), (50, 5, 12), (33, 0, 7), (40, 10, 0), (17, 16, 16)])
+def test_row_min_share_uniform_closed_form(n, k_f, w_l):
+    """Zero queries: row i spreads 1/(i+1) over keys 0..i, so cum_j = H_n - H_j is strictly
+    decreasing and F = {0 .. k_f-1}.  With the special set {0} and no punctuation, row i keeps
+    1/(i+1) under entries 0 and 1, |{0} u F u window| / (i+1) under entries 2 and 3; the kept
+    counts stop growing once the row passes them, so the least share of each entry is at the
+    last row: 1/n, 1/n, max(k_f, 1)/n, |{0} u F u (n - w_l, n - 1]|/n, and 1."""
+    d = 8
+    Qg = np.zeros((1, n, d))
+    K = np.random.default_rng(n).standard_normal((n, d))
+    cls = np.zeros(n, dtype=np.uint8)
+    cls[0] = ref.TOKEN_SPECIAL
+    F = np.zeros(n, dtype=bool)
+    F[:k_f] = True
+    bins = ref.row_bins(Qg, K, cls, F, w_l)
+    got = ref.row_min_share(bins)
+    # the kept count of the last row under entry 3: the union of {0}, F and the window (n - w_l, n - 1]
+    kept3 = len({0} | set(range(k_f)) | set(range(max(0, n - w_l), n)))
+    want = np.array([1.0 / n, 1.0 / n, max(k_f, 1) / n, kept3 / n, 1.0])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
