@@ -90,7 +90,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
   const bool fits = row_offset[hd + 1] <= total_rows && w1 <= n_work && w1 - w0 <= S;
   const int n_items = fits ? (int)(w1 - w0) : 0;
   const int cap = capacity[hd];
-  const int L = len[hd];
+  const int L = len[hd];                           // rows in use before this step (see the deferred store)
   const float qv = to_f32(q[(size_t)qh * D + dd]);
   const float kv_self = to_f32(k_new[(size_t)hd * D + dd]);   // thread dd holds k_new[dd], v_new[dd]
   const float vv_self = to_f32(v_new[(size_t)hd * D + dd]);
@@ -103,6 +103,10 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     av[k] = pp[2 + dd];
   }
 
+  // The new row count and the work item's rows-in-use count are stored only after the merge's barrier
+  // below: every thread reads len[hd] above and uses it (dst) before that barrier, so no thread can
+  // see the incremented count (a store in the update itself could reach a late wave's load).
+  bool bump = false, overflow = false;
   if (g == 0 && fits) {                           // one cache update per KV head, before the merge
     // ---- cache update: afterwards the cache holds {j <= p : level(p + 1, j) <= policy}
     const bool to_ring = (cls == kNormal) && pol == 3 && w_l >= 2 && R > 0;
@@ -174,15 +178,8 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
     if (tid == 0) {
       if (pol == 3 && R > 0 && !to_ring) pos[base_h + slot] = -1;   // key p + 1 - w_l leaves the window
       if (dst >= 0) pos[dst] = p;
-      if (to_perm) {
-        if (dst >= 0) {
-          len[hd] = L + 1;
-          const int64_t wi = w0 + L / CH;                           // the item that holds row L
-          work[4 * wi + 3] = L % CH + 1;
-        } else {
-          atomicOr(error_word, 1u);
-        }
-      }
+      bump = to_perm && dst >= 0;
+      overflow = to_perm && dst < 0;
     }
   }
   // ---- the new token's score: lane sums, then the D / 64 waves of one item group in LDS
@@ -219,6 +216,12 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(
   const int lvl_self = cls == kSpecial ? 0 : (cls == kPunct ? 1 : (w_l >= 1 ? 3 : 4));
   const bool att_self = lvl_self <= pol;
   __syncthreads();
+  if (bump) {                                      // thread 0 of the updating workgroup (see above)
+    len[hd] = L + 1;
+    const int64_t wi = w0 + L / CH;                // the item that holds row L
+    work[4 * wi + 3] = L % CH + 1;
+  }
+  if (overflow) atomicOr(error_word, 1u);
   if (grp == 0) {
     float s_self = 0.f;
 #pragma unroll

@@ -882,13 +882,21 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
     ref_out = outs.clone()
     ref_state = [(c.t["pos"].clone(), c.t["len"].clone()) for c in caches]
     ref_prof = [(p.policy.clone(), p.recovery.clone(), p.cum.clone()) for p in (profs_graph if pgraph else profs)]
+    # the check starts from caches whose rows are all NaN before the refill, so a row the refill or
+    # a decode step should write and does not shows up in the outputs (the timed run's stale rows
+    # hold the same stream's earlier values and would hide it)
+    for c in caches:
+        c.t["k"].fill_(float("nan"))
+        c.t["v"].fill_(float("nan"))
     prompt_phase(check=True)
     for t_a in range(0, steps_dec, 256):
         decode_tokens(t_a, min(steps_dec, t_a + 256))
         torch.cuda.synchronize()
         say(f"eager check: {min(steps_dec, t_a + 256)} of {steps_dec} tokens")
     if not torch.equal(ref_out, outs):
-        raise RuntimeError("timed decode and eager decode disagree")
+        bad = [l for l in range(L) if not torch.equal(ref_out[l], outs[l])]
+        raise RuntimeError(f"timed decode and eager decode disagree in layers {bad[:16]} ({len(bad)} of {L}); "
+                           f"max |diff| {float((ref_out - outs).abs().max()):.3e}")
     for l in range(L):
         if not (torch.equal(ref_state[l][0], caches[l].t["pos"]) and torch.equal(ref_state[l][1], caches[l].t["len"])):
             raise RuntimeError(f"layer {l}: caches after the timed and the eager decode disagree")
