@@ -103,13 +103,22 @@ CALIB_BLOCKS = 1000          # the calibration copy's grid (1000 x 256 threads),
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_sources_digest() -> str:
-    """Digest of the HIP sources; counter-derived traffic is reported only for the same sources."""
+KERNEL_SOURCES = {
+    "profile_rowstats": "profile_kernels.hip", "profile_colsums": "profile_kernels.hip",
+    "profile_select": "select_kernels.hip", "compact_gather": "compact_kernels.hip",
+    "decode_partials": "decode_kernels.hip", "decode_merge": "decode_kernels.hip",
+}
+
+
+def kernel_sources_digest(kernel=None) -> str:
+    """Digest of the HIP sources a kernel is built from (its own file and the shared headers; every
+    source when ``kernel`` is None): counter-derived traffic is reported only for the same sources."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "adaptive_kv_cache_fg_amd", "csrc")
+    own = KERNEL_SOURCES.get(kernel)
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
+        if name.endswith(".h") or (name.endswith(".hip") and (own is None or name == own)):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + f.read())
     return h.hexdigest()
@@ -118,17 +127,18 @@ def kernel_sources_digest() -> str:
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of ``kernel`` in ``workload`` from profiles/traffic.json (FETCH_SIZE +
     WRITE_SIZE, scaled by the calibration copy), or None when absent, taken on another workload,
-    or taken on other kernel sources."""
+    or taken on other sources of that kernel."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     entry = t.get("workloads", {}).get(workload)
-    if not entry or entry.get("sources_digest") != kernel_sources_digest():
+    if not entry or kernel not in entry.get("bytes_per_launch", {}):
         return None
-    v = entry.get("bytes_per_launch", {}).get(kernel)
-    return float(v) if v is not None else None
+    if entry.get("sources_digest", {}).get(kernel) != kernel_sources_digest(kernel):
+        return None
+    return float(entry["bytes_per_launch"][kernel])
 
 
 def calibration_copy(torch, fg) -> None:
@@ -1236,8 +1246,8 @@ def record_traffic(fetch_dir: str, write_dir: str, key: str, command: str) -> st
     except (OSError, ValueError):
         t = {}
     t = {"workloads": t.get("workloads", {})}
-    t["workloads"][key] = {"sources_digest": kernel_sources_digest(), "fetch_factor": f_factor,
-                           "write_factor": w_factor, "bytes_per_launch": per_launch}
+    t["workloads"][key] = {"sources_digest": {k: kernel_sources_digest(k) for k in per_launch},
+                           "fetch_factor": f_factor, "write_factor": w_factor, "bytes_per_launch": per_launch}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(t, f, indent=1)
     return "\n".join(lines) + "\n"
