@@ -78,12 +78,19 @@ def cpu_baseline(spec: syn.ConfigSpec, sample_heads: int, layer: int = 0) -> dic
     cores = min(16, len(os.sched_getaffinity(0)))
     heads = list(range(min(sample_heads, spec.n_kv_heads)))
     ctx = mp.get_context("fork")
+    def progress(it, what):
+        out = []
+        for k, r in enumerate(it):
+            out.append(r)
+            print(f"[cpu] {what}: {k + 1} of {len(heads)} KV heads", file=sys.stderr, flush=True)
+        return out
+
     with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
         t0 = time.perf_counter()
-        res = list(ex.map(_oracle_head, [(spec.cfg_id, layer, h, False) for h in heads]))
+        res = progress(ex.map(_oracle_head, [(spec.cfg_id, layer, h, False) for h in heads]), "profile+compact")
         w_prompt = time.perf_counter() - t0
         t0 = time.perf_counter()
-        res_d = list(ex.map(_oracle_head, [(spec.cfg_id, layer, h, True) for h in heads]))
+        res_d = progress(ex.map(_oracle_head, [(spec.cfg_id, layer, h, True) for h in heads]), "with decode")
         w_both = time.perf_counter() - t0
     scale = spec.batch * spec.n_kv_heads / len(heads)
     prompt_tok_s = spec.batch * spec.seq_len / (w_prompt * scale)
@@ -696,7 +703,11 @@ def cpu_baseline_stack(spec: syn.ConfigSpec, layers_layers: int) -> dict:
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
-        res = list(ex.map(_oracle_stack_head, jobs))
+        res = []
+        for k, r in enumerate(ex.map(_oracle_stack_head, jobs)):
+            res.append(r)
+            if k % 16 == 15:
+                print(f"[cpu] {k + 1} of {len(jobs)} sampled heads", file=sys.stderr, flush=True)
     wall = time.perf_counter() - t0
     prof_s = {outer: 0.0, middle: 0.0}
     dec_s = {outer: 0.0, middle: 0.0}
@@ -1270,8 +1281,13 @@ def main() -> int:
                     help="recovery route of the prompt phase: column sums (fg_profile) or per-row level bins "
                          "(fg_profile_rows)")
     ap.add_argument("--no-row-route", action="store_true", help="skip timing the per-row route beside the default")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the Llama-1-7B-shaped stack at its three T after the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=16)
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="time only the CPU oracle (every KV head of a one-layer workload; the sampled layers "
+                         "of a stack) and exit")
     ap.add_argument("--no-peaks", action="store_true", help="skip the chip-ceiling micro-benchmarks")
     ap.add_argument("--no-full-baseline", action="store_true",
                     help="one layer: skip the full-cache decode baseline (every head keeps every key)")
@@ -1313,6 +1329,12 @@ def main() -> int:
         if not 0 <= args.layer < spec.layers:
             print(json.dumps({"error": f"--layer must be in [0, {spec.layers})"}))
             return 2
+    if args.cpu_only:
+        # the oracle alone: every KV head of a one-layer workload, or the stack's sampled layers
+        cpu = (cpu_baseline_stack(spec, spec.layers) if spec.layers > 1 else
+               cpu_baseline(spec, spec.n_kv_heads, 0))
+        print(json.dumps({"config": spec.name, "cpu_baseline": cpu}))
+        return 0
     cpu = None
     if not args.no_cpu_baseline:                              # before any GPU call (fork pool)
         if stack:
@@ -1320,8 +1342,43 @@ def main() -> int:
         else:
             cpu = cpu_baseline(spec, args.cpu_sample_heads, args.layer)
     result = bench_stack(args, spec, cpu) if stack else bench_layer(args, spec, cpu)
+    if stack and args.config == 3 and args.stack_layers is None and not args.no_secondary:
+        result["secondary"] = secondary_llama7b_stack(args)
     print(json.dumps(result))
     return 0
+
+
+def secondary_llama7b_stack(args) -> dict:
+    """The Llama-1-7B-shaped stack (32 layers x 32 heads, B=8, n=4096, 512 decode steps) at each of
+    its three T, outside the headline's timing: 2 timed steps after 1 warm-up each."""
+    import copy
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+    spec = syn.CONFIGS[2]
+    out = {}
+    for T in spec.T:
+        a = copy.copy(args)
+        a.steps, a.warmup, a.T = 2, 1, T
+        a.no_peaks = True
+        a.no_row_route = True
+        r = bench_stack(a, spec, None)
+        out[f"T={T}"] = {
+            "prompt_tok_s": r["value"], "decode_tok_s": r["decode_tok_s"], "prompt_ms": r["prompt_ms"],
+            "decode_ms": r["decode_ms"], "prompt_mfma_frac": r["phases"]["prompt_mfma_frac"],
+            "decode_hbm_frac": r["phases"]["decode_hbm_frac"],
+            "decode_partials_hbm_frac": r["kernels"]["decode_partials"]["frac"],
+            "policy_histogram": r["compression"]["policy_histogram"],
+            "kv_pruned_fraction": r["compression"]["kv_pruned_fraction"],
+            "prompt_keys_kept_fraction": r["compression"]["prompt_keys_kept_fraction"],
+        }
+        gc.collect()
+        torch.cuda.empty_cache()
+    return {"workload": f"{spec.name}: {spec.layers} layers x {spec.n_q_heads} heads, d={spec.head_dim}, "
+                        f"{spec.dtype}, B={spec.batch}, n={spec.seq_len}, r_l={spec.r_l}, r_f={spec.r_f}, "
+                        f"{spec.decode_steps} decode steps through every layer",
+            "per_T": out, "note": "the same measurement as the headline, 2 timed steps after 1 warm-up per T"}
 
 
 if __name__ == "__main__":
