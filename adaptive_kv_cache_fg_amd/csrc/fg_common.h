@@ -69,6 +69,16 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// m + log2(l) for a running (reference, sum) pair whose sum may be far from 1 (l > 0): the
+// logarithm is taken of l's mantissa only (in [0.5, 1), where log2 is accurate to a few units
+// of 2^-24 absolute) and the exponent and reference are added in double, so the result is
+// rounded to fp32 once.
+__device__ __forceinline__ float log2_of_scaled(float m, float l) {
+  int e;
+  const float mant = frexpf(l, &e);
+  return (float)((double)m + (double)e + (double)fast_log2(mant));
+}
+
 template <typename T>
 __device__ __forceinline__ T zero_val() { return T(0.0f); }
 

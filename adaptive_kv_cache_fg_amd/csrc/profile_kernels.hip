@@ -106,15 +106,27 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
     }
   };
   auto needs_mask = [&](int key0) { return key0 + 31 > q0 || key0 + 32 > kend; };   // wave-uniform
+  // Deferred row maximum: a unit's exponents are taken against the row's reference m[cb], which is
+  // raised (and the running sum rescaled) only when some value of the unit lies more than 2^64 above
+  // it -- at the row's first unit (m = -big) and rarely after -- so most units need no max tree and
+  // no rescale.  (m, l) then stands for l * 2^m with l < 2^75 (at most 2048 terms of at most 2^64
+  // each between raises), which every consumer of (max, sum) pairs handles unchanged.
   auto softmax_update = [&](f32x16 (&acc)[2]) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const float m_new = fmaxf(m[cb], tree_max16(acc[cb]) * c);
       float e[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(acc[cb][r], c, -m_new));
-      l[cb] = fmaf(l[cb], fast_exp2(m[cb] - m_new), tree_sum16(e));
-      m[cb] = m_new;
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(acc[cb][r], c, -m[cb]));
+      float ts = tree_sum16(e);
+      if (__any(!(ts <= 0x1p64f))) {                         // wave-uniform: raise the reference
+        const float m_new = fmaxf(m[cb], tree_max16(acc[cb]) * c);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(acc[cb][r], c, -m_new));
+        ts = tree_sum16(e);
+        l[cb] *= fast_exp2(m[cb] - m_new);
+        m[cb] = m_new;
+      }
+      l[cb] += ts;
     }
   };
   auto softmax_unit = [&](int key0, f32x16 (&acc)[2]) {
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
       if (rs_part) {                                       // one key chunk: keep (max, sum) for the merge
         rs_part[((size_t)ch * nbh + bh) * n + qrow] = make_float2(M2, L);
       } else {
-        const float v = M2 + fast_log2(L);
+        const float v = log2_of_scaled(M2, L);
         lse2[(size_t)bh * n + qrow] = v;
         if (lse_out) lse_out[(size_t)bh * n + qrow] = v * kLn2;
       }
@@ -277,7 +289,7 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
         for (int k = 0; k < kPre; ++k)
           if (k < pre_nc) merge(pre[k]);
         for (int k = kPre; k < pre_nc; ++k) merge(rs_part[((size_t)k * nbq + pre_qh) * n + pre_row]);
-        lpre = pre_row < i_end ? Mx + fast_log2(Ls) : INFINITY;
+        lpre = pre_row < i_end ? log2_of_scaled(Mx, Ls) : INFINITY;
         if (kb == 0 && pre_row < i_end) {                        // every row once: the merged statistics
           lse2[pre_qh * n + pre_row] = lpre;                     // (nothing reads lse2 in a split sweep)
           if (lse_out) lse_out[pre_qh * n + pre_row] = lpre * kLn2;
