@@ -762,6 +762,17 @@ fg_status fg_peak_copy(const void* src, void* dst, size_t bytes, int32_t nontemp
   return FG_OK;
 }
 
+fg_status fg_peak_read(const void* src, size_t bytes, int32_t nontemporal, int32_t blocks, uint32_t* out,
+                       hipStream_t stream) {
+  if (!src || !out) return fail(FG_ERR_INVALID_ARG, "src and out must not be NULL");
+  if (!aligned16(src)) return fail(FG_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0) return fail(FG_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (blocks < 1) return fail(FG_ERR_INVALID_ARG, "blocks must be >= 1");
+  const hipError_t e = fg::launch_peak_read(src, bytes, nontemporal != 0, blocks, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "peak read");
+  return FG_OK;
+}
+
 fg_status fg_cache_error(const fg_cache* cache, uint32_t* bits_out, hipStream_t stream) {
   if (!cache || !cache->error_word) return fail(FG_ERR_INVALID_ARG, "cache or error_word is NULL");
   hipError_t e = hipStreamSynchronize(stream);

@@ -80,6 +80,32 @@ __global__ __launch_bounds__(256) void peak_copy_kernel(const uint4* __restrict_
   }
 }
 
+// A read-only stream: 8 independent 16-byte loads per thread in flight over a grid-stride loop
+// (plain or non-temporal), each thread's words folded into one word stored at the end so the
+// loads are kept.
+constexpr int kReadUnroll = 8;
+template <bool NT>
+__global__ __launch_bounds__(256) void peak_read_kernel(const uint4* __restrict__ src, size_t n16,
+                                                        unsigned* __restrict__ out) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  unsigned acc = 0u;
+  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {   // every load in bounds
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = NT ? __builtin_nontemporal_load(s + i + u * stride) : s[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = s[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 hipError_t launch_peak_mfma(const void* operands, float* out, int iters, int blocks, hipStream_t st) {
   peak_mfma_kernel<<<dim3(blocks), dim3(256), 0, st>>>(static_cast<const bf16x8*>(operands), out, iters);
   return hipGetLastError();
@@ -98,6 +124,16 @@ hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, bool nonte
   else
     peak_copy_kernel<false><<<dim3(blocks), dim3(256), 0, st>>>(static_cast<const uint4*>(src),
                                                                  static_cast<uint4*>(dst), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_peak_read(const void* src, size_t bytes, bool nontemporal, int blocks, unsigned* out,
+                            hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  if (nontemporal)
+    peak_read_kernel<true><<<dim3(blocks), dim3(256), 0, st>>>(static_cast<const uint4*>(src), n16, out);
+  else
+    peak_read_kernel<false><<<dim3(blocks), dim3(256), 0, st>>>(static_cast<const uint4*>(src), n16, out);
   return hipGetLastError();
 }
 

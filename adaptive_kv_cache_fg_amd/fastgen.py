@@ -108,6 +108,7 @@ def lib() -> ctypes.CDLL:
     L.fg_peak_mfma_bf16.argtypes, L.fg_peak_mfma_bf16.restype = [P, P, I32, I32, P], ctypes.c_int
     L.fg_peak_exp.argtypes, L.fg_peak_exp.restype = [P, I32, I32, P], ctypes.c_int
     L.fg_peak_copy.argtypes, L.fg_peak_copy.restype = [P, P, S, I32, I32, P], ctypes.c_int
+    L.fg_peak_read.argtypes, L.fg_peak_read.restype = [P, S, I32, I32, P, P], ctypes.c_int
     _ = D, I64
     _lib = L
     return L
@@ -630,3 +631,15 @@ def peak_copy(src: torch.Tensor, dst: torch.Tensor, nontemporal: bool, blocks: i
     _check(lib().fg_peak_copy(_ptr(src), _ptr(dst), nbytes, 1 if nontemporal else 0, int(blocks), _stream()),
            "fg_peak_copy")
     return 2 * nbytes
+
+
+def peak_read(src: torch.Tensor, out: torch.Tensor, nontemporal: bool, blocks: int) -> int:
+    """fg_peak_read of src's bytes (out: int32, at least blocks * 256 elements); returns the bytes read."""
+    _need(src, "src")
+    _need(out, "out", torch.int32)
+    if out.numel() < blocks * 256:
+        raise ValueError("out must hold blocks * 256 words")
+    nbytes = src.numel() * src.element_size()
+    _check(lib().fg_peak_read(_ptr(src), nbytes, 1 if nontemporal else 0, int(blocks), _ptr(out), _stream()),
+           "fg_peak_read")
+    return nbytes

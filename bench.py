@@ -732,8 +732,9 @@ def cpu_baseline_stack(spec: syn.ConfigSpec, layers_layers: int) -> dict:
 
 # ---------------------------------------------------------------- the chip's own ceilings
 def chip_peaks(torch, fg) -> dict:
-    """Micro-benchmarks (libfastgen's fg_peak_*): bf16 MFMA issue rate, v_exp_f32 rate and a
-    1 GiB HBM copy, each the best over a few occupancies, events around repeated launches."""
+    """Micro-benchmarks (libfastgen's fg_peak_*): bf16 MFMA issue rate, v_exp_f32 rate, a 1 GiB
+    HBM copy and a 4 GiB read-only stream, each the best over a few occupancies, events around
+    repeated launches."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def timed(fn, reps=5):
@@ -776,6 +777,16 @@ def chip_peaks(torch, fg) -> dict:
             t = timed(lambda: fg.peak_copy(src, dst, nt, blocks), reps=10)
             copies.append({"nontemporal": nt, "blocks_per_cu": per_cu, "gbs": 2 * nbytes / t / 1e9})
     del src, dst
+    rbytes = 4 << 30
+    rsrc = torch.empty(rbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    reads = []
+    for nt in (False, True):
+        for per_cu in (16, 32, 64):
+            blocks = per_cu * cus
+            words = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+            t = timed(lambda: fg.peak_read(rsrc, words, nt, blocks), reps=10)
+            reads.append({"nontemporal": nt, "blocks_per_cu": per_cu, "gbs": rbytes / t / 1e9})
+    del rsrc
     best = lambda xs, k: max(x[k] for x in xs)   # noqa: E731
     clock_ghz = 2.4
     return {
@@ -787,6 +798,8 @@ def chip_peaks(torch, fg) -> dict:
                                       f"half rate (8 lanes/clk/SIMD) x 4 SIMD x {cus} CU x {clock_ghz} GHz"},
         "hbm_copy": {"measured_gbs": best(copies, "gbs"), "vendor_gbs": HBM_PEAK_GBS, "bytes": 2 * nbytes,
                      "runs": copies, "note": "1 GiB read + 1 GiB written, 16-byte loads and stores"},
+        "hbm_read": {"measured_gbs": best(reads, "gbs"), "vendor_gbs": HBM_PEAK_GBS, "bytes": rbytes,
+                     "runs": reads, "note": "4 GiB read only, 16-byte loads, 8 in flight per thread"},
         "compute_units": cus,
     }
 
@@ -1110,15 +1123,23 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
     if not args.no_peaks:
         pk = chip_peaks(torch, fg)
         mf, ex, cp = pk["mfma_bf16"]["measured_tflops"], pk["exp"]["measured_t_per_s"], pk["hbm_copy"]["measured_gbs"]
+        rd = pk["hbm_read"]["measured_gbs"]
         for k in ("profile_rowstats", "profile_colsums"):
             if k in kstats:
                 kstats[k]["frac_of_measured_mfma"] = kstats[k]["achieved"] / mf
                 kstats[k]["exp_frac_of_measured"] = kstats[k]["exp_rate_t_per_s"] / ex
         for k in ("compact_gather", "decode_partials", "decode_step"):
             kstats[k]["frac_of_measured_copy"] = kstats[k]["achieved"] / cp
+        for k in ("decode_partials", "decode_step"):                 # read streams: the read ceiling
+            kstats[k]["frac_of_measured_read"] = kstats[k]["achieved"] / rd
         phases["prompt_frac_of_measured_mfma"] = phases["prompt_mfma_frac"] * peak_mfma / mf
         phases["decode_frac_of_measured_copy"] = phases["decode_hbm_frac"] * HBM_PEAK_GBS / cp
-        roofline["frac_of_measured"] = dk["achieved"] / (cp if dk["bound"] == "hbm" else mf)
+        phases["decode_frac_of_measured_read"] = phases["decode_hbm_frac"] * HBM_PEAK_GBS / rd
+        ceiling = mf if dk["bound"] != "hbm" else (rd if dominant.startswith("decode") else cp)
+        roofline["frac_of_measured"] = dk["achieved"] / ceiling
+        roofline["measured_ceiling"] = {"value": ceiling, "unit": dk["unit"],
+                                        "kind": "mfma" if dk["bound"] != "hbm" else
+                                        ("hbm_read" if dominant.startswith("decode") else "hbm_copy")}
 
     calibration_copy(torch, fg)
 

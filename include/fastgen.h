@@ -421,6 +421,11 @@ fg_status fg_decode_track(const fg_cache* cache, const void* q, const uint8_t* t
  *   not overlapping) from src to dst with 16-byte loads and stores over a
  *   grid-stride loop of `blocks` x 256 threads; nontemporal != 0 stores
  *   non-temporally (as the compaction's gather does).
+ * fg_peak_read: read `bytes` (a positive multiple of 16, src 16-byte aligned)
+ *   with 16-byte loads, 8 in flight per thread, over a grid-stride loop of
+ *   `blocks` x 256 threads; nontemporal != 0 loads non-temporally (as the
+ *   decode's split-K launch does).  out [blocks * 256] u32 receives each
+ *   thread's XOR of the words it read (kept so the loads are not removed).
  * Errors: FG_ERR_INVALID_ARG for NULL or misaligned pointers, iters < 1,
  * blocks < 1, a byte count that is not a positive multiple of 16, or
  * overlapping copy buffers; FG_ERR_HIP for a failed launch.
@@ -428,6 +433,8 @@ fg_status fg_decode_track(const fg_cache* cache, const void* q, const uint8_t* t
 fg_status fg_peak_mfma_bf16(const void* operands, float* out, int32_t iters, int32_t blocks, hipStream_t stream);
 fg_status fg_peak_exp(float* out, int32_t iters, int32_t blocks, hipStream_t stream);
 fg_status fg_peak_copy(const void* src, void* dst, size_t bytes, int32_t nontemporal, int32_t blocks,
+                       hipStream_t stream);
+fg_status fg_peak_read(const void* src, size_t bytes, int32_t nontemporal, int32_t blocks, uint32_t* out,
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------ diagnostics */

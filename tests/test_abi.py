@@ -230,3 +230,8 @@ def test_peak_benchmarks_reject_bad_arguments():
     assert L.fg_peak_copy(p, ctypes.c_void_p(0x100000), 24, 0, 8, None) == 1        # not a multiple of 16
     assert L.fg_peak_copy(p, ctypes.c_void_p(0x1100), 4096, 0, 8, None) == 1        # overlapping
     assert L.fg_peak_copy(p, ctypes.c_void_p(0x100000), 0, 0, 8, None) == 1
+    assert L.fg_peak_read(None, 4096, 0, 8, p, None) == 1
+    assert L.fg_peak_read(p, 4096, 0, 8, None, None) == 1
+    assert L.fg_peak_read(ctypes.c_void_p(0x1008), 4096, 0, 8, p, None) == 1       # misaligned
+    assert L.fg_peak_read(p, 24, 0, 8, p, None) == 1                               # not a multiple of 16
+    assert L.fg_peak_read(p, 4096, 1, 0, p, None) == 1
