@@ -51,8 +51,9 @@ template <> struct Vec16<float> {
 // Every load is issued before its first use: the per-head scalars, the new
 // token's q . k_new and K/V row, and the partial slots in batches of kBatch
 // items per thread (masked by the head's item count afterwards, so they do not
-// wait for it).  NT threads: 512 when one batch covers a head's items (a
-// smaller workgroup starts and drains sooner), else 1024.
+// wait for it).  NT threads: 256 when at most two batches cover a head's items
+// (a smaller workgroup starts and drains sooner: 256 measured about 1 us per step
+// faster than 512 at the Llama-1-65B shape), else 1024.
 constexpr int kMergeBatch = 8;                     // items per thread whose loads are in flight together
 
 // HAS_CLASS = false: new_class is NULL and every generated token is normal.
@@ -407,10 +408,10 @@ static hipError_t launch_decode_tg(const DecodeArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && !a.partials_only) {
     timed_begin(FG_K_DECODE_MERGE, st);
-    const bool small = a.items_per_head <= (512 / D) * kMergeBatch;
-    auto kern = a.new_class ? (small ? decode_merge_kernel<T, D, G, true, 512> : decode_merge_kernel<T, D, G, true, 1024>)
-                            : (small ? decode_merge_kernel<T, D, G, false, 512> : decode_merge_kernel<T, D, G, false, 1024>);
-    kern<<<dim3(H * G), dim3(small ? 512 : 1024), 0, st>>>(
+    const bool small = a.items_per_head <= 2 * (256 / D) * kMergeBatch;
+    auto kern = a.new_class ? (small ? decode_merge_kernel<T, D, G, true, 256> : decode_merge_kernel<T, D, G, true, 1024>)
+                            : (small ? decode_merge_kernel<T, D, G, false, 256> : decode_merge_kernel<T, D, G, false, 1024>);
+    kern<<<dim3(H * G), dim3(small ? 256 : 1024), 0, st>>>(
         (const T*)a.q, (const T*)a.k_new, (const T*)a.v_new, a.new_class, a.out, a.part, a.work_offset, a.work,
         (T*)a.Kc, (T*)a.Vc, a.pos, a.row_offset, a.len, a.capacity, a.ring, a.policy, a.error_word, a.score,
         a.cls_all, a.n_total, a.Hkv, a.w_l, a.p, a.items_per_head, a.chunk_rows, a.total_rows, a.n_work, c);
