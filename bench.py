@@ -17,8 +17,9 @@ Python); before timing, one replayed step is checked bit for bit against an
 eager run.
 
 Prints ONE JSON line.  ``value`` is profile+compact prompt tokens/s over the
-whole stack (B * n / prompt-phase time); decode tokens/s (B * steps / decode
-time), per-kernel figures, the roofline of the dominant kernel, whole-phase
+whole stack (B * n / prompt-phase time, the median over the timed steps; by
+default 5 steps after 2 warm-ups); decode tokens/s (B * steps / decode time,
+likewise), per-kernel figures, the roofline of the dominant kernel, whole-phase
 fractions of the MFMA and HBM ceilings, the chip's measured ceilings and the
 CPU oracle (sampled heads, extrapolated) are reported beside it.
 ``--config 1`` (or ``--layer L`` of a stack) times one attention layer instead,
@@ -475,8 +476,8 @@ def bench_layer(args, spec: syn.ConfigSpec, cpu) -> dict:
         fg.timing_enable(False)
         recs += fg.timing_read()
 
-    prompt_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][1]) for s in range(args.steps)]))
-    decode_ms = float(np.mean([evs[s][1].elapsed_time(evs[s][2]) for s in range(args.steps)]))
+    prompt_ms = float(np.median([evs[s][0].elapsed_time(evs[s][1]) for s in range(args.steps)]))
+    decode_ms = float(np.median([evs[s][1].elapsed_time(evs[s][2]) for s in range(args.steps)]))
     ms_per_step = wall * 1e3 / args.steps
     prompt_tok_s = B * n / (prompt_ms * 1e-3)
     decode_tok_s = B * steps_dec / (decode_ms * 1e-3)
@@ -948,8 +949,8 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
         one_step(evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    prompt_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs]))
-    decode_ms = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in evs]))
+    prompt_ms = float(np.median([ev[0].elapsed_time(ev[1]) for ev in evs]))   # median over the timed steps
+    decode_ms = float(np.median([ev[1].elapsed_time(ev[2]) for ev in evs]))
     ms_per_step = wall * 1e3 / args.steps
     prompt_tok_s = B * n / (prompt_ms * 1e-3)
     decode_tok_s = B * steps_dec / (decode_ms * 1e-3)
@@ -1288,8 +1289,8 @@ def record_traffic(fetch_dir: str, write_dir: str, key: str, command: str) -> st
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3,
                     help="workload id (3 = the Llama-1-65B-shaped stack, the default; 1 = one Llama-1-7B layer)")
     ap.add_argument("--layer", type=int, default=None,
