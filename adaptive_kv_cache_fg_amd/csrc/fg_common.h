@@ -41,8 +41,10 @@ template <> struct Mfma<float> {
   }
 };
 
-// Row (within the 32x32 tile) held by accumulator r of this lane.
-__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+// Row (within the 32x32 tile) held by accumulator r of this lane, and its lane-independent part
+// (acc_row(r, lane) = acc_row0(r) + 4 * (lane >> 5)).
+__device__ __forceinline__ constexpr int acc_row0(int r) { return 8 * (r >> 2) + (r & 3); }
+__device__ __forceinline__ int acc_row(int r, int lane) { return acc_row0(r) + 4 * (lane >> 5); }
 
 // Index of this thread's wave in the workgroup, as a scalar (wave-uniform) value so
 // that branches on it stay scalar branches instead of exec-masked regions.

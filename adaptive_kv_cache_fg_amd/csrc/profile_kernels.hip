@@ -131,14 +131,15 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, 
   };
   auto softmax_unit = [&](int key0, f32x16 (&acc)[2]) {
     if (needs_mask(key0)) {                                  // diagonal or ragged unit: mask
+      // accumulator r holds key key0 + acc_row0(r) + 4 * (lane >> 5); it is masked when past the query
+      // row or past the chunk: one per-lane threshold against compile-time key offsets
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         const int qrow = q0 + 32 * cb + (lane & 31);
+        const int th = min(qrow, kend - 1) - key0 - 4 * (lane >> 5);   // key offset > th: masked
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + acc_row(r, lane);
-          if (key > qrow || key >= kend) acc[cb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (acc_row0(r) > th) acc[cb][r] = -INFINITY;
       }
     }
     softmax_update(acc);
@@ -335,20 +336,25 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
           float p[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(acc[kc][r], c, -lrow[r]));
+          // accumulator r holds row r0 + acc_row(r, lane) = r0 + acc_row0(r) + 4 * (lane >> 5), so each
+          // mask below is one per-lane threshold against compile-time row offsets
+          const int lane_row = 4 * (lane >> 5);
           if (r0 < jc + 31) {                                   // diagonal: rows above the key get 0
+            const int th = key - r0 - lane_row;                 // row offset < th: above the key
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (r0 + acc_row(r, lane) < key) p[r] = 0.f;
+              if (acc_row0(r) < th) p[r] = 0.f;
           }
           const float ts = tree_sum16(p);
           cum_g[kc] += ts;
           if ((r0 + 31) - jc < w_l) {
             band_g[kc] += ts;                                   // every pair of the slice is in the band
           } else if (r0 - (jc + 31) < w_l) {
+            const int th = key + w_l - r0 - lane_row;           // row offset < th: inside the band
             float tb = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (r0 + acc_row(r, lane) - key < w_l) tb += p[r];
+              if (acc_row0(r) < th) tb += p[r];
             band_g[kc] += tb;
           }
         }
