@@ -34,7 +34,8 @@ namespace fg {
 
 constexpr int kRowsPerWave = 64;  // sweep 1: query rows per wave (two MFMA column blocks)
 constexpr int kRowsPerWG = kSweepRowsPerWG;   // sweep 1: 4 waves x 64 query rows
-constexpr int kKeyTile = 128;     // sweep 1: keys staged per LDS tile (4 units of 32 keys)
+constexpr int kKeyTile = 64;      // sweep 1: keys staged per LDS tile (2 units of 32 keys; 35 KB of LDS for
+                                  // both buffers at bf16, d = 128, so three workgroups fit a CU)
 constexpr int kKeysPerWave = 64;  // sweep 2: keys per wave (two MFMA column blocks)
 constexpr int kKeysPerWG = kSweepKeysPerWG;   // sweep 2: 4 waves x 64 keys
 constexpr int kRowTile = 128;     // sweep 2: query rows staged per LDS tile (4 halves of 32 rows)
@@ -43,8 +44,11 @@ constexpr int kRowTile = 128;     // sweep 2: query rows staged per LDS tile (4 
 // A wave owns 64 query rows as two 32-column MFMA blocks (cb = 0, 1) whose B
 // operands stay in registers; every A operand (32 keys x KS dims) read from the
 // staged K tile feeds both blocks, halving LDS traffic per MFMA.
+// Three waves per SIMD (at most 168 VGPRs; the few values that do not fit are the tile loader's row
+// indices, reloaded only on a ragged last tile): a third wave per SIMD overlaps the matrix cores and
+// the softmax VALU of the others better than two (6 % faster at the Llama-1-65B shape).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void rowstats_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                        float* __restrict__ lse2, float* __restrict__ lse_out,
                                                        float2* __restrict__ rs_part, int Hq, int Hkv, int n,
                                                        int n_rb, int kchunk, float c) {
