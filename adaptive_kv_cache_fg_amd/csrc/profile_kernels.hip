@@ -38,17 +38,23 @@ constexpr int kKeyTile = 64;      // sweep 1: keys staged per LDS tile (2 units 
                                   // both buffers at bf16, d = 128, so three workgroups fit a CU)
 constexpr int kKeysPerWave = 64;  // sweep 2: keys per wave (two MFMA column blocks)
 constexpr int kKeysPerWG = kSweepKeysPerWG;   // sweep 2: 4 waves x 64 keys
-constexpr int kRowTile = 128;     // sweep 2: query rows staged per LDS tile (4 halves of 32 rows)
+constexpr int kRowTile = 64;      // sweep 2: query rows staged per LDS tile (2 slices of 32 rows; 35 KB of LDS
+                                  // for both buffers at bf16, d = 128, so three workgroups fit a CU)
+
+// Waves per SIMD the sweeps are compiled for: three for bf16 (at most 168 VGPRs), where a third wave
+// overlaps the matrix cores and the softmax VALU of the others better than two; no bound otherwise
+// (fp32 operands take twice the registers, and three waves would spill).
+template <typename T> constexpr int kSweepMinWaves = 1;
+template <> constexpr int kSweepMinWaves<__bf16> = 3;
 
 // ---------------------------------------------------------------- sweep 1: row statistics
 // A wave owns 64 query rows as two 32-column MFMA blocks (cb = 0, 1) whose B
 // operands stay in registers; every A operand (32 keys x KS dims) read from the
 // staged K tile feeds both blocks, halving LDS traffic per MFMA.
-// Three waves per SIMD (at most 168 VGPRs; the few values that do not fit are the tile loader's row
-// indices, reloaded only on a ragged last tile): a third wave per SIMD overlaps the matrix cores and
-// the softmax VALU of the others better than two (6 % faster at the Llama-1-65B shape).
+// Three waves per SIMD at bf16 (the few values that do not fit 168 VGPRs are the tile loader's row
+// indices, reloaded only on a ragged last tile): 6 % faster than two at the Llama-1-65B shape.
 template <typename T, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void rowstats_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSweepMinWaves<T>))) void rowstats_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                        float* __restrict__ lse2, float* __restrict__ lse_out,
                                                        float2* __restrict__ rs_part, int Hq, int Hkv, int n,
                                                        int n_rb, int kchunk, float c) {
@@ -195,8 +201,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // A wave owns 64 keys as two 32-column MFMA blocks (kc = 0, 1) held in
 // registers; every A operand (32 query rows x KS dims) read from the staged Q
 // tile feeds both blocks.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+// RS_SPLIT: sweep 1 was split over key chunks (rs_part holds their (max, sum) pairs); the unsplit
+// kernel carries none of the merge's state, which is what lets it run three waves per SIMD at bf16.
+template <typename T, int D, bool RS_SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RS_SPLIT ? 1 : kSweepMinWaves<T>)))
+void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                       float* __restrict__ lse2, float* __restrict__ cum,
                                                       float* __restrict__ band, float2* __restrict__ cs_part,
                                                       const float2* __restrict__ rs_part, int kchunk,
@@ -265,7 +274,7 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
     ldr.issue(Q + qh * n * D, i0, n, qtile[u & 1], wave);
     if (threadIdx.x < kRowTile) {
       const int row = i0 + (int)threadIdx.x;
-      if (rs_part == nullptr) {
+      if constexpr (!RS_SPLIT) {
         lpre = row < i_end ? lse2[qh * n + row] : INFINITY;
       } else {
         const int rr = min(row, n - 1);
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(256) void colsums_kernel(const T* __restrict__ Q, c
   auto commit = [&](int u) {                                     // tile u's lse2 into its LDS slot
     wait_lds_loads();
     if (threadIdx.x < kRowTile) {
-      if (rs_part != nullptr) {
+      if constexpr (RS_SPLIT) {
         float Mx = kNegBig, Ls = 0.f;
         auto merge = [&](float2 v) {
           if (v.y > 0.f) {
@@ -411,9 +420,11 @@ static hipError_t launch_profile_sweeps_t(const ProfileArgs& a, hipStream_t st) 
     if (e != hipSuccess) return e;
   }
   timed_begin(FG_K_COLSUMS, st);
-  colsums_kernel<T, D><<<dim3((unsigned)(a.Hkv * cs_groups), a.B), dim3(256), 0, st>>>(
-      (const T*)a.Q, (const T*)a.K, a.lse2, a.cum, a.band, a.cs_part, a.lse_ready ? nullptr : a.rs_part, a.kchunk,
-      a.lse_out, a.Hq, a.Hkv, a.n, n_kb, a.rchunk, a.w_l, c);
+  const float2* rs_part = a.lse_ready ? nullptr : a.rs_part;
+  auto colsums = rs_part ? colsums_kernel<T, D, true> : colsums_kernel<T, D, false>;
+  colsums<<<dim3((unsigned)(a.Hkv * cs_groups), a.B), dim3(256), 0, st>>>(
+      (const T*)a.Q, (const T*)a.K, a.lse2, a.cum, a.band, a.cs_part, rs_part, a.kchunk, a.lse_out, a.Hq, a.Hkv, a.n,
+      n_kb, a.rchunk, a.w_l, c);
   timed_end(st);
   return hipGetLastError();
 }
