@@ -191,7 +191,7 @@ size_t fg_profile_workspace_size(const fg_shape* s) {
   const size_t rows_q = (size_t)s->batch * s->n_q_heads * s->seq_len;
   const size_t rows_k = (size_t)s->batch * s->n_kv_heads * s->seq_len;
   // buffer sizes do not depend on the slot count (it only steers the chunk size)
-  const fg::SweepSplit sp = fg::sweep_split(s->batch, s->n_q_heads, s->n_kv_heads, s->seq_len, 512);
+  const fg::SweepSplit sp = fg::sweep_split(s->batch, s->n_q_heads, s->n_kv_heads, s->seq_len, 256, true);
   return align256(rows_q * sizeof(float)) + align256(rows_k * sizeof(float)) + align256(sp.rs_bytes) +
          align256(sp.cs_bytes);
 }
@@ -260,7 +260,7 @@ fg_status profile_impl(const fg_shape* shape, const fg_params* params, const voi
   const size_t rows_q = (size_t)a.B * a.Hq * a.n;
   const size_t rows_k = (size_t)a.B * a.Hkv * a.n;
   a.band = band_out ? band_out : reinterpret_cast<float*>(ws + align256(rows_q * sizeof(float)));
-  const fg::SweepSplit sp = fg::sweep_split(a.B, a.Hq, a.Hkv, a.n, sweep_slots());
+  const fg::SweepSplit sp = fg::sweep_split(a.B, a.Hq, a.Hkv, a.n, sweep_slots() / 2, a.dtype == FG_DTYPE_BF16);
   unsigned char* parts = ws + align256(rows_q * sizeof(float)) + align256(rows_k * sizeof(float));
   a.kchunk = sp.kchunk;
   a.rchunk = sp.rchunk;

@@ -97,16 +97,18 @@ struct SweepSplit {
   bool rs_split, cs_split;
   size_t rs_bytes, cs_bytes;
 };
-// slots: workgroups that run at once (two per compute unit); it only steers the
-// chunk size, never the buffer sizes.
-inline SweepSplit sweep_split(int B, int Hq, int Hkv, int n, int slots) {
+// cus: compute units; with bf16 operands sweep 1 runs three workgroups per CU, sweep 2 three when
+// sweep 1 is not split and two when it is (it then merges sweep 1's partial statistics); fp32 runs
+// two of each.  The slots only steer the chunk sizes, never the buffer sizes.
+inline SweepSplit sweep_split(int B, int Hq, int Hkv, int n, int cus, bool bf16) {
   SweepSplit p{};
   const int n_rb = (n + kSweepRowsPerWG - 1) / kSweepRowsPerWG;
   const int n_kb = (n + kSweepKeysPerWG - 1) / kSweepKeysPerWG;
   p.rs_split = (long long)B * Hq * n_rb < kSplitBelowGroups && n > kSplitMinChunk;
   p.cs_split = (long long)B * Hkv * n_kb < kSplitBelowGroups && n > kSplitMinChunk;
-  p.kchunk = p.rs_split ? choose_split_chunk(n, n_rb, (long long)B * Hq, false, slots) : n_rb * kSweepRowsPerWG;
-  p.rchunk = p.cs_split ? choose_split_chunk(n, n_kb, (long long)B * Hkv, true, slots) : n;
+  const int rs_slots = cus * (bf16 ? 3 : 2), cs_slots = cus * (bf16 && !p.rs_split ? 3 : 2);
+  p.kchunk = p.rs_split ? choose_split_chunk(n, n_rb, (long long)B * Hq, false, rs_slots) : n_rb * kSweepRowsPerWG;
+  p.rchunk = p.cs_split ? choose_split_chunk(n, n_kb, (long long)B * Hkv, true, cs_slots) : n;
   p.rs_bytes = p.rs_split ? (size_t)split_count(n, kSplitMinChunk) * B * Hq * n * sizeof(float) * 2 : 0;
   p.cs_bytes = p.cs_split ? (size_t)split_count(n, kSplitMinChunk) * B * Hkv * n * sizeof(float) * 2 : 0;
   return p;

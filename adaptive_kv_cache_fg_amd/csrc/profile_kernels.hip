@@ -38,8 +38,10 @@ constexpr int kKeyTile = 64;      // sweep 1: keys staged per LDS tile (2 units 
                                   // both buffers at bf16, d = 128, so three workgroups fit a CU)
 constexpr int kKeysPerWave = 64;  // sweep 2: keys per wave (two MFMA column blocks)
 constexpr int kKeysPerWG = kSweepKeysPerWG;   // sweep 2: 4 waves x 64 keys
-constexpr int kRowTile = 64;      // sweep 2: query rows staged per LDS tile (2 slices of 32 rows; 35 KB of LDS
-                                  // for both buffers at bf16, d = 128, so three workgroups fit a CU)
+// sweep 2: query rows staged per LDS tile -- 64 (2 slices of 32 rows; 35 KB of LDS for both buffers at
+// bf16, d = 128, so three workgroups fit a CU), 128 for the kernel that merges a split sweep 1 (two
+// workgroups per CU, so the larger tile halves its barriers)
+template <bool RS_SPLIT> constexpr int kRowTile = RS_SPLIT ? 128 : 64;
 
 // Waves per SIMD the sweeps are compiled for: three for bf16 (at most 168 VGPRs), where a third wave
 // overlaps the matrix cores and the softmax VALU of the others better than two; no bound otherwise
@@ -215,8 +217,8 @@ void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   using op_t = typename M::op_t;
   constexpr int NK = D / M::KS;
   constexpr int kRB = D * (int)sizeof(T) + kPadBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char qtile[2][kRowTile * kRB];
-  __shared__ __attribute__((aligned(16))) float lse_t[2][kRowTile];
+  __shared__ __attribute__((aligned(16))) unsigned char qtile[2][kRowTile<RS_SPLIT> * kRB];
+  __shared__ __attribute__((aligned(16))) float lse_t[2][kRowTile<RS_SPLIT>];
 
   const int nbh = Hkv * (gridDim.y);                     // B * Hkv (grid.y = batch)
   const int bh = blockIdx.y * Hkv + (int)(blockIdx.x % Hkv);
@@ -249,9 +251,9 @@ void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   float cum_g[2] = {0.f, 0.f}, band_g[2] = {0.f, 0.f};
   const int i_begin = kb * kKeysPerWG + split_begin(n_rows, n_ch, ch);   // this chunk's query rows [i_begin, i_end)
   const int i_end = kb * kKeysPerWG + min(n_rows, split_begin(n_rows, n_ch, ch + 1));
-  const int ntiles = (i_end - i_begin + kRowTile - 1) / kRowTile;   // query tiles per query head
+  const int ntiles = (i_end - i_begin + kRowTile<RS_SPLIT> - 1) / kRowTile<RS_SPLIT>;   // query tiles per query head
   const int total = G * ntiles;
-  LdsLoader<T, D, kRowTile> ldr;
+  LdsLoader<T, D, kRowTile<RS_SPLIT>> ldr;
   ldr.init(wave, lane);
   float lpre = 0.f;
   // With sweep 1 split over key chunks (rs_part), a row's log-sum-exp is merged here from the
@@ -269,10 +271,10 @@ void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // tile to issue is tracked incrementally (no integer division per tile).
   int ig = 0, it = 0;
   auto issue = [&](int u) {                                      // tile u = (ig, it) of the sequence
-    const int i0 = i_begin + (ntiles - 1 - it) * kRowTile;   // last rows first (see below)
+    const int i0 = i_begin + (ntiles - 1 - it) * kRowTile<RS_SPLIT>;   // last rows first (see below)
     const size_t qh = (size_t)b * Hq + (size_t)h * G + ig;
     ldr.issue(Q + qh * n * D, i0, n, qtile[u & 1], wave);
-    if (threadIdx.x < kRowTile) {
+    if (threadIdx.x < kRowTile<RS_SPLIT>) {
       const int row = i0 + (int)threadIdx.x;
       if constexpr (!RS_SPLIT) {
         lpre = row < i_end ? lse2[qh * n + row] : INFINITY;
@@ -289,7 +291,7 @@ void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   };
   auto commit = [&](int u) {                                     // tile u's lse2 into its LDS slot
     wait_lds_loads();
-    if (threadIdx.x < kRowTile) {
+    if (threadIdx.x < kRowTile<RS_SPLIT>) {
       if constexpr (RS_SPLIT) {
         float Mx = kNegBig, Ls = 0.f;
         auto merge = [&](float2 v) {
@@ -318,12 +320,12 @@ void colsums_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   int t_cur = 0;                                                 // row tile of tile u
   for (int u = 0; u < total; ++u) {
     if (u + 1 < total) issue(u + 1);
-    const int i0 = i_begin + (ntiles - 1 - t_cur) * kRowTile;
+    const int i0 = i_begin + (ntiles - 1 - t_cur) * kRowTile<RS_SPLIT>;
     const unsigned char* qt = qtile[u & 1];
     const float* lt = lse_t[u & 1];
-    if (i0 + kRowTile - 1 >= j0 && i0 < i_end) {                // wave-uniform: some pair is causal
+    if (i0 + kRowTile<RS_SPLIT> - 1 >= j0 && i0 < i_end) {                // wave-uniform: some pair is causal
 #pragma unroll
-      for (int rh = 0; rh < kRowTile / 32; ++rh) {              // 32-row slices of the tile
+      for (int rh = 0; rh < kRowTile<RS_SPLIT> / 32; ++rh) {              // 32-row slices of the tile
         const int r0 = i0 + 32 * rh;
         if (r0 + 31 < j0 || r0 >= i_end) continue;              // wave-uniform
         op_t a[NK];
