@@ -48,10 +48,13 @@ struct LdsLoader {
         load(base, (unsigned)(off[j] - max(0, r0 + row[j] - (n - 1)) * kRowBytes), lds, j, w);
     }
   }
-  // base is wave-uniform and o a 32-bit lane offset: the scalar-base + vector-offset form
+  // base is wave-uniform and o a 32-bit lane offset: the scalar-base + vector-offset form.  The empty
+  // asm (no instruction) keeps the compiler from hoisting 64-bit copies of the loop-invariant offsets
+  // out of the tile loop, which would hold twice the registers for the whole kernel.
   static __device__ __forceinline__ void load(const unsigned char* base, unsigned o, unsigned char* lds, int j,
                                               int w) {
     if (kWaveLoads % 4 != 0 && j == kPerWave - 1 && 4 * j + w >= kWaveLoads) return;
+    asm volatile("" : "+v"(o));
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + o),
                                      reinterpret_cast<__attribute__((address_space(3))) void*>(
                                          reinterpret_cast<uintptr_t>(lds + (4 * j + w) * 1024)),
