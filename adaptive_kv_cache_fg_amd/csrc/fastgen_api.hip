@@ -264,6 +264,7 @@ fg_status profile_impl(const fg_shape* shape, const fg_params* params, const voi
   unsigned char* parts = ws + align256(rows_q * sizeof(float)) + align256(rows_k * sizeof(float));
   a.kchunk = sp.kchunk;
   a.rchunk = sp.rchunk;
+  a.cus = sweep_slots() / 2;
   a.rs_part = sp.rs_split ? reinterpret_cast<float2*>(parts) : nullptr;
   a.cs_part = sp.cs_split ? reinterpret_cast<float2*>(parts + align256(sp.rs_bytes)) : nullptr;
   a.lse_out = lse_out;

@@ -33,6 +33,7 @@ struct ProfileArgs {
   float2* rs_part;   // [ceil(n/kchunk), B*Hq, n]
   float2* cs_part;   // [ceil(n/rchunk), B*Hkv, n]
   bool lse_ready;    // lse2 already written (by the attention kernel): skip sweep 1
+  int cus;           // compute units of the device (steers the launch shape only)
 };
 
 // Sweep tiling shared by the launcher and the workspace query.

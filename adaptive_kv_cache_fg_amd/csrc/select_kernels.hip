@@ -22,11 +22,10 @@
 
 namespace fg {
 
-constexpr int kSelThreads = 1024;
-
 // Block sums of four fp64 values at once (one shuffle ladder and one barrier
 // for all four); the totals are valid in thread 0.
-__device__ __forceinline__ void block_sum4(double (&v)[4], double (*red)[kSelThreads / 64]) {
+template <int NT>
+__device__ __forceinline__ void block_sum4(double (&v)[4], double (*red)[NT / 64]) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1)
 #pragma unroll
@@ -45,11 +44,11 @@ __device__ __forceinline__ void block_sum4(double (&v)[4], double (*red)[kSelThr
     }
 }
 
-// VPT > 0: each thread holds the scores (and band sums) of keys tid + k * kSelThreads,
-// k < VPT, in registers for every pass (n <= VPT * kSelThreads); VPT = 0: every pass
-// reads them from memory (long prompts).
-template <int VPT>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__ cum, float* __restrict__ band,
+// NT threads per workgroup.  VPT > 0: each thread holds the scores (and band sums) of
+// keys tid + k * NT, k < VPT, in registers for every pass (n <= VPT * NT); VPT = 0:
+// every pass reads them from memory (long prompts).
+template <int VPT, int NT>
+__global__ __launch_bounds__(NT) void select_kernel(float* __restrict__ cum, float* __restrict__ band,
                                                              const float2* __restrict__ cs_part, int rchunk,
                                                              const uint8_t* __restrict__ cls, int Hkv, int n, int G,
                                                              int k_f, double T, uint32_t* __restrict__ fmask,
@@ -57,19 +56,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
   constexpr int NV = VPT > 0 ? VPT : 1;
   __shared__ unsigned hist[256];
   __shared__ unsigned s_sel, s_rem, s_cnt;
-  __shared__ int wave_cnt[kSelThreads / 64];
-  __shared__ double red[4][kSelThreads / 64];
+  __shared__ int wave_cnt[NT / 64];
+  __shared__ double red[4][NT / 64];
 
   const int bh = blockIdx.x, b = bh / Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n_waves = blockDim.x >> 6;
-  const int n_it = (n + kSelThreads - 1) / kSelThreads;   // key batches of kSelThreads
+  const int n_it = (n + NT - 1) / NT;                     // key batches of NT
   float cv[NV], bv[NV];
   if (cs_part) {
     // the column sweep ran in row chunks: add each key's partial sums in chunk order
     const int nbh = gridDim.x;
     for (int it = 0; it < (VPT > 0 ? VPT : n_it); ++it) {
-      const int j = it * kSelThreads + tid;
+      const int j = it * NT + tid;
       float cs = 0.f, bs = 0.f;
       if (j < n) {
         const int nc = split_count(n - (j / kSweepKeysPerWG) * kSweepKeysPerWG, rchunk);
@@ -90,7 +89,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
   } else if (VPT > 0) {
 #pragma unroll
     for (int it = 0; it < NV; ++it) {
-      const int j = it * kSelThreads + tid;
+      const int j = it * NT + tid;
       cv[it] = j < n ? cum[(size_t)bh * n + j] : 0.f;
       bv[it] = j < n ? band[(size_t)bh * n + j] : 0.f;
     }
@@ -101,7 +100,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
   uint8_t cv_cls[NV];                             // token classes of this thread's keys, loaded up front
 #pragma unroll
   for (int it = 0; it < NV; ++it) {
-    const int j = it * kSelThreads + tid;
+    const int j = it * NT + tid;
     cv_cls[it] = (VPT > 0 && j < n) ? cl[j] : (uint8_t)0;
   }
   const int nw = (n + 31) / 32;
@@ -123,7 +122,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
 #pragma unroll
       for (int it = 0; it < (VPT > 0 ? VPT : 1); ++it) {
         if (VPT > 0) {
-          const int j = it * kSelThreads + tid;
+          const int j = it * NT + tid;
           const uint32_t u = __float_as_uint(score_of(it, j));
           if (j < n && (u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
         } else {
@@ -176,7 +175,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
   int run = 0;                                   // equal-to-threshold keys seen at lower indices
 #pragma unroll
   for (int it = 0; it < (VPT > 0 ? VPT : 1); ++it) {
-    for (int base = it * kSelThreads; base < (VPT > 0 ? min(n, (it + 1) * kSelThreads) : n); base += blockDim.x) {
+    for (int base = it * NT; base < (VPT > 0 ? min(n, (it + 1) * NT) : n); base += blockDim.x) {
       const int j = base + tid;
       const bool valid = j < n;
       const float v = valid ? score_of(it, j) : 0.f;
@@ -214,7 +213,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
     }
   }
   double ms[4] = {m_s, m_p, m_f, m_b};
-  block_sum4(ms, red);
+  block_sum4<NT>(ms, red);
   m_s = ms[0];
   m_p = ms[1];
   m_f = ms[2];
@@ -235,14 +234,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(float* __restrict__
   }
 }
 
+template <int NT>
+static void launch_select_nt(const ProfileArgs& a, hipStream_t st) {
+  const int per = (a.n + NT - 1) / NT;
+  auto kern = per <= 1 ? select_kernel<1, NT> : per <= 2 ? select_kernel<2, NT> : per <= 4 ? select_kernel<4, NT> :
+              per <= 8 ? select_kernel<8, NT> : per <= 16 ? select_kernel<16, NT> :
+              per <= 32 ? select_kernel<32, NT> : select_kernel<0, NT>;
+  kern<<<dim3(a.B * a.Hkv), dim3(NT), 0, st>>>(a.cum, a.band, a.cs_part, a.rchunk, a.cls, a.Hkv, a.n, a.Hq / a.Hkv,
+                                               a.k_f, a.T, a.fmask, a.recovery, a.policy);
+}
+
 hipError_t launch_select(const ProfileArgs& a, hipStream_t st) {
   timed_begin(FG_K_SELECT, st);
-  const int per = (a.n + kSelThreads - 1) / kSelThreads;
-  auto kern = per <= 1 ? select_kernel<1> : per <= 2 ? select_kernel<2> : per <= 4 ? select_kernel<4> :
-              per <= 8 ? select_kernel<8> : per <= 16 ? select_kernel<16> : per <= 32 ? select_kernel<32> :
-              select_kernel<0>;
-  kern<<<dim3(a.B * a.Hkv), dim3(kSelThreads), 0, st>>>(a.cum, a.band, a.cs_part, a.rchunk, a.cls, a.Hkv, a.n,
-                                                         a.Hq / a.Hkv, a.k_f, a.T, a.fmask, a.recovery, a.policy);
+  // One workgroup per head.  A head's selection is a chain of barriers, so while every head's
+  // workgroup is resident at once (two 1024-thread workgroups per CU) the widest workgroup is the
+  // fastest; with more heads than that, narrower workgroups keep every head resident instead of
+  // running the heads in rounds.
+  const int heads = a.B * a.Hkv;
+  if (heads <= 2 * a.cus) launch_select_nt<1024>(a, st);
+  else if (heads <= 4 * a.cus) launch_select_nt<512>(a, st);
+  else launch_select_nt<256>(a, st);
   timed_end(st);
   return hipGetLastError();
 }
