@@ -742,6 +742,16 @@ fg_status fg_peak_mfma_bf16(const void* operands, float* out, int32_t iters, int
   return FG_OK;
 }
 
+fg_status fg_peak_mfma_softmax(const void* operands, float* out, int32_t iters, int32_t blocks,
+                               hipStream_t stream) {
+  if (!operands || !out) return fail(FG_ERR_INVALID_ARG, "operands and out must not be NULL");
+  if (!aligned16(operands)) return fail(FG_ERR_INVALID_ARG, "operands must be 16-byte aligned");
+  if (iters < 1 || blocks < 1) return fail(FG_ERR_INVALID_ARG, "iters and blocks must be >= 1");
+  const hipError_t e = fg::launch_peak_mfma_softmax(operands, out, iters, blocks, stream);
+  if (e != hipSuccess) return hip_fail(e, "peak mfma softmax");
+  return FG_OK;
+}
+
 fg_status fg_peak_exp(float* out, int32_t iters, int32_t blocks, hipStream_t stream) {
   if (!out) return fail(FG_ERR_INVALID_ARG, "out must not be NULL");
   if (iters < 1 || blocks < 1) return fail(FG_ERR_INVALID_ARG, "iters and blocks must be >= 1");

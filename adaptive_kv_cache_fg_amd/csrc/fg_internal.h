@@ -260,6 +260,7 @@ hipError_t launch_track_init(const int64_t* row_offset, const int32_t* pos, cons
 // Micro-benchmarks of the chip's ceilings (measurement only).
 hipError_t launch_peak_mfma(const void* operands, float* out, int iters, int blocks, hipStream_t st);
 hipError_t launch_peak_exp(float* out, int iters, int blocks, hipStream_t st);
+hipError_t launch_peak_mfma_softmax(const void* operands, float* out, int iters, int blocks, hipStream_t st);
 hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, bool nontemporal, int blocks, hipStream_t st);
 hipError_t launch_peak_read(const void* src, size_t bytes, bool nontemporal, int blocks, unsigned* out,
                             hipStream_t st);

@@ -1,7 +1,7 @@
 // Micro-benchmarks of the chip's own ceilings, against which the profiling and
 // decode kernels are reported next to the vendor figures.  They take no part
-// in the method: bf16 MFMA issue rate, transcendental (v_exp_f32) rate, and
-// a plain 16-byte-vector copy through HBM.
+// in the method: bf16 MFMA issue rate, transcendental (v_exp_f32) rate, the MFMA rate beside the
+// sweeps' softmax work, a plain 16-byte-vector copy and a read-only stream through HBM.
 #include "fg_common.h"
 #include "fg_internal.h"
 
@@ -49,6 +49,53 @@ __global__ __launch_bounds__(256) void peak_exp_kernel(float* __restrict__ out, 
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < kExpChains; ++c) s += x[c];
+  out[t] = s;
+}
+
+// The profiling sweeps' instruction mix with the two kinds of work in different waves of one SIMD:
+// a 512-thread workgroup holds 8 waves, and waves w and w + 4 run on the same SIMD.  Waves 0-3 run
+// the 4 MFMA chains of peak_mfma_kernel; waves 4-7 run, per lane and iteration, 8 independent
+// score updates of the sweeps' softmax (one FMA, one v_exp_f32, one add each).  One iteration of a
+// wave pair is 4 MFMAs (512 score pairs at d = 128) against 8 updates per lane (512 pairs), the ratio
+// of a sweep, so the MFMA rate of this kernel is the ceiling of a sweep whose MFMA and VALU work
+// overlap as well as the chip lets waves of one SIMD overlap them.
+__global__ __launch_bounds__(512) void peak_mfma_softmax_kernel(const bf16x8* __restrict__ src,
+                                                                float* __restrict__ out, int iters) {
+  const int t = blockIdx.x * 512 + threadIdx.x;
+  float s = 0.f;
+  if (threadIdx.x < 256) {                                   // waves 0-3: MFMA
+    const bf16x8 a = src[t & 1023];
+    const bf16x8 b = src[(t + 512) & 1023];
+    f32x16 acc[kMfmaChains];
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int c = 0; c < kMfmaChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s += acc[c][r];
+  } else {                                                   // waves 4-7: x <- 2^(x c - m), sum += x
+    float x[kExpChains], sum[kExpChains];
+#pragma unroll
+    for (int c = 0; c < kExpChains; ++c) {
+      x[c] = 0.01f * c + 1e-6f * (t & 1023);
+      sum[c] = 0.f;
+    }
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int c = 0; c < kExpChains; ++c) {
+        x[c] = __builtin_amdgcn_exp2f(fmaf(x[c], 0.18f, -0.5f));   // stays in (0.7, 0.9)
+        sum[c] += x[c];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kExpChains; ++c) s += sum[c];
+  }
   out[t] = s;
 }
 
@@ -113,6 +160,11 @@ hipError_t launch_peak_mfma(const void* operands, float* out, int iters, int blo
 
 hipError_t launch_peak_exp(float* out, int iters, int blocks, hipStream_t st) {
   peak_exp_kernel<<<dim3(blocks), dim3(256), 0, st>>>(out, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_peak_mfma_softmax(const void* operands, float* out, int iters, int blocks, hipStream_t st) {
+  peak_mfma_softmax_kernel<<<dim3(blocks), dim3(512), 0, st>>>(static_cast<const bf16x8*>(operands), out, iters);
   return hipGetLastError();
 }
 

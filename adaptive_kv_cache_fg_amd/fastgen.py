@@ -107,6 +107,7 @@ def lib() -> ctypes.CDLL:
     L.fg_decode_step_noalloc.restype = ctypes.c_int
     L.fg_peak_mfma_bf16.argtypes, L.fg_peak_mfma_bf16.restype = [P, P, I32, I32, P], ctypes.c_int
     L.fg_peak_exp.argtypes, L.fg_peak_exp.restype = [P, I32, I32, P], ctypes.c_int
+    L.fg_peak_mfma_softmax.argtypes, L.fg_peak_mfma_softmax.restype = [P, P, I32, I32, P], ctypes.c_int
     L.fg_peak_copy.argtypes, L.fg_peak_copy.restype = [P, P, S, I32, I32, P], ctypes.c_int
     L.fg_peak_read.argtypes, L.fg_peak_read.restype = [P, S, I32, I32, P, P], ctypes.c_int
     _ = D, I64
@@ -609,6 +610,18 @@ def peak_mfma_bf16(operands: torch.Tensor, out: torch.Tensor, iters: int, blocks
         raise ValueError("operands must hold 8192 bf16 values and out blocks * 256 floats")
     _check(lib().fg_peak_mfma_bf16(_ptr(operands), _ptr(out), int(iters), int(blocks), _stream()),
            "fg_peak_mfma_bf16")
+    return float(blocks) * 4 * 4 * 32768 * iters
+
+
+def peak_mfma_softmax(operands: torch.Tensor, out: torch.Tensor, iters: int, blocks: int) -> float:
+    """fg_peak_mfma_softmax; returns the MFMA flops of the call (waves 0-3 of each workgroup: 4 chains x
+    32768 flops x iters; waves 4-7 run the sweeps' softmax updates beside them)."""
+    _need(operands, "operands", torch.bfloat16)
+    _need(out, "out", torch.float32)
+    if operands.numel() < 8192 or out.numel() < blocks * 512:
+        raise ValueError("operands must hold 8192 bf16 values and out blocks * 512 floats")
+    _check(lib().fg_peak_mfma_softmax(_ptr(operands), _ptr(out), int(iters), int(blocks), _stream()),
+           "fg_peak_mfma_softmax")
     return float(blocks) * 4 * 4 * 32768 * iters
 
 

@@ -733,9 +733,9 @@ def cpu_baseline_stack(spec: syn.ConfigSpec, layers_layers: int) -> dict:
 
 # ---------------------------------------------------------------- the chip's own ceilings
 def chip_peaks(torch, fg) -> dict:
-    """Micro-benchmarks (libfastgen's fg_peak_*): bf16 MFMA issue rate, v_exp_f32 rate, a 1 GiB
-    HBM copy and a 4 GiB read-only stream, each the best over a few occupancies, events around
-    repeated launches."""
+    """Micro-benchmarks (libfastgen's fg_peak_*): bf16 MFMA issue rate, the MFMA rate beside the
+    sweeps' softmax work in other waves of the same SIMDs, v_exp_f32 rate, a 1 GiB HBM copy and a
+    4 GiB read-only stream, each the best over a few occupancies, events around repeated launches."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def timed(fn, reps=5):
@@ -760,6 +760,14 @@ def chip_peaks(torch, fg) -> dict:
         flops = blocks * 4 * 4 * 32768 * iters
         t = timed(lambda: fg.peak_mfma_bf16(ops, out, iters, blocks))
         mfma.append({"waves_per_simd": per_cu, "tflops": flops / t / 1e12, "ms": t * 1e3})
+    mix = []
+    for per_cu in (1, 2, 3):                       # 512-thread workgroups: 2, 4, 6 waves per SIMD, half MFMA
+        blocks = per_cu * cus
+        out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+        iters = 8000
+        flops = blocks * 4 * 4 * 32768 * iters
+        t = timed(lambda: fg.peak_mfma_softmax(ops, out, iters, blocks))
+        mix.append({"waves_per_simd": 2 * per_cu, "tflops": flops / t / 1e12, "ms": t * 1e3})
     exps = []
     for per_cu in (2, 4, 8):
         blocks = per_cu * cus
@@ -794,6 +802,10 @@ def chip_peaks(torch, fg) -> dict:
         "mfma_bf16": {"measured_tflops": best(mfma, "tflops"), "vendor_tflops": BF16_MFMA_PEAK_TFLOPS,
                       "runs": mfma, "note": "4 independent 32x32x16 bf16 accumulator chains per wave, "
                                             "register operands (random bf16)"},
+        "mfma_softmax": {"measured_tflops": best(mix, "tflops"), "vendor_tflops": BF16_MFMA_PEAK_TFLOPS,
+                         "runs": mix, "note": "MFMA rate of half the waves of each SIMD while the other half "
+                                              "run the sweeps' softmax updates (FMA, v_exp_f32, add) in the "
+                                              "sweeps' ratio: one update per lane per 256 MFMA flops"},
         "exp": {"measured_t_per_s": best(exps, "t_exp_per_s"), "derived_t_per_s": EXP_PEAK_T_PER_S,
                 "runs": exps, "note": f"v_exp_f32, 8 independent chains per lane; derived figure = "
                                       f"half rate (8 lanes/clk/SIMD) x 4 SIMD x {cus} CU x {clock_ghz} GHz"},
@@ -1129,11 +1141,14 @@ def bench_stack(args, spec: syn.ConfigSpec, cpu) -> dict:
             if k in kstats:
                 kstats[k]["frac_of_measured_mfma"] = kstats[k]["achieved"] / mf
                 kstats[k]["exp_frac_of_measured"] = kstats[k]["exp_rate_t_per_s"] / ex
+                kstats[k]["frac_of_measured_mfma_softmax"] = kstats[k]["achieved"] / pk["mfma_softmax"]["measured_tflops"]
         for k in ("compact_gather", "decode_partials", "decode_step"):
             kstats[k]["frac_of_measured_copy"] = kstats[k]["achieved"] / cp
         for k in ("decode_partials", "decode_step"):                 # read streams: the read ceiling
             kstats[k]["frac_of_measured_read"] = kstats[k]["achieved"] / rd
         phases["prompt_frac_of_measured_mfma"] = phases["prompt_mfma_frac"] * peak_mfma / mf
+        phases["prompt_frac_of_measured_mfma_softmax"] = (phases["prompt_mfma_frac"] * peak_mfma /
+                                                          pk["mfma_softmax"]["measured_tflops"])
         phases["decode_frac_of_measured_copy"] = phases["decode_hbm_frac"] * HBM_PEAK_GBS / cp
         phases["decode_frac_of_measured_read"] = phases["decode_hbm_frac"] * HBM_PEAK_GBS / rd
         ceiling = mf if dk["bound"] != "hbm" else (rd if dominant.startswith("decode") else cp)

@@ -417,6 +417,15 @@ fg_status fg_decode_track(const fg_cache* cache, const void* q, const uint8_t* t
  * fg_peak_exp: `blocks` x 256 threads each run `iters` iterations of 8
  *   independent chains x <- 2^(-x) (one v_exp_f32 each): blocks * 256 * 8 * iters
  *   exponentials per call.  out [blocks * 256] fp32.
+ * fg_peak_mfma_softmax: `blocks` workgroups of 512 threads (8 wave64; waves w
+ *   and w + 4 share a SIMD).  Waves 0-3 run fg_peak_mfma_bf16's loop; waves 4-7
+ *   run, per lane and iteration, 8 independent score updates of the profiling
+ *   sweeps' softmax (x <- 2^(x c - m), sum += x: one FMA, one v_exp_f32, one
+ *   add), i.e. the sweeps' ratio of one score update per lane to each 256 MFMA
+ *   flops.  blocks * 4 * 4 * 32768 * iters MFMA flops per call; operands and out
+ *   as for fg_peak_mfma_bf16 with out [blocks * 512].  Its MFMA rate is the
+ *   ceiling of a sweep whose two kinds of work overlap as well as different
+ *   waves of one SIMD can overlap them.
  * fg_peak_copy: copy `bytes` (a multiple of 16, both pointers 16-byte aligned,
  *   not overlapping) from src to dst with 16-byte loads and stores over a
  *   grid-stride loop of `blocks` x 256 threads; nontemporal != 0 stores
@@ -432,6 +441,8 @@ fg_status fg_decode_track(const fg_cache* cache, const void* q, const uint8_t* t
  */
 fg_status fg_peak_mfma_bf16(const void* operands, float* out, int32_t iters, int32_t blocks, hipStream_t stream);
 fg_status fg_peak_exp(float* out, int32_t iters, int32_t blocks, hipStream_t stream);
+fg_status fg_peak_mfma_softmax(const void* operands, float* out, int32_t iters, int32_t blocks,
+                               hipStream_t stream);
 fg_status fg_peak_copy(const void* src, void* dst, size_t bytes, int32_t nontemporal, int32_t blocks,
                        hipStream_t stream);
 fg_status fg_peak_read(const void* src, size_t bytes, int32_t nontemporal, int32_t blocks, uint32_t* out,

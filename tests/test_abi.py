@@ -226,6 +226,9 @@ def test_peak_benchmarks_reject_bad_arguments():
     assert L.fg_peak_mfma_bf16(ctypes.c_void_p(0x1008), p, 10, 10, None) == 1      # misaligned operands
     assert L.fg_peak_mfma_bf16(p, p, 0, 10, None) == 1
     assert L.fg_peak_exp(None, 10, 10, None) == 1
+    assert L.fg_peak_mfma_softmax(None, p, 10, 10, None) == 1
+    assert L.fg_peak_mfma_softmax(ctypes.c_void_p(0x1008), p, 10, 10, None) == 1   # misaligned operands
+    assert L.fg_peak_mfma_softmax(p, p, 10, 0, None) == 1
     assert L.fg_peak_exp(p, 10, 0, None) == 1
     assert L.fg_peak_copy(p, ctypes.c_void_p(0x100000), 24, 0, 8, None) == 1        # not a multiple of 16
     assert L.fg_peak_copy(p, ctypes.c_void_p(0x1100), 4096, 0, 8, None) == 1        # overlapping
