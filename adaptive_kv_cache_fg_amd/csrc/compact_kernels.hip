@@ -11,7 +11,7 @@
 //
 // Kernels: a per-head count (plan), one scan over heads for row and work-item
 // offsets (one workgroup does both for plans of modest size), and a gather
-// over (head, 128-position chunk) whose workgroups rank their kept keys with a
+// over (head, 64-position chunk) whose workgroups rank their kept keys with a
 // wave ballot prefix and copy rows with 16-byte loads; the last chunk of a
 // head also writes the head's decode work items.
 #include "fg_common.h"
@@ -19,7 +19,7 @@
 
 namespace fg {
 
-constexpr int kPosChunk = 128;
+constexpr int kPosChunk = 64;      // positions per gather workgroup (one wave): the most workgroups for the copy
 constexpr int kCopyBatch = 4;     // 16-byte chunks of K and of V per thread in flight in the gather's copy
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
