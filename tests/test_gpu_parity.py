@@ -32,6 +32,8 @@ def test_config0_tiny_planted_fp32(lib_mod):
     (300, 64, "f32", 4, 4, 1),
     (517, 128, "bf16", 8, 1, 1),
     (2600, 128, "bf16", 2, 2, 1),      # split sweep 1 with 11 key chunks per row: merge past the prefetched 8
+    (1100, 128, "f32", 4, 2, 1),       # fp32 operands at d = 128 (two waves per SIMD), GQA, ragged tiles
+    (2600, 64, "f32", 2, 1, 1),        # fp32, both sweeps split
 ])
 def test_ragged_shapes(lib_mod, n, d, dtype, hq, hkv, batch):
     types = ("special", "punct", "heavy", "local", "none", "none", "none", "none")[:hkv]
